@@ -1,0 +1,277 @@
+"""Throughput of the grouped-linear hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of seeded synthetic input:
+split-offset scan, grouped forward (+bias), dgrad, wgrad, bias grad, on the
+8-group bf16 workload (G=8, K=4096, N=14336, 16384 rows, multinomial splits).
+``value`` is the algorithmic fwd+dgrad+wgrad flops (6*T*N*K) per step divided by
+the measured time of a whole step (scan and bias grad included), in TFLOP/s,
+with all inputs resident in HBM before timing starts.
+
+Also reported on the same line: per-pass kernel times from HIP events on the
+launch stream, the roofline entry of the dominant kernel, the MXFP8 forward on
+its own workload (G=32, K=N=4096, 32768 rows), and the CPU oracle timed on a
+bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-mxfp8] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 / MXFP8 MFMA
+PEAK_HBM_GBS = 8000.0
+METRIC = "grouped GEMM TFLOP/s (fwd+dgrad+wgrad) and % of MFMA peak, bf16 & MXFP8"
+GEMM_SRC = os.path.join(ROOT, "grouped_gemm_gl_amd", "csrc", "gl_gemm_mfma.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash(path: str) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def traffic_for(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were taken
+    on the current kernel source; otherwise None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        rec = json.load(open(path))[f"{workload}:{kernel}"]
+    except Exception:
+        return None
+    if rec.get("source_sha") != source_hash(GEMM_SRC):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+class EventTimer:
+    """HIP events recorded on torch's current stream, which is the stream every
+    library call is enqueued on."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = {}
+
+    def run(self, name, fn):
+        s = self.torch.cuda.Event(enable_timing=True)
+        e = self.torch.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        self.pairs.setdefault(name, []).append((s, e))
+
+    def mean_ms(self):
+        return {k: sum(s.elapsed_time(e) for s, e in v) / len(v) for k, v in self.pairs.items()}
+
+
+def cpu_baseline(wl, m, x, w, b, dy, budget_s=15.0):
+    """The oracle, as it stands, on whole groups of the same workload until about
+    `budget_s` seconds of CPU work; TFLOP/s over the same 6*m_g*N*K flops."""
+    import numpy as np
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [os.cpu_count() or 1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    off = np.concatenate([[0], np.cumsum(m)])
+    done_flops, t_total, groups = 0.0, 0.0, []
+    for g in range(wl.G):
+        if m[g] == 0:
+            continue
+        lo, hi = int(off[g]), int(off[g + 1])
+        sub_m = [hi - lo]
+        xs = x[lo:hi].double().numpy()
+        dys = dy[lo:hi].double().numpy()
+        wg = w[g:g + 1].double().numpy()
+        bg = b[g:g + 1].double().numpy() if b is not None else None
+        t0 = time.perf_counter()
+        oracle.forward(xs, wg, bg, sub_m)
+        oracle.dgrad(dys, wg, sub_m)
+        oracle.wgrad(xs, dys, sub_m)
+        t_total += time.perf_counter() - t0
+        done_flops += 6.0 * (hi - lo) * wl.N * wl.K
+        groups.append(g)
+        if t_total >= budget_s:
+            break
+    return {"value": round(done_flops / t_total / 1e12, 4), "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"oracle fp64 forward+dgrad+wgrad of groups {groups} ({sum(m[g] for g in groups)} of "
+                      f"{wl.T} rows) of the same workload, {t_total:.1f} s"}
+
+
+def bench_bf16(torch, gl, synth, steps, warmup):
+    wl = synth.WORKLOADS["bf16_train_g8_k4096_n14336"]
+    dev = torch.device("cuda")
+    t0 = time.time()
+    m = synth.split_sizes(wl)
+    x, w, b, dy = synth.x(wl), synth.weight(wl), synth.bias(wl), synth.dy(wl)
+    log(f"inputs generated in {time.time() - t0:.1f}s; m_splits={m.tolist()}")
+    xd, wd, bd, dyd = (t.to(dev) for t in (x, w, b, dy))
+    md = torch.from_numpy(m).to(dev)
+    G, K, N, T = wl.G, wl.K, wl.N, wl.T
+    ws = gl.new_workspace(G, dev)
+    y = torch.empty(T, N, dtype=torch.bfloat16, device=dev)
+    dx = torch.empty(T, K, dtype=torch.bfloat16, device=dev)
+    dw = torch.empty(G, N, K, dtype=torch.bfloat16, device=dev)
+    db = torch.empty(G, N, dtype=torch.bfloat16, device=dev)
+    timer = EventTimer(torch)
+
+    def step(t=None):
+        run = (lambda n, f: t.run(n, f)) if t else (lambda n, f: f())
+        run("offsets", lambda: gl.gl_offsets(md, T, ws))
+        run("forward", lambda: gl.gl_forward(xd, wd, y, ws, bias=bd))
+        run("dgrad", lambda: gl.gl_dgrad(dyd, wd, dx, ws))
+        run("wgrad", lambda: gl.gl_wgrad(xd, dyd, dw, ws))
+        run("bgrad", lambda: gl.gl_bgrad(dyd, db, ws))
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    if gl.gl_read_status(ws) != 0:
+        raise RuntimeError("invalid split sizes")
+    # whole-step wall time (no per-kernel events inside)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    # per-kernel durations on the launch stream
+    for _ in range(max(3, min(steps, 10))):
+        step(timer)
+    torch.cuda.synchronize()
+    per = timer.mean_ms()
+    flops_pass = 2.0 * T * N * K
+    ms_step = elapsed * 1e3 / steps
+    value = 3 * flops_pass / (ms_step * 1e-3) / 1e12
+    passes = {}
+    for k, ms in per.items():
+        d = {"ms": round(ms, 4)}
+        if k in ("forward", "dgrad", "wgrad"):
+            d["tflops"] = round(flops_pass / (ms * 1e-3) / 1e12, 2)
+            d["pct_bf16_peak"] = round(100 * d["tflops"] / PEAK_BF16_TFLOPS, 2)
+        if k == "bgrad":
+            gbs = (T * N * 2 + G * N * 2) / (ms * 1e-3) / 1e9
+            d["gbs"] = round(gbs, 1)
+            d["pct_hbm"] = round(100 * gbs / PEAK_HBM_GBS, 2)
+        if k == "offsets":
+            d["us"] = round(ms * 1e3, 2)
+        passes[k] = d
+    dom = max(("forward", "dgrad", "wgrad"), key=lambda k: per[k])
+    achieved = flops_pass / (per[dom] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": f"gemm_mfma_kernel ({dom})", "achieved": round(achieved, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic_for(dom, wl.name),
+                "algorithmic_flops_per_launch": flops_pass}
+    return wl, m, (x, w, b, dy), {
+        "value": value, "ms_per_step": ms_step, "passes": passes, "roofline": roofline,
+        "fwd_dgrad_wgrad_ms": sum(per[k] for k in ("forward", "dgrad", "wgrad")),
+    }
+
+
+def bench_mxfp8(torch, gl, synth, steps, warmup):
+    wl = synth.WORKLOADS["mxfp8_fwd_g32_k4096_n4096"]
+    dev = torch.device("cuda")
+    t0 = time.time()
+    m = synth.split_sizes(wl)
+    x, w = synth.x(wl).to(dev), synth.weight(wl).to(dev)
+    log(f"mxfp8 inputs generated in {time.time() - t0:.1f}s")
+    G, K, N, T = wl.G, wl.K, wl.N, wl.T
+    ws = gl.new_workspace(G, dev)
+    gl.gl_offsets(torch.from_numpy(m).to(dev), T, ws)
+    xq = torch.empty(T, K, dtype=torch.uint8, device=dev)
+    xs = torch.empty(T, K // 32, dtype=torch.uint8, device=dev)
+    wq = torch.empty(G, N, K, dtype=torch.uint8, device=dev)
+    wsc = torch.empty(G, N, K // 32, dtype=torch.uint8, device=dev)
+    y = torch.empty(T, N, dtype=torch.bfloat16, device=dev)
+    gl.gl_group_quantize_mxfp8(w, wq, wsc)  # weights quantized once, as a cached workspace
+    timer = EventTimer(torch)
+    for i in range(warmup + steps):
+        t = timer if i >= warmup else None
+        run = (lambda n, f: t.run(n, f)) if t else (lambda n, f: f())
+        run("quantize_x", lambda: gl.gl_group_quantize_mxfp8(x, xq, xs))
+        run("quantize_w", lambda: gl.gl_group_quantize_mxfp8(w, wq, wsc))
+        run("mx_forward", lambda: gl.gl_forward(xq, wq, y, ws, x_scale=xs, w_scale=wsc))
+    torch.cuda.synchronize()
+    per = timer.mean_ms()
+    flops = 2.0 * T * N * K
+    tf = flops / (per["mx_forward"] * 1e-3) / 1e12
+    qx_bytes = T * K * 2 + T * K + T * K // 32
+    qw_bytes = G * N * K * 2 + G * N * K + G * N * K // 32
+    return {
+        "workload": wl.name,
+        "mx_forward_ms": round(per["mx_forward"], 4),
+        "mx_forward_tflops": round(tf, 2),
+        "pct_fp8_peak": round(100 * tf / PEAK_FP8_TFLOPS, 2),
+        "quantize_x_ms": round(per["quantize_x"], 4),
+        "quantize_x_gbs": round(qx_bytes / (per["quantize_x"] * 1e-3) / 1e9, 1),
+        "quantize_w_ms": round(per["quantize_w"], 4),
+        "quantize_w_gbs": round(qw_bytes / (per["quantize_w"] * 1e-3) / 1e9, 1),
+        "quantize_x_plus_forward_tflops": round(flops / ((per["mx_forward"] + per["quantize_x"]) * 1e-3) / 1e12,
+                                                2),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-mxfp8", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(groups would shard across GPUs as expert parallelism; see the design notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import grouped_gemm_gl_amd as gl
+    import synth
+
+    gl.load()
+    wl, m, host_inputs, r = bench_bf16(torch, gl, synth, args.steps, args.warmup)
+    out = {
+        "metric": METRIC,
+        "value": round(r["value"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "num_groups": wl.G, "in_features": wl.K, "out_features": wl.N,
+                   "total_rows": wl.T, "m_splits": m.tolist(), "bias": True,
+                   "step": "offsets+forward+dgrad+wgrad+bgrad", "parallelism": "single GPU"},
+        "pct_bf16_peak": round(100 * r["value"] / PEAK_BF16_TFLOPS, 2),
+        "passes": r["passes"],
+        "roofline": r["roofline"],
+    }
+    if not args.no_mxfp8:
+        out["mxfp8"] = bench_mxfp8(torch, gl, synth, max(5, args.steps // 2), 2)
+    if not args.no_cpu_baseline:
+        x, w, b, dy = host_inputs
+        out["cpu_baseline"] = cpu_baseline(wl, m.tolist(), x, w, b, dy)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

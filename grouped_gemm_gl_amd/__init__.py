@@ -1,0 +1,238 @@
+"""Python binding of the gfx950 grouped-linear library ``libgrouped_linear.so``.
+
+Argument marshalling only: each function takes torch tensors (device memory),
+checks that their shapes, dtypes and devices agree with one another, and passes
+their addresses plus the current HIP stream to the C entry point of the same name
+(declared in ``include/grouped_linear.h``).  Every step of the computation runs in
+the library's HIP kernels; nothing here computes, and there is no fallback: if the
+library is not built, importing works but the first call raises.
+
+Weights, biases and weight gradients are accepted stacked (one tensor with a
+leading group dimension) or per group (a list of tensors); for a list, a device
+array of their addresses is built and handed over.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Union
+
+import torch
+
+__all__ = [
+    "GL_F32", "GL_BF16", "GL_F16", "GL_E4M3", "GLError", "library_path", "load",
+    "gl_workspace_size", "new_workspace", "gl_offsets", "gl_read_status", "gl_forward",
+    "gl_dgrad", "gl_wgrad", "gl_bgrad", "gl_group_quantize_mxfp8", "gl_version",
+]
+
+GL_F32, GL_BF16, GL_F16, GL_E4M3 = 0, 1, 2, 3
+GL_STATUS_NEGATIVE_SPLIT, GL_STATUS_SUM_MISMATCH, GL_STATUS_WORKSPACE = 1, 2, 4
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libgrouped_linear.so")
+_lib = None
+
+Tensor = torch.Tensor
+Grouped = Union[Tensor, Sequence[Tensor]]
+
+
+class GLError(RuntimeError):
+    """A non-zero return code of the C library, with its message."""
+
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"[{code}] {msg}")
+        self.code = code
+
+
+def load():
+    """Load the shared library (once); raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(library_path):
+        raise RuntimeError(f"{library_path} is not built; run `python -m grouped_gemm_gl_amd.build`")
+    lib = ctypes.CDLL(library_path)
+    P, I, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+    sig = {
+        "gl_workspace_size": (ctypes.c_size_t, [I]),
+        "gl_workspace_offsets": (P, [P]),
+        "gl_offsets": (I, [P, I, I64, P, P]),
+        "gl_read_status": (I, [P, ctypes.POINTER(ctypes.c_int), P]),
+        "gl_forward": (I, [I, I64, I64, I64, I, I, P, P, P, P, P, P, P, P, P, I64, P, P]),
+        "gl_dgrad": (I, [I, I64, I64, I64, I, P, P, P, P, I64, P, P]),
+        "gl_wgrad": (I, [I, I64, I64, I64, I, I, P, P, P, P, I, P, P]),
+        "gl_bgrad": (I, [I, I64, I64, I, P, P, P, P, P]),
+        "gl_group_quantize_mxfp8": (I, [P, I64, I64, P, P, P]),
+        "gl_last_error": (ctypes.c_char_p, []),
+        "gl_version": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype, fn.argtypes = res, args
+    _lib = lib
+    return lib
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise GLError(rc, load().gl_last_error().decode())
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t: Optional[Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the library must be contiguous")
+    return t.data_ptr() if t.numel() else None
+
+
+_DT = {torch.float32: GL_F32, torch.bfloat16: GL_BF16, torch.float16: GL_F16, torch.uint8: GL_E4M3}
+
+
+def _dtype(t: Tensor) -> int:
+    if t.dtype not in _DT:
+        raise ValueError(f"unsupported dtype {t.dtype}")
+    return _DT[t.dtype]
+
+
+def _grouped(g: Optional[Grouped], device):
+    """(stacked pointer, pointer-array pointer, keep-alive) for a stacked tensor or a list."""
+    if g is None:
+        return None, None, None
+    if isinstance(g, Tensor):
+        return _ptr(g), None, None
+    ptrs = torch.tensor([_ptr(t) or 0 for t in g], dtype=torch.int64, device=device)
+    return None, ptrs.data_ptr(), (ptrs, list(g))
+
+
+def _first(g: Grouped) -> Tensor:
+    return g[0] if not isinstance(g, Tensor) or g.dim() == 3 else g
+
+
+def gl_version() -> str:
+    return load().gl_version().decode()
+
+
+def gl_workspace_size(num_groups: int) -> int:
+    return int(load().gl_workspace_size(num_groups))
+
+
+def new_workspace(num_groups: int, device="cuda") -> Tensor:
+    """Device buffer sized for a call sequence over ``num_groups`` groups."""
+    return torch.empty(gl_workspace_size(num_groups), dtype=torch.uint8, device=device)
+
+
+def gl_offsets(m_splits: Tensor, total_rows: int, workspace: Tensor, stream=None) -> None:
+    """Split-offset scan of the device int64 split sizes into ``workspace``."""
+    if m_splits.dtype != torch.int64:
+        raise ValueError("m_splits must be int64")
+    _check(load().gl_offsets(_ptr(m_splits), m_splits.numel(), int(total_rows), _ptr(workspace), _stream(stream)))
+
+
+def workspace_offsets(workspace: Tensor, num_groups: int) -> Tensor:
+    """The int64[G+1] offsets inside a workspace, as a view (no device work)."""
+    return workspace[32: 32 + 8 * (num_groups + 1)].view(torch.int64)
+
+
+def gl_read_status(workspace: Tensor, stream=None) -> int:
+    """Synchronise the stream and return the workspace status word (0 = valid splits)."""
+    st = ctypes.c_int(0)
+    _check(load().gl_read_status(_ptr(workspace), ctypes.byref(st), _stream(stream)))
+    return st.value
+
+
+def gl_forward(x: Tensor, w: Grouped, y: Tensor, workspace: Tensor, *, bias: Optional[Grouped] = None,
+               x_scale: Optional[Tensor] = None, w_scale: Optional[Grouped] = None, stream=None) -> Tensor:
+    """y[:T] = grouped x W_g^T (+ b_g); T = x.shape[0]; rows of y past T are left untouched.
+
+    x: [T, K] float32 / bfloat16, or uint8 E4M3 codes with ``x_scale`` [T, K/32];
+    w: [G, N, K] or G tensors [N, K] (uint8 with ``w_scale`` for MXFP8);
+    y: [>= T, N] (float32 / bfloat16; for MXFP8 its dtype picks the output type).
+    """
+    G = w.shape[0] if isinstance(w, Tensor) else len(w)
+    w0 = _first(w)
+    N, K = w0.shape[-2], w0.shape[-1]
+    T = x.shape[0]
+    if x.dim() != 2 or x.shape[1] != K:
+        raise ValueError(f"x must be [T, {K}], got {tuple(x.shape)}")
+    if y.dim() != 2 or y.shape[1] != N:
+        raise ValueError(f"y must be [rows >= {T}, {N}], got {tuple(y.shape)}")
+    if w0.dtype != x.dtype:
+        raise ValueError("x and w must have the same dtype")
+    if bias is not None and _first(bias).dtype != y.dtype:
+        raise ValueError("bias dtype must equal the output dtype")
+    dev = x.device
+    wp, wpp, keep_w = _grouped(w, dev)
+    bp, bpp, keep_b = _grouped(bias, dev)
+    sp, spp, keep_s = _grouped(w_scale, dev)
+    _check(load().gl_forward(G, K, N, T, _dtype(x), _dtype(y), _ptr(x), _ptr(x_scale), wp, wpp, sp, spp, bp, bpp,
+                             _ptr(y), y.shape[0], _ptr(workspace), _stream(stream)))
+    del keep_w, keep_b, keep_s
+    return y
+
+
+def gl_dgrad(dy: Tensor, w: Grouped, dx: Tensor, workspace: Tensor, stream=None) -> Tensor:
+    """dx[:T] = grouped dy W_g; T = dy.shape[0]; rows of dx past T are left untouched."""
+    G = w.shape[0] if isinstance(w, Tensor) else len(w)
+    w0 = _first(w)
+    N, K = w0.shape[-2], w0.shape[-1]
+    T = dy.shape[0]
+    if dy.dim() != 2 or dy.shape[1] != N:
+        raise ValueError(f"dy must be [T, {N}], got {tuple(dy.shape)}")
+    if dx.dim() != 2 or dx.shape[1] != K or dx.dtype != dy.dtype or w0.dtype != dy.dtype:
+        raise ValueError("dx must be [rows >= T, K] and dy, w, dx must share one dtype")
+    wp, wpp, keep = _grouped(w, dy.device)
+    _check(load().gl_dgrad(G, K, N, T, _dtype(dy), _ptr(dy), wp, wpp, _ptr(dx), dx.shape[0], _ptr(workspace),
+                           _stream(stream)))
+    del keep
+    return dx
+
+
+def gl_wgrad(x: Tensor, dy: Tensor, dw: Grouped, workspace: Tensor, *, accumulate: bool = False,
+             stream=None) -> Grouped:
+    """dW_g (+)= dy_g^T x_g over each group's rows; dw is [G, N, K] or G tensors [N, K]."""
+    G = dw.shape[0] if isinstance(dw, Tensor) else len(dw)
+    d0 = _first(dw)
+    N, K = d0.shape[-2], d0.shape[-1]
+    T = x.shape[0]
+    if x.shape != (T, K) or dy.shape != (T, N) or x.dtype != dy.dtype:
+        raise ValueError("x must be [T, K] and dy [T, N] with one dtype")
+    dp, dpp, keep = _grouped(dw, x.device)
+    _check(load().gl_wgrad(G, K, N, T, _dtype(x), _dtype(d0), _ptr(x), _ptr(dy), dp, dpp, int(bool(accumulate)),
+                           _ptr(workspace), _stream(stream)))
+    del keep
+    return dw
+
+
+def gl_bgrad(dy: Tensor, db: Grouped, workspace: Tensor, stream=None) -> Grouped:
+    """db_g = column sums of dy over each group's rows; db is [G, N] or G tensors [N]."""
+    G = db.shape[0] if isinstance(db, Tensor) else len(db)
+    N = dy.shape[1]
+    d0 = db[0] if not isinstance(db, Tensor) else db
+    if d0.shape[-1] != N or d0.dtype != dy.dtype:
+        raise ValueError("db must have dy's column count and dtype")
+    dp, dpp, keep = _grouped(db, dy.device)
+    _check(load().gl_bgrad(G, N, dy.shape[0], _dtype(dy), _ptr(dy), dp, dpp, _ptr(workspace), _stream(stream)))
+    del keep
+    return db
+
+
+def gl_group_quantize_mxfp8(src: Tensor, data: Tensor, scale: Tensor, stream=None):
+    """Rowwise MXFP8 of a bf16 [rows, cols] tensor into uint8 data [rows, cols] and
+    uint8 scale [rows, cols/32] (leading dimensions are flattened into rows)."""
+    if src.dtype != torch.bfloat16:
+        raise ValueError("src must be bfloat16")
+    cols = src.shape[-1]
+    rows = src.numel() // cols if cols else 0
+    if data.numel() != src.numel() or data.dtype != torch.uint8:
+        raise ValueError("data must be uint8 with src's element count")
+    if scale.numel() != rows * (cols // 32) or scale.dtype != torch.uint8:
+        raise ValueError("scale must be uint8 with rows * cols/32 elements")
+    _check(load().gl_group_quantize_mxfp8(_ptr(src), rows, cols, _ptr(data), _ptr(scale), _stream(stream)))
+    return data, scale

@@ -1,0 +1,76 @@
+"""Build the gfx950 shared library ``libgrouped_linear.so`` in-tree with hipcc.
+
+Usage: ``python -m grouped_gemm_gl_amd.build`` (or ``build()`` from Python).  Each
+``csrc/*.hip`` file is compiled to an object in ``_build/`` in parallel and the
+objects are linked into ``grouped_gemm_gl_amd/libgrouped_linear.so``.
+"""
+from __future__ import annotations
+
+import concurrent.futures
+import glob
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+OUT = os.path.join(HERE, "libgrouped_linear.so")
+BUILD_DIR = os.path.join(ROOT, "_build")
+ARCH = "gfx950"
+
+HIP_FLAGS = [
+    f"--offload-arch={ARCH}",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-Wall",
+    "-Wno-unused-result",
+    "-Wno-unused-function",
+    # packed fp32 VALU forms are kept out of the generated code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", os.path.join(ROOT, "include"),
+]
+
+
+def _hipcc() -> str:
+    for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", "hipcc"):
+        if c and (os.path.isabs(c) and os.path.exists(c) or not os.path.isabs(c)):
+            return c
+    raise RuntimeError("hipcc not found")
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    noise = "is not a recognized feature for this target"
+    text = "\n".join(l for l in r.stdout.splitlines() if noise not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"command failed ({r.returncode}): {' '.join(cmd)}\n{text}")
+    return text
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    hipcc = _hipcc()
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    objs = [os.path.join(BUILD_DIR, os.path.basename(s) + ".o") for s in srcs]
+
+    def compile_one(pair):
+        src, obj = pair
+        return _run([hipcc, *HIP_FLAGS, "-c", src, "-o", obj])
+
+    workers = max(1, min(len(srcs), os.cpu_count() or 1, 16))
+    with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+        logs = list(ex.map(compile_one, zip(srcs, objs)))
+    tmp = OUT + ".tmp"
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
+    os.replace(tmp, OUT)
+    if verbose:
+        for l in logs:
+            if l.strip():
+                print(l)
+    return OUT
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

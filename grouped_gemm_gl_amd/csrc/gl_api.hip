@@ -1,0 +1,268 @@
+// Host entry points of the C ABI declared in include/grouped_linear.h.
+//
+// Each entry point validates its arguments on the host before anything is
+// enqueued (the reference layer raises before allocating or launching: page
+// "transformer_engine/pytorch/ops/basic/grouped_linear.py", constructor and
+// fuser_forward checks; caller buffers are validated by shape/dtype/contiguity on
+// page "[PyTorch] Add optional caller-provided output/grad-input buffers ...").  On
+// an error nothing is launched and the message is kept per thread.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/grouped_linear.h"
+#include "gl_common.hpp"
+
+namespace gl {
+hipError_t launch_offsets(const int64_t *m_splits, int G, int64_t total_rows, void *ws, hipStream_t stream);
+hipError_t launch_forward_bf16(int G, int64_t K, int64_t N, int64_t T, const uint16_t *x, const uint16_t *w,
+                               const uint16_t *const *w_ptrs, const void *bias, const void *const *bias_ptrs,
+                               uint16_t *y, const void *ws, hipStream_t s);
+hipError_t launch_dgrad_bf16(int G, int64_t K, int64_t N, int64_t T, const uint16_t *dy, const uint16_t *w,
+                             const uint16_t *const *w_ptrs, uint16_t *dx, const void *ws, hipStream_t s);
+hipError_t launch_wgrad_bf16(int G, int64_t K, int64_t N, int64_t T, const uint16_t *x, const uint16_t *dy,
+                             void *dw, void *const *dw_ptrs, int out_f32, int accumulate, const void *ws,
+                             hipStream_t s);
+hipError_t launch_forward_mxfp8(int G, int64_t K, int64_t N, int64_t T, const uint8_t *xq, const uint8_t *xs,
+                                const uint8_t *wq, const uint8_t *const *wq_ptrs, const uint8_t *ws_scale,
+                                const uint8_t *const *ws_scale_ptrs, const void *bias,
+                                const void *const *bias_ptrs, void *y, int out_f32, const void *ws,
+                                hipStream_t s);
+hipError_t launch_forward_f32(int G, int64_t K, int64_t N, int64_t T, const float *x, const float *w,
+                              const float *const *w_ptrs, const float *bias, const float *const *bias_ptrs,
+                              float *y, const void *ws, hipStream_t s);
+hipError_t launch_dgrad_f32(int G, int64_t K, int64_t N, int64_t T, const float *dy, const float *w,
+                            const float *const *w_ptrs, float *dx, const void *ws, hipStream_t s);
+hipError_t launch_wgrad_f32(int G, int64_t K, int64_t N, int64_t T, const float *x, const float *dy, float *dw,
+                            float *const *dw_ptrs, int accumulate, const void *ws, hipStream_t s);
+hipError_t launch_bgrad(int G, int64_t N, int64_t T, int f32, const void *dy, void *db, void *const *db_ptrs,
+                        const void *ws, hipStream_t s);
+hipError_t launch_quantize_mxfp8(const uint16_t *src, int64_t rows, int64_t cols, uint8_t *data, uint8_t *scale,
+                                 hipStream_t s);
+}  // namespace gl
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = 0;
+  return GL_OK;
+}
+
+int hip_result(hipError_t e, const char *what) {
+  if (e != hipSuccess) return fail(GL_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Sizes shared by every GEMM entry point.
+int check_sizes(int G, int64_t K, int64_t N, int64_t T) {
+  if (G <= 0) return fail(GL_ERR_ARG, "Invalid number of groups (%d)", G);
+  if (K <= 0) return fail(GL_ERR_ARG, "Invalid input size (%lld)", (long long)K);
+  if (N <= 0) return fail(GL_ERR_ARG, "Invalid output size (%lld)", (long long)N);
+  if (T < 0) return fail(GL_ERR_ARG, "Invalid total_rows (%lld)", (long long)T);
+  if (T > INT32_MAX || (int64_t)G * 256 > INT32_MAX)
+    return fail(GL_ERR_SHAPE, "sizes exceed the 32-bit work-item range");
+  return GL_OK;
+}
+
+int check_float_dtype(gl_dtype d, const char *what) {
+  if (d == GL_F16) return fail(GL_ERR_UNSUPPORTED, "%s: fp16 is not built in this library", what);
+  if (d != GL_F32 && d != GL_BF16) return fail(GL_ERR_DTYPE, "%s: dtype must be GL_F32 or GL_BF16", what);
+  return GL_OK;
+}
+
+int check_one_form(const void *stacked, const void *ptrs, const char *what, bool optional) {
+  if (stacked && ptrs) return fail(GL_ERR_ARG, "%s: pass either the stacked buffer or the pointer array, not both", what);
+  if (!optional && !stacked && !ptrs) return fail(GL_ERR_ARG, "%s: missing (stacked buffer or pointer array)", what);
+  if (stacked && !aligned16(stacked)) return fail(GL_ERR_ARG, "%s: buffer not 16-byte aligned", what);
+  if (ptrs && ((uintptr_t)ptrs & 7u)) return fail(GL_ERR_ARG, "%s: pointer array not 8-byte aligned", what);
+  return GL_OK;
+}
+
+int check_buf(const void *p, int64_t T, const char *what) {
+  if (T == 0) return GL_OK;
+  if (!p) return fail(GL_ERR_ARG, "%s is NULL", what);
+  if (!aligned16(p)) return fail(GL_ERR_ARG, "%s not 16-byte aligned", what);
+  return GL_OK;
+}
+
+int check_bf16_dims(gl_dtype d, int64_t K, int64_t N) {
+  if (d == GL_BF16 && (K % 8 || N % 8))
+    return fail(GL_ERR_SHAPE, "bf16 needs in_features and out_features that are multiples of 8 (got %lld, %lld)",
+                (long long)K, (long long)N);
+  return GL_OK;
+}
+
+}  // namespace
+
+#define GL_TRY(expr)          \
+  do {                        \
+    int _rc = (expr);         \
+    if (_rc != GL_OK) return _rc; \
+  } while (0)
+
+extern "C" {
+
+size_t gl_workspace_size(int num_groups) { return num_groups > 0 ? gl::ws_bytes(num_groups) : 0; }
+
+const int64_t *gl_workspace_offsets(const void *workspace) {
+  return workspace ? (const int64_t *)((const char *)workspace + gl::ws_offsets_byte(0)) : nullptr;
+}
+
+const char *gl_last_error(void) { return g_err; }
+
+const char *gl_version(void) { return "grouped_gemm_gl_amd 0.1 (gfx950)"; }
+
+int gl_offsets(const int64_t *m_splits, int num_groups, int64_t total_rows, void *workspace, hipStream_t stream) {
+  if (num_groups <= 0) return fail(GL_ERR_ARG, "Invalid number of groups (%d)", num_groups);
+  if (total_rows < 0) return fail(GL_ERR_ARG, "Invalid total_rows (%lld)", (long long)total_rows);
+  if (!m_splits) return fail(GL_ERR_ARG, "m_splits is NULL");
+  if ((uintptr_t)m_splits & 7u) return fail(GL_ERR_ARG, "m_splits not 8-byte aligned");
+  if (!workspace || !aligned16(workspace)) return fail(GL_ERR_ARG, "workspace NULL or not 16-byte aligned");
+  return hip_result(gl::launch_offsets(m_splits, num_groups, total_rows, workspace, stream), "gl_offsets");
+}
+
+int gl_read_status(const void *workspace, int *status, hipStream_t stream) {
+  if (!workspace || !status) return fail(GL_ERR_ARG, "workspace or status is NULL");
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_result(e, "gl_read_status");
+  int32_t st = 0;
+  e = hipMemcpy(&st, workspace, sizeof(st), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_result(e, "gl_read_status");
+  *status = st;
+  return ok();
+}
+
+int gl_forward(int num_groups, int64_t in_features, int64_t out_features, int64_t total_rows, gl_dtype in_dtype,
+               gl_dtype out_dtype, const void *x, const uint8_t *x_scale, const void *w, const void *const *w_ptrs,
+               const uint8_t *w_scale, const uint8_t *const *w_scale_ptrs, const void *bias,
+               const void *const *bias_ptrs, void *y, int64_t y_rows, const void *workspace,
+               hipStream_t stream) {
+  const int G = num_groups;
+  const int64_t K = in_features, N = out_features, T = total_rows;
+  GL_TRY(check_sizes(G, K, N, T));
+  if (!workspace) return fail(GL_ERR_ARG, "workspace is NULL");
+  if (y_rows < T) return fail(GL_ERR_SHAPE, "output buffer has %lld rows, needs at least %lld", (long long)y_rows,
+                              (long long)T);
+  GL_TRY(check_one_form(w, w_ptrs, "weight", false));
+  GL_TRY(check_one_form(bias, bias_ptrs, "bias", true));
+  GL_TRY(check_buf(x, T, "x"));
+  GL_TRY(check_buf(y, T, "y"));
+  if (in_dtype == GL_E4M3) {
+    if (out_dtype != GL_BF16 && out_dtype != GL_F32)
+      return fail(GL_ERR_DTYPE, "MXFP8 forward: out_dtype must be GL_BF16 or GL_F32");
+    if (K % 128) return fail(GL_ERR_SHAPE, "MXFP8 forward needs in_features %% 128 == 0 (got %lld)", (long long)K);
+    if (N % 8) return fail(GL_ERR_SHAPE, "MXFP8 forward needs out_features %% 8 == 0 (got %lld)", (long long)N);
+    if (T > 0 && (!x_scale || ((uintptr_t)x_scale & 3u))) return fail(GL_ERR_ARG, "x_scale NULL or not 4-byte aligned");
+    if ((w != nullptr) != (w_scale != nullptr) || (w_ptrs != nullptr) != (w_scale_ptrs != nullptr))
+      return fail(GL_ERR_ARG, "weight scales must come in the same form as the weights");
+    if (w_scale && ((uintptr_t)w_scale & 3u)) return fail(GL_ERR_ARG, "w_scale not 4-byte aligned");
+    if (T == 0) return ok();
+    return hip_result(gl::launch_forward_mxfp8(G, K, N, T, (const uint8_t *)x, x_scale, (const uint8_t *)w,
+                                               (const uint8_t *const *)w_ptrs, w_scale, w_scale_ptrs, bias,
+                                               bias_ptrs, y, out_dtype == GL_F32, workspace, stream),
+                      "gl_forward");
+  }
+  GL_TRY(check_float_dtype(in_dtype, "gl_forward"));
+  if (out_dtype != in_dtype) return fail(GL_ERR_DTYPE, "gl_forward: out_dtype must equal in_dtype for fp32/bf16");
+  if (x_scale || w_scale || w_scale_ptrs) return fail(GL_ERR_ARG, "scales are only for GL_E4M3 inputs");
+  GL_TRY(check_bf16_dims(in_dtype, K, N));
+  if (T == 0) return ok();
+  hipError_t e;
+  if (in_dtype == GL_BF16)
+    e = gl::launch_forward_bf16(G, K, N, T, (const uint16_t *)x, (const uint16_t *)w,
+                                (const uint16_t *const *)w_ptrs, bias, bias_ptrs, (uint16_t *)y, workspace, stream);
+  else
+    e = gl::launch_forward_f32(G, K, N, T, (const float *)x, (const float *)w, (const float *const *)w_ptrs,
+                               (const float *)bias, (const float *const *)bias_ptrs, (float *)y, workspace, stream);
+  return hip_result(e, "gl_forward");
+}
+
+int gl_dgrad(int num_groups, int64_t in_features, int64_t out_features, int64_t total_rows, gl_dtype dtype,
+             const void *dy, const void *w, const void *const *w_ptrs, void *dx, int64_t dx_rows,
+             const void *workspace, hipStream_t stream) {
+  const int G = num_groups;
+  const int64_t K = in_features, N = out_features, T = total_rows;
+  GL_TRY(check_sizes(G, K, N, T));
+  GL_TRY(check_float_dtype(dtype, "gl_dgrad"));
+  GL_TRY(check_bf16_dims(dtype, K, N));
+  if (!workspace) return fail(GL_ERR_ARG, "workspace is NULL");
+  if (dx_rows < T) return fail(GL_ERR_SHAPE, "dgrad buffer has %lld rows, needs at least %lld", (long long)dx_rows,
+                               (long long)T);
+  GL_TRY(check_one_form(w, w_ptrs, "weight", false));
+  GL_TRY(check_buf(dy, T, "dy"));
+  GL_TRY(check_buf(dx, T, "dx"));
+  if (T == 0) return ok();
+  hipError_t e;
+  if (dtype == GL_BF16)
+    e = gl::launch_dgrad_bf16(G, K, N, T, (const uint16_t *)dy, (const uint16_t *)w, (const uint16_t *const *)w_ptrs,
+                              (uint16_t *)dx, workspace, stream);
+  else
+    e = gl::launch_dgrad_f32(G, K, N, T, (const float *)dy, (const float *)w, (const float *const *)w_ptrs,
+                             (float *)dx, workspace, stream);
+  return hip_result(e, "gl_dgrad");
+}
+
+int gl_wgrad(int num_groups, int64_t in_features, int64_t out_features, int64_t total_rows, gl_dtype in_dtype,
+             gl_dtype out_dtype, const void *x, const void *dy, void *dw, void *const *dw_ptrs, int accumulate,
+             const void *workspace, hipStream_t stream) {
+  const int G = num_groups;
+  const int64_t K = in_features, N = out_features, T = total_rows;
+  GL_TRY(check_sizes(G, K, N, T));
+  GL_TRY(check_float_dtype(in_dtype, "gl_wgrad"));
+  GL_TRY(check_float_dtype(out_dtype, "gl_wgrad"));
+  if (in_dtype == GL_F32 && out_dtype != GL_F32)
+    return fail(GL_ERR_DTYPE, "gl_wgrad: fp32 inputs need an fp32 weight gradient");
+  GL_TRY(check_bf16_dims(in_dtype, K, N));
+  if (!workspace) return fail(GL_ERR_ARG, "workspace is NULL");
+  GL_TRY(check_one_form(dw, dw_ptrs, "weight gradient", false));
+  GL_TRY(check_buf(x, T, "x"));
+  GL_TRY(check_buf(dy, T, "dy"));
+  if (accumulate != 0 && accumulate != 1) return fail(GL_ERR_ARG, "accumulate must be 0 or 1");
+  hipError_t e;
+  if (in_dtype == GL_BF16)
+    e = gl::launch_wgrad_bf16(G, K, N, T, (const uint16_t *)x, (const uint16_t *)dy, dw, dw_ptrs,
+                              out_dtype == GL_F32, accumulate, workspace, stream);
+  else
+    e = gl::launch_wgrad_f32(G, K, N, T, (const float *)x, (const float *)dy, (float *)dw, (float *const *)dw_ptrs,
+                             accumulate, workspace, stream);
+  return hip_result(e, "gl_wgrad");
+}
+
+int gl_bgrad(int num_groups, int64_t out_features, int64_t total_rows, gl_dtype dtype, const void *dy, void *db,
+             void *const *db_ptrs, const void *workspace, hipStream_t stream) {
+  const int G = num_groups;
+  const int64_t N = out_features, T = total_rows;
+  GL_TRY(check_sizes(G, 8, N, T));
+  GL_TRY(check_float_dtype(dtype, "gl_bgrad"));
+  if (N % (dtype == GL_BF16 ? 8 : 4))
+    return fail(GL_ERR_SHAPE, "gl_bgrad needs out_features %% %d == 0", dtype == GL_BF16 ? 8 : 4);
+  if (!workspace) return fail(GL_ERR_ARG, "workspace is NULL");
+  GL_TRY(check_one_form(db, db_ptrs, "bias gradient", false));
+  GL_TRY(check_buf(dy, T, "dy"));
+  return hip_result(gl::launch_bgrad(G, N, T, dtype == GL_F32, dy, db, db_ptrs, workspace, stream), "gl_bgrad");
+}
+
+int gl_group_quantize_mxfp8(const void *src, int64_t rows, int64_t cols, uint8_t *data, uint8_t *scale,
+                            hipStream_t stream) {
+  if (rows < 0 || cols <= 0) return fail(GL_ERR_ARG, "Invalid shape (%lld, %lld)", (long long)rows, (long long)cols);
+  if (cols % 32) return fail(GL_ERR_SHAPE, "cols must be a multiple of 32 (got %lld)", (long long)cols);
+  if (rows == 0) return ok();
+  if (!src || !data || !scale) return fail(GL_ERR_ARG, "src, data or scale is NULL");
+  if (!aligned16(src) || !aligned16(data)) return fail(GL_ERR_ARG, "src and data must be 16-byte aligned");
+  return hip_result(gl::launch_quantize_mxfp8((const uint16_t *)src, rows, cols, data, scale, stream),
+                    "gl_group_quantize_mxfp8");
+}
+
+}  // extern "C"

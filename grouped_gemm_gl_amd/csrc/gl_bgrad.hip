@@ -1,0 +1,91 @@
+// Bias gradient: per-group column sums of dy (page
+// "transformer_engine/pytorch/ops/basic/grouped_linear.py", fuser_backward: the bias
+// grad of each split is dy_split.sum(dim=0)).
+//
+// HBM-bound: dy is read exactly once.  One workgroup owns (group g, a slab of 512
+// columns); each of its 8 waves reads 16 bytes per lane of every 8th row of the
+// group, keeping eight rows in flight, and the 8 wave partials are combined through
+// LDS in a fixed order -- deterministic, no atomics.  An empty group writes zeros.
+#include "gl_common.hpp"
+
+namespace gl {
+
+constexpr int kBgThreads = 512, kBgWaves = kBgThreads / 64, kBgCols = 512, kBgUnroll = 8;
+
+template <bool F32>
+__device__ __forceinline__ void add16(float *a, const uint4 &v) {
+  if constexpr (F32) {
+    a[0] += __uint_as_float(v.x);
+    a[1] += __uint_as_float(v.y);
+    a[2] += __uint_as_float(v.z);
+    a[3] += __uint_as_float(v.w);
+  } else {
+    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a[2 * e] += bf16_to_f32(d[e] & 0xffff);
+      a[2 * e + 1] += bf16_to_f32(d[e] >> 16);
+    }
+  }
+}
+
+template <bool F32>
+__global__ __launch_bounds__(kBgThreads) void bgrad_kernel(const void *__restrict__ dy_, void *db_,
+                                                           void *const *db_ptrs, int G, int64_t N, int64_t T,
+                                                           const void *ws_) {
+  __shared__ float part[kBgWaves][kBgCols];
+  const WsView ws = ws_view(ws_, G);
+  if (!ws_usable(ws.hdr, G, T)) return;
+  constexpr int kEl = F32 ? 4 : 8;  // elements per 16-byte lane load
+  constexpr int kEsz = F32 ? 4 : 2;
+  const int g = blockIdx.y;
+  const int64_t lo = ws.off[g], hi = ws.off[g + 1];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t c0 = (int64_t)blockIdx.x * kBgCols;
+  const char *dy = (const char *)dy_;
+
+  // a wave covers 64 * kEl columns of a row; fp32 takes two sweeps of the slab
+  for (int sweep = 0; sweep < kBgCols / (64 * kEl); ++sweep) {
+    const int lc = sweep * 64 * kEl + lane * kEl;
+    const int64_t col = c0 + lc;
+    float a[kEl];
+#pragma unroll
+    for (int e = 0; e < kEl; ++e) a[e] = 0.f;
+    if (col < N) {  // N is a multiple of kEl, so a lane's 16 bytes are all in range
+      int64_t r = lo + wave;
+      for (; r + (kBgUnroll - 1) * kBgWaves < hi; r += kBgUnroll * kBgWaves) {
+        uint4 v[kBgUnroll];
+#pragma unroll
+        for (int u = 0; u < kBgUnroll; ++u) v[u] = *(const uint4 *)(dy + ((r + u * kBgWaves) * N + col) * kEsz);
+#pragma unroll
+        for (int u = 0; u < kBgUnroll; ++u) add16<F32>(a, v[u]);
+      }
+      for (; r < hi; r += kBgWaves) add16<F32>(a, *(const uint4 *)(dy + (r * N + col) * kEsz));
+    }
+#pragma unroll
+    for (int e = 0; e < kEl; ++e) part[wave][lc + e] = a[e];
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < kBgCols; c += kBgThreads) {
+    const int64_t col = c0 + c;
+    if (col >= N) continue;
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < kBgWaves; ++w) s += part[w][c];
+    char *dst = db_ ? (char *)db_ + ((int64_t)g * N + col) * kEsz : (char *)db_ptrs[g] + col * kEsz;
+    if constexpr (F32) *(float *)dst = s;
+    else *(uint16_t *)dst = f32_to_bf16(s);
+  }
+}
+
+hipError_t launch_bgrad(int G, int64_t N, int64_t T, int f32, const void *dy, void *db, void *const *db_ptrs,
+                        const void *ws, hipStream_t s) {
+  dim3 grid((unsigned)((N + kBgCols - 1) / kBgCols), (unsigned)G);
+  if (f32)
+    hipLaunchKernelGGL(bgrad_kernel<true>, grid, dim3(kBgThreads), 0, s, dy, db, db_ptrs, G, N, T, ws);
+  else
+    hipLaunchKernelGGL(bgrad_kernel<false>, grid, dim3(kBgThreads), 0, s, dy, db, db_ptrs, G, N, T, ws);
+  return hipGetLastError();
+}
+
+}  // namespace gl

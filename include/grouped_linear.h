@@ -1,0 +1,187 @@
+/*
+ * grouped_linear.h -- C ABI of the MI355X (gfx950) grouped-linear library.
+ *
+ * The method (page "transformer_engine/pytorch/ops/basic/grouped_linear.py",
+ * GroupedLinear class docstring): a token matrix x [T, K] is split along its rows
+ * into num_groups consecutive blocks of m_splits[g] rows (zeros allowed), and
+ * block g goes through its own linear layer, y_g = x_g W_g^T + b_g -- the same as
+ * torch.split, one torch.nn.Linear per split, torch.cat.  The backward pass
+ * (same page, fuser_backward) is dgrad dx_g = dy_g W_g, wgrad dW_g = dy_g^T x_g
+ * (optionally added into an fp32 main_grad) and bias grad db_g = column sums of
+ * dy_g.
+ *
+ * Notation: G = num_groups, K = in_features, N = out_features, T = total_rows =
+ * sum of m_splits.  All matrices are dense row-major: x [T,K], y/dy [T,N],
+ * dx [T,K], W [G,N,K] (or G separate [N,K]), b/db [G,N] (or G separate [N]),
+ * dW/main_grad [G,N,K] (or G separate [N,K]).
+ *
+ * Conventions shared by every entry point:
+ *  - Every pointer argument is a DEVICE pointer owned by the caller, except the
+ *    stream.  The library allocates nothing, keeps no pointer after return and
+ *    never synchronises the host (gl_read_status is the one exception).  Work is
+ *    enqueued on `stream` in call order.
+ *  - Weights (and biases, wgrad outputs) come in one of two forms: a stacked
+ *    buffer (`w`) or a DEVICE array of G per-group pointers (`w_ptrs`); exactly one
+ *    of the two must be non-NULL (page "Improve device-init grouped linear module
+ *    with single grouped weight support": single stacked weight or discrete
+ *    per-group weights).  For biases both NULL means "no bias".
+ *  - Buffers must be 16-byte aligned, and for bf16 K and N must be multiples of 8
+ *    so every row starts on a 16-byte boundary (GL_ERR_SHAPE otherwise).
+ *  - Output buffers may have more rows than T (`y_rows`, `dx_rows` >= T): only the
+ *    packed valid rows [0, T) are written and any padded tail is left untouched
+ *    (page "[PyTorch] Add optional caller-provided output/grad-input buffers to
+ *    GroupedLinear and fused grouped MLP", Changes: the GEMM writes only the packed
+ *    valid rows per m_splits).
+ *  - Return value: GL_OK (0) or a negative GL_ERR_* code.  On any host-detected
+ *    error nothing is launched and nothing is written; gl_last_error() gives a
+ *    message (thread-local).
+ *  - Split sizes live on the device.  gl_offsets validates them there: a negative
+ *    size or a sum different from total_rows sets the status word in the
+ *    workspace, and every later kernel that reads that workspace then exits
+ *    without writing anything.  gl_read_status() reports the word.
+ */
+#ifndef GROUPED_LINEAR_H
+#define GROUPED_LINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types.  GL_F16 is accepted by the reference layer but not built here. */
+typedef enum gl_dtype { GL_F32 = 0, GL_BF16 = 1, GL_F16 = 2, GL_E4M3 = 3 } gl_dtype;
+
+enum {
+  GL_OK = 0,
+  GL_ERR_ARG = -1,         /* bad size, NULL or misaligned pointer, both/neither weight forms */
+  GL_ERR_DTYPE = -2,       /* element type not valid for this call */
+  GL_ERR_SHAPE = -3,       /* output capacity < total_rows, K/N alignment, K % 32 for MXFP8 */
+  GL_ERR_UNSUPPORTED = -4, /* recognised but not built (fp16) */
+  GL_ERR_HIP = -5          /* a HIP runtime call failed */
+};
+
+/* Status word bits written by gl_offsets (read back with gl_read_status). */
+enum {
+  GL_STATUS_NEGATIVE_SPLIT = 1, /* some m_splits[g] < 0 */
+  GL_STATUS_SUM_MISMATCH = 2,   /* sum of m_splits != total_rows */
+  GL_STATUS_WORKSPACE = 4       /* a later call named a workspace built for other G / T */
+};
+
+/* Bytes of device workspace a call sequence over num_groups groups needs (>= 256). */
+size_t gl_workspace_size(int num_groups);
+
+/*
+ * Split-offset scan (page "Single parameter for GroupedLinear module", Greptile
+ * summary and the common.cu row of its files table: an exclusive prefix sum with a
+ * leading zero, one kernel instead of cumsum + cat).
+ *   m_splits   device int64[num_groups], row count of each group (zeros allowed)
+ *   total_rows rows of x / dy; the splits must add up to it
+ *   workspace  device buffer of gl_workspace_size(num_groups) bytes; receives the
+ *              offsets int64[G+1] (off[0] = 0, off[g+1] = off[g] + m[g]), the
+ *              per-group row-tile tables the GEMMs schedule from, and the status word.
+ * One small kernel; reads m_splits once.  The workspace then serves every later
+ * call of the same step (forward, dgrad, wgrad, bgrad) with the same G and T.
+ */
+int gl_offsets(const int64_t *m_splits, int num_groups, int64_t total_rows, void *workspace,
+               hipStream_t stream);
+
+/* Device address of the int64[G+1] offsets inside a workspace (no device access). */
+const int64_t *gl_workspace_offsets(const void *workspace);
+
+/* Synchronises `stream`, then copies the status word to *status (0 = valid splits). */
+int gl_read_status(const void *workspace, int *status, hipStream_t stream);
+
+/*
+ * Grouped forward y[r,:] = x[r,:] W_g^T + b_g for the rows r of group g (page
+ * "transformer_engine/pytorch/ops/basic/grouped_linear.py", class docstring and
+ * fuser_forward "Perform GEMMs").
+ *   in_dtype   GL_F32, GL_BF16, or GL_E4M3 (MXFP8: x and W are E4M3 codes with one
+ *              E8M0 scale byte per 32 consecutive elements of a row, as produced by
+ *              gl_group_quantize_mxfp8)
+ *   out_dtype  equals in_dtype for GL_F32 / GL_BF16; GL_BF16 or GL_F32 for GL_E4M3
+ *   x          [T, K] (elements of in_dtype); x_scale [T, K/32] bytes (E4M3 only, else NULL)
+ *   w / w_ptrs stacked [G, N, K] or device array of G pointers to [N, K];
+ *   w_scale / w_scale_ptrs  [G, N, K/32] or G pointers to [N, K/32] (E4M3 only)
+ *   bias / bias_ptrs  [G, N] or G pointers to [N], type out_dtype; both NULL = no bias
+ *   y          [y_rows, N] of out_dtype, y_rows >= T; rows >= T are never written
+ * Accumulation is fp32 (MFMA); the bias is added to the fp32 sum before the single
+ * rounding to out_dtype.
+ */
+int gl_forward(int num_groups, int64_t in_features, int64_t out_features, int64_t total_rows,
+               gl_dtype in_dtype, gl_dtype out_dtype, const void *x, const uint8_t *x_scale,
+               const void *w, const void *const *w_ptrs, const uint8_t *w_scale,
+               const uint8_t *const *w_scale_ptrs, const void *bias, const void *const *bias_ptrs,
+               void *y, int64_t y_rows, const void *workspace, hipStream_t stream);
+
+/*
+ * Grouped dgrad dx[r,:] = dy[r,:] W_g for the rows r of group g (page
+ * "transformer_engine/pytorch/ops/basic/grouped_linear.py", fuser_backward
+ * "Perform dgrad GEMMs", layout NN).
+ *   dtype  GL_F32 or GL_BF16 for dy, W and dx
+ *   dy [T, N]; w / w_ptrs as in gl_forward; dx [dx_rows, K], dx_rows >= T, rows >= T
+ *   untouched (the caller-provided dgrad buffer of the caller-buffer pull request).
+ */
+int gl_dgrad(int num_groups, int64_t in_features, int64_t out_features, int64_t total_rows,
+             gl_dtype dtype, const void *dy, const void *w, const void *const *w_ptrs, void *dx,
+             int64_t dx_rows, const void *workspace, hipStream_t stream);
+
+/*
+ * Grouped wgrad dW_g = dy_g^T x_g, contracted over the m_splits[g] rows of group g
+ * (page "transformer_engine/pytorch/ops/basic/grouped_linear.py", fuser_backward
+ * "Perform wgrad GEMMs", layout NT; accumulate follows the main_grad fusion in
+ * "Initialize grad weight buffers").
+ *   in_dtype   GL_F32 or GL_BF16 for x [T, K] and dy [T, N]
+ *   out_dtype  GL_BF16 or GL_F32 for dW (GL_F32 for an fp32 main_grad)
+ *   dw / dw_ptrs  stacked [G, N, K] or device array of G pointers to [N, K]
+ *   accumulate 0: dW_g is overwritten (an empty group writes zeros);
+ *              1: dW_g += dy_g^T x_g (an empty group is not touched at all).
+ * Every element of dW is produced by one work item in a fixed summation order, so
+ * results are deterministic (no atomics).
+ */
+int gl_wgrad(int num_groups, int64_t in_features, int64_t out_features, int64_t total_rows,
+             gl_dtype in_dtype, gl_dtype out_dtype, const void *x, const void *dy, void *dw,
+             void *const *dw_ptrs, int accumulate, const void *workspace, hipStream_t stream);
+
+/*
+ * Bias grad db_g = sum over the rows of group g of dy (page
+ * "transformer_engine/pytorch/ops/basic/grouped_linear.py", fuser_backward: a
+ * column sum per split of the grad output).  fp32 accumulation in a fixed order;
+ * an empty group gets zeros.
+ *   dtype  GL_F32 or GL_BF16 for dy [T, N] and db
+ *   db / db_ptrs  stacked [G, N] or device array of G pointers to [N]
+ */
+int gl_bgrad(int num_groups, int64_t out_features, int64_t total_rows, gl_dtype dtype,
+             const void *dy, void *db, void *const *db_ptrs, const void *workspace,
+             hipStream_t stream);
+
+/*
+ * Rowwise MXFP8 quantization of a bf16 [rows, cols] matrix (page
+ * "transformer_engine/pytorch/ops/basic/grouped_linear.py", _quantize_weights_mxfp8:
+ * E4M3 data with one scale per 32 elements along the inner dimension; the scale
+ * rule is OCP MX v1.0): per block of 32 consecutive elements of a row, shared
+ * exponent e = floor(log2(amax)) - 8 clamped to [-127, 127] (all-zero block: -127),
+ * scale byte = e + 127, codes = E4M3 round-to-nearest-even of v * 2^-e saturated
+ * to +-448, signed zeros kept; a block holding Inf/NaN gets scale 0xFF and codes
+ * 0x7F | sign.  Blocks never straddle rows, so stacked activations [T, K] and
+ * stacked weights [G*N, K] are both one call, independent of m_splits.
+ *   src  bf16 [rows, cols], cols % 32 == 0;  data  uint8 [rows, cols];
+ *   scale  uint8 [rows, cols / 32] (compact, row-major, no padding)
+ */
+int gl_group_quantize_mxfp8(const void *src, int64_t rows, int64_t cols, uint8_t *data,
+                            uint8_t *scale, hipStream_t stream);
+
+/* Message of the last error on this thread ("" if none). */
+const char *gl_last_error(void);
+
+/* Library identification string. */
+const char *gl_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GROUPED_LINEAR_H */

@@ -1,0 +1,106 @@
+"""The C ABI: the built library loads, exports every entry point the header
+declares, and rejects bad arguments on the host (no GPU needed: each call below
+fails validation before anything is enqueued, so no pointer is dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import grouped_gemm_gl_amd as gl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "grouped_linear.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(gl.library_path), reason="library not built")
+
+FAKE = 0x100000  # aligned, never dereferenced: validation fails first
+FAKE2 = 0x200000
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gl_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_symbols()
+    for n in ["gl_offsets", "gl_forward", "gl_dgrad", "gl_wgrad", "gl_bgrad", "gl_group_quantize_mxfp8",
+              "gl_workspace_size", "gl_last_error", "gl_read_status"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(gl.library_path)
+    missing = [n for n in declared_symbols() if not hasattr(lib, n)]
+    assert not missing
+
+
+def test_version_and_workspace_size():
+    lib = gl.load()
+    assert b"gfx950" in lib.gl_version()
+    assert gl.gl_workspace_size(0) == 0
+    for G in (1, 4, 256, 1000):
+        sz = gl.gl_workspace_size(G)
+        assert sz % 256 == 0
+        assert sz >= 32 + 8 * (G + 1) + 4 * 4 * (G + 1)
+
+
+def fwd(G=4, K=64, N=32, T=32, ind=gl.GL_BF16, outd=gl.GL_BF16, x=FAKE, xs=None, w=FAKE, wp=None, ws_=None,
+        wsp=None, b=None, bp=None, y=FAKE2, y_rows=None, ws=FAKE):
+    lib = gl.load()
+    return lib.gl_forward(G, K, N, T, ind, outd, x, xs, w, wp, ws_, wsp, b, bp, y, T if y_rows is None else y_rows,
+                          ws, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(G=0), -1), (dict(K=0), -1), (dict(N=-3), -1), (dict(T=-1), -1),
+    (dict(y_rows=31), -3),                          # caller buffer too small
+    (dict(w=None), -1), (dict(wp=FAKE), -1),        # neither / both weight forms
+    (dict(b=FAKE, bp=FAKE), -1),
+    (dict(x=FAKE + 8), -1),                         # misaligned
+    (dict(ind=gl.GL_F16, outd=gl.GL_F16), -4),      # fp16: recognised, not built
+    (dict(ind=gl.GL_BF16, outd=gl.GL_F32), -2),
+    (dict(ind=7, outd=7), -2),
+    (dict(K=60), -3), (dict(N=36), -3),             # bf16 rows must be 16-byte multiples
+    (dict(ind=gl.GL_E4M3, outd=gl.GL_BF16, K=96), -3),
+    (dict(ind=gl.GL_E4M3, outd=gl.GL_BF16, K=128, xs=None), -1),
+    (dict(ind=gl.GL_E4M3, outd=gl.GL_E4M3, K=128, xs=FAKE), -2),
+    (dict(ws=None), -1),
+])
+def test_forward_rejects(kw, code):
+    assert fwd(**kw) == code
+    assert gl.load().gl_last_error()
+
+
+def test_other_entry_points_reject():
+    lib = gl.load()
+    assert lib.gl_offsets(None, 4, 32, FAKE, None) == -1
+    assert lib.gl_offsets(FAKE, 0, 32, FAKE, None) == -1
+    assert lib.gl_offsets(FAKE, 4, -1, FAKE, None) == -1
+    assert lib.gl_offsets(FAKE, 4, 32, FAKE + 4, None) == -1
+    assert lib.gl_dgrad(4, 64, 32, 32, gl.GL_BF16, FAKE, FAKE, None, FAKE2, 16, FAKE, None) == -3
+    assert lib.gl_dgrad(4, 64, 32, 32, gl.GL_F16, FAKE, FAKE, None, FAKE2, 32, FAKE, None) == -4
+    assert lib.gl_wgrad(4, 64, 32, 32, gl.GL_F32, gl.GL_BF16, FAKE, FAKE, FAKE2, None, 0, FAKE, None) == -2
+    assert lib.gl_wgrad(4, 64, 32, 32, gl.GL_BF16, gl.GL_F32, FAKE, FAKE, None, None, 0, FAKE, None) == -1
+    assert lib.gl_wgrad(4, 64, 32, 32, gl.GL_BF16, gl.GL_F32, FAKE, FAKE, FAKE2, None, 2, FAKE, None) == -1
+    assert lib.gl_bgrad(4, 36, 32, gl.GL_BF16, FAKE, FAKE2, None, FAKE, None) == -3
+    assert lib.gl_bgrad(4, 32, 32, gl.GL_BF16, FAKE, FAKE2, FAKE2, FAKE, None) == -1
+    assert lib.gl_group_quantize_mxfp8(FAKE, 4, 48, FAKE2, FAKE2, None) == -3
+    assert lib.gl_group_quantize_mxfp8(FAKE, -1, 64, FAKE2, FAKE2, None) == -1
+    assert lib.gl_group_quantize_mxfp8(FAKE + 2, 4, 64, FAKE2, FAKE2, None) == -1
+    assert lib.gl_read_status(None, None, None) == -1
+
+
+def test_zero_rows_is_a_no_op_without_device_work():
+    # nothing to compute and nothing to write: returns OK without touching pointers
+    assert fwd(T=0, x=None, y=None) == 0
+    assert gl.load().gl_group_quantize_mxfp8(None, 0, 64, None, None, None) == 0
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(gl, "_lib", None)
+    monkeypatch.setattr(gl, "library_path", "/nonexistent/libgrouped_linear.so")
+    with pytest.raises(RuntimeError, match="not built"):
+        gl.load()
