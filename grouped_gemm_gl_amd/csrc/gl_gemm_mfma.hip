@@ -393,61 +393,6 @@ static int persistent_grid(int64_t max_items) {
   return (int)(g > 0 ? g : 1);
 }
 
-// forward: y = x W^T (+ b); A = x [T,K], B = W [N,K]
-hipError_t launch_forward_bf16(int G, int64_t K, int64_t N, int64_t T, const uint16_t *x, const uint16_t *w,
-                               const uint16_t *const *w_ptrs, const void *bias, const void *const *bias_ptrs,
-                               uint16_t *y, const void *ws, hipStream_t s) {
-  GemmBf16Params p{};
-  p.A = x; p.lda = K;
-  p.B = w; p.B_ptrs = w_ptrs; p.b_gstride = N * K; p.ldb = K;
-  p.C = y; p.ldc = N;
-  p.bias = bias; p.bias_ptrs = bias_ptrs;
-  p.ws = ws; p.G = G; p.T = T;
-  p.cols_j = N; p.P = K;
-  p.tiles_j = (int)((N + kBN - 1) / kBN);
-  p.out_f32 = 0;
-  const int64_t max_items = ((T + kBM - 1) / kBM + G) * p.tiles_j;
-  hipLaunchKernelGGL((gemm_mfma_kernel<true, true, MODE_ROWS, false>), dim3(persistent_grid(max_items)), dim3(kThreads),
-                     0, s, p);
-  return hipGetLastError();
-}
-
-// dgrad: dx = dy W; A = dy [T,N] (n contiguous), B[j=k][p=n] = W[n][k] (k contiguous)
-hipError_t launch_dgrad_bf16(int G, int64_t K, int64_t N, int64_t T, const uint16_t *dy, const uint16_t *w,
-                             const uint16_t *const *w_ptrs, uint16_t *dx, const void *ws, hipStream_t s) {
-  GemmBf16Params p{};
-  p.A = dy; p.lda = N;
-  p.B = w; p.B_ptrs = w_ptrs; p.b_gstride = N * K; p.ldb = K;
-  p.C = dx; p.ldc = K;
-  p.ws = ws; p.G = G; p.T = T;
-  p.cols_j = K; p.P = N;
-  p.tiles_j = (int)((K + kBN - 1) / kBN);
-  const int64_t max_items = ((T + kBM - 1) / kBM + G) * p.tiles_j;
-  hipLaunchKernelGGL((gemm_mfma_kernel<true, false, MODE_ROWS, false>), dim3(persistent_grid(max_items)), dim3(kThreads),
-                     0, s, p);
-  return hipGetLastError();
-}
-
-// wgrad: dW_g[n][k] = sum_r dy[r][n] x[r][k]; A[i=n][p=r] (n contiguous), B[j=k][p=r] (k contiguous)
-hipError_t launch_wgrad_bf16(int G, int64_t K, int64_t N, int64_t T, const uint16_t *x, const uint16_t *dy,
-                             void *dw, void *const *dw_ptrs, int out_f32, int accumulate, const void *ws,
-                             hipStream_t s) {
-  GemmBf16Params p{};
-  p.A = dy; p.lda = N;
-  p.B = x; p.ldb = K;
-  p.C = dw; p.C_ptrs = dw_ptrs; p.c_gstride = N * K; p.ldc = K;
-  p.ws = ws; p.G = G; p.T = T;
-  p.rows_i = N; p.cols_j = K;
-  p.tiles_i = (int)((N + kBM - 1) / kBM);
-  p.tiles_j = (int)((K + kBN - 1) / kBN);
-  p.accumulate = accumulate;
-  p.out_f32 = out_f32;
-  const int64_t max_items = (int64_t)G * p.tiles_i * p.tiles_j;
-  hipLaunchKernelGGL((gemm_mfma_kernel<false, false, MODE_CONTR, false>), dim3(persistent_grid(max_items)),
-                     dim3(kThreads), 0, s, p);
-  return hipGetLastError();
-}
-
 // MXFP8 forward: y = deq(xq) deq(wq)^T (+ b).  Codes travel as two-byte units, so the
 // loader sees K/2 units per row; K % 128 == 0 keeps scale dwords aligned.
 hipError_t launch_forward_mxfp8(int G, int64_t K, int64_t N, int64_t T, const uint8_t *xq, const uint8_t *xs,
