@@ -11,62 +11,60 @@
 //   wgrad    i = n, j = k, p = token row of group g:  A = dy (i contiguous), B = x   (j contiguous)
 //
 // Tiles: 256x256 outputs per workgroup, 8 waves (two per SIMD) in a 2x4 grid, each
-// wave a 128x64 block of 32x32x16 bf16 MFMAs with fp32 accumulators (GL_WAVES=4
-// builds 4 waves of 128x128 instead).
+// wave a 128x64 block of 32x32x16 bf16 MFMAs with fp32 accumulators.
 //
-// Operand staging: the contraction advances 32 at a time through a 4-stage LDS ring
-// (16 KiB per operand per stage), filled by direct global->LDS loads
-// (global_load_lds, 16 bytes per lane) issued three tiles ahead of the MFMAs, with a
-// single workgroup barrier per tile.  An operand whose contraction index is
-// contiguous ("K-major") is staged as 256 rows of 64 bytes and read with 16-byte
-// LDS loads; one whose tile index is contiguous ("MN-major") is staged as 32 rows
-// of 512 bytes and read with the gfx950 LDS transpose load (ds_read_b64_tr_b16),
-// which hands each lane 4 consecutive contraction values of one column -- exactly
-// the MFMA operand layout -- so no operand is ever transposed in registers.  Both
-// layouts XOR-swizzle 16-byte slots so the fragment reads are bank-conflict free.
+// Operand staging: the contraction advances 64 at a time through two LDS stages
+// (32 KiB per operand per stage) filled by direct global->LDS loads
+// (global_load_lds, 16 bytes per lane).  An operand whose contraction index is
+// contiguous ("K-major") is staged as 256 rows of 128 bytes -- whole cache lines --
+// and read with 16-byte LDS loads; one whose tile index is contiguous ("MN-major")
+// is staged as 64 rows of 512 bytes and read with the gfx950 LDS transpose load
+// (ds_read_b64_tr_b16), which hands each lane 4 consecutive contraction values of
+// one column -- exactly the MFMA operand layout -- so no operand is transposed in
+// registers.  Both layouts XOR-swizzle 16-byte slots so fragment reads are free of
+// bank conflicts on gfx950's 64-bank LDS.
+//
+// Pipeline, per 64-deep tile kt (4 MFMA steps of 16): the loads of tile kt + 1 go
+// out first, into the stage tile kt - 1 used; MFMA steps 0-2 run while the
+// fragments of the following step are read; then every wave waits for its own
+// loads of tile kt + 1 and the workgroup meets at one barrier, after which step 3
+// runs while the first fragments of tile kt + 1 are read.  The steady-state body
+// (every tile but the last two) is straight-line code: unconditional loads, no
+// per-lane predicates.
 //
 // Masking: rows past the valid extent of a K-major tile are clamped onto a valid
 // row (their products land in output rows that are never stored); columns past an
 // MN-major tile's extent are clamped likewise; contraction indices past the end
 // (the last tile of a group in wgrad, or a contraction length not a multiple of
-// 32) are not loaded -- those lanes write zeros into their LDS slot instead.
+// 64) are not loaded -- those lanes write zeros into their LDS slot instead.
 //
 // Scheduling: persistent grid, one workgroup per CU; workgroup b walks items b,
-// b + grid, ...; items are remapped so each XCD (blockIdx % 8) works on a
-// contiguous run of neighbouring tiles that share operand panels in its L2.  In row
-// mode the item -> (group, row tile, column tile) map comes from the row-tile
-// prefix table the offsets kernel left in the workspace.
+// b + grid, ...; items are remapped so each XCD (blockIdx % 8) works on a run of
+// neighbouring tiles (8 x 4 blocks of output tiles) that share operand panels in
+// its L2.  In row mode the item -> (group, row tile, column tile) map comes from
+// the row-tile prefix table the offsets kernel left in the workspace.
 #include "gl_common.hpp"
 
 namespace gl {
 
-namespace v2 {
+namespace mfma_bf16 {
 
-#ifndef GL_WAVES
-#define GL_WAVES 8
-#endif
-#ifndef GL_TILE_ORDER
-#define GL_TILE_ORDER 1
-#endif
-#ifndef GL_INTERLEAVE
-#define GL_INTERLEAVE 1
-#endif
-
-constexpr int kBM = 256, kBN = 256, kBK = 32, kStages = 4;
-constexpr int kWaves = GL_WAVES, kThreads = 64 * kWaves;
-constexpr int kWM = 2, kWN = kWaves / kWM;           // wave grid
-constexpr int kWTM = kBM / kWM, kWTN = kBN / kWN;    // wave tile
-constexpr int kNI = kWTM / 32, kNJ = kWTN / 32;      // 32x32 MFMA blocks per wave
-constexpr int kOpElems = 256 * kBK;                  // bf16 elements per operand per stage
-constexpr int kPieces = kOpElems * 2 / 1024;         // 1 KiB direct-load pieces per operand per stage
-constexpr int kLoadsPerTile = 2 * kPieces / kWaves;  // direct-to-LDS instructions per wave per tile
-// blocked tile order: each XCD's run of neighbouring work items covers a
-// kOrdM x kOrdN block of output tiles
-constexpr int kOrdM = 8, kOrdN = 4;
+constexpr int kBM = 256, kBN = 256, kBK = 64;
+constexpr int kWaves = 8, kThreads = 64 * kWaves;
+constexpr int kWM = 2, kWN = kWaves / kWM;          // wave grid
+constexpr int kWTM = kBM / kWM, kWTN = kBN / kWN;   // wave tile 128 x 64
+constexpr int kNI = kWTM / 32, kNJ = kWTN / 32;     // 32x32 MFMA blocks per wave
+constexpr int kKS = kBK / 16;                       // MFMA steps per tile
+constexpr int kOpElems = 256 * kBK;                 // bf16 elements per operand per stage
+constexpr int kOpBytes = kOpElems * 2;
+constexpr int kPieces = kOpBytes / 1024;            // 1 KiB direct-load pieces per operand per stage
+constexpr int kQ = kPieces / kWaves;                // pieces per wave per operand per tile
+constexpr int kOrdM = 8, kOrdN = 4;                 // blocked work-item order
 
 enum { MODE_ROWS = 0, MODE_CONTR = 1 };
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
 #define GL_LDS __attribute__((address_space(3)))
 
 struct Params {
@@ -91,34 +89,23 @@ struct Params {
   int out_f32;
 };
 
-// 16-byte slot swizzles, chosen for gfx950's LDS (64 banks of 4 bytes; a 16-byte
-// read serves 16 lanes per cycle, an 8-byte read 32 lanes).
-// K-major rows are 64 bytes (4 slots): chunk c of row r sits in slot c ^ swz_k(r).
+// 16-byte slot swizzles for gfx950's LDS (64 banks of 4 bytes; a 16-byte read
+// serves 16 lanes per cycle, an 8-byte read 32 lanes).
+// K-major rows are 128 bytes (8 slots): chunk c of row r sits in slot c ^ swz_k(r).
 // A fragment read takes one chunk of 16 consecutive rows per cycle; rows r and
-// r + 4k share a 256-byte bank window, so the slot must differ across r >> 2.
+// r + 2 share a 256-byte bank window, so the slot must differ across r >> 1.
 // MN-major rows are 512 bytes (32 slots): chunk c of contraction row p sits in slot
 // c ^ swz_m(p).  A transpose read serves 4 rows x 64 bytes per 32 lanes; the rows
 // are 512 bytes apart (same banks), so the XOR moves each row's 64 bytes to its own
 // quarter of the 256-byte window.
-__device__ __forceinline__ int swz_k(int r) { return (r >> 2) & 3; }
+__device__ __forceinline__ int swz_k(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int swz_m(int p) { return (p & 3) << 2; }
 
-// s_waitcnt immediate for vmcnt(n) that leaves expcnt and lgkmcnt unconstrained
-constexpr int vm_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0f70; }
-
-// Wait until at most `tiles` tiles' worth of this wave's direct loads are in flight.
-__device__ __forceinline__ void wait_vm_tiles(int tiles) {
-  if (tiles <= 0) __builtin_amdgcn_s_waitcnt(vm_imm(0));
-  else if (tiles == 1) __builtin_amdgcn_s_waitcnt(vm_imm(kLoadsPerTile));
-  else __builtin_amdgcn_s_waitcnt(vm_imm(2 * kLoadsPerTile));
-}
-
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0f70); }
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xc07f); }
 
-constexpr int kQ = kPieces / kWaves;  // direct-load pieces per wave per operand per tile
-
-// Direct global->LDS loads of one operand, one 256 x 32 tile per contraction step.
-// A wave owns the 1 KiB pieces wave, wave + kWaves, ... of each 16 KiB operand
+// Direct global->LDS loads of one operand, one 256 x 64 tile per contraction step.
+// A wave owns the 1 KiB pieces wave, wave + kWaves, ... of each 32 KiB operand
 // stage; lane l of a piece fills bytes [16 l, 16 l + 16) of it.  Per lane the
 // global address of a piece is a fixed 32-bit offset from a wave-uniform tile base
 // that advances by `step` bytes per tile, so issuing a full tile is straight-line
@@ -128,11 +115,11 @@ struct Stream {
   const char *base;  // operand tile base for contraction tile 0
   int64_t step;      // bytes per contraction tile
   uint32_t off[kQ];  // lane byte offsets of its pieces
-  int pfirst[kQ];    // first contraction index (within the tile) a lane's piece holds
 
-  // K-major: element (r, p) at b[r * ld + p]; rows >= rv clamp to rv - 1.
-  // MN-major: element (r, p) at b[p * ld + r]; columns >= rv clamp to the last
-  // valid 8-column chunk (rv is a multiple of 8).
+  // K-major: element (r, p) at b[r * ld + p]; rows >= rv clamp to rv - 1; a piece
+  // is 8 rows x 128 bytes.  MN-major: element (r, p) at b[p * ld + r]; a piece is
+  // 2 contraction rows x 512 bytes; columns >= rv clamp to the last valid 8-column
+  // chunk (rv is a multiple of 8).
   __device__ __forceinline__ void init(const uint16_t *b, int64_t ld, int rv, int wave, int lane) {
     base = (const char *)b;
     step = KMAJ ? kBK * 2 : (int64_t)kBK * ld * 2;
@@ -140,17 +127,15 @@ struct Stream {
     for (int q = 0; q < kQ; ++q) {
       const int u = wave + kWaves * q;
       if (KMAJ) {
-        const int R = 16 * u + (lane >> 2);
-        const int c = (lane & 3) ^ swz_k(R);
+        const int R = 8 * u + (lane >> 3);
+        const int c = (lane & 7) ^ swz_k(R);
         const int r = R < rv ? R : rv - 1;
         off[q] = (uint32_t)(((int64_t)r * ld + c * 8) * 2);
-        pfirst[q] = c * 8;
       } else {
         const int prow = 2 * u + (lane >> 5);
         int col = ((lane & 31) ^ swz_m(prow)) * 8;
         col = col < rv - 8 ? col : rv - 8;
         off[q] = (uint32_t)(((int64_t)prow * ld + col) * 2);
-        pfirst[q] = prow;
       }
     }
   }
@@ -169,8 +154,11 @@ struct Stream {
     const char *tb = base + (int64_t)t * step;
 #pragma unroll
     for (int q = 0; q < kQ; ++q) {
-      char *dst = st + (wave + kWaves * q) * 1024;
-      if ((int64_t)t * kBK + pfirst[q] < pmax)
+      const int u = wave + kWaves * q;
+      char *dst = st + u * 1024;
+      // first contraction index (within the tile) this lane's piece holds
+      const int pfirst = KMAJ ? ((lane & 7) ^ swz_k(8 * u + (lane >> 3))) * 8 : 2 * u + (lane >> 5);
+      if ((int64_t)t * kBK + pfirst < pmax)
         __builtin_amdgcn_global_load_lds(tb + off[q], (GL_LDS void *)dst, 16, 0, 0);
       else
         *(uint4 *)(dst + lane * 16) = make_uint4(0, 0, 0, 0);
@@ -179,7 +167,7 @@ struct Stream {
 };
 
 // MFMA operand fragment (32 rows/columns x 16 contraction values; lane l holds row
-// l % 32, contraction values 8 * (l / 32) + 0..7) for contraction step ks of a stage.
+// l % 32, contraction values 8 (l / 32) + 0..7) for MFMA step ks of a stage.
 __device__ __forceinline__ bf16x8_t frag_kmaj(const uint16_t *st, int row0, int ks, int lane) {
   const int r = row0 + (lane & 31);
   const int c = 2 * ks + (lane >> 5);
@@ -188,8 +176,8 @@ __device__ __forceinline__ bf16x8_t frag_kmaj(const uint16_t *st, int row0, int 
 
 __device__ __forceinline__ bf16x8_t frag_mnmaj(const uint16_t *st, int col0, int ks, int lane) {
   // 16-lane groups: lanes 0-15 / 16-31 take columns 0-15 / 16-31, lane halves take
-  // contraction rows 0-7 / 8-7; lane s of a group names row (s / 4) and columns
-  // 4 (s % 4) .. + 3, and the transpose hands lane s column s of those 4 rows.
+  // contraction rows 0-7 / 8-15 of the step; lane s of a group names row s / 4 and
+  // columns 4 (s % 4) .. + 3, and the transpose hands lane s column s of those rows.
   const int s = lane & 15, grp = lane >> 4;
   const int col = col0 + ((grp & 1) << 4) + ((s & 3) << 2);
   const int chunk = col >> 3, within = col & 7;
@@ -200,15 +188,13 @@ __device__ __forceinline__ bf16x8_t frag_mnmaj(const uint16_t *st, int col0, int
     const uint16_t *a = st + prow * 256 + ((chunk ^ swz_m(prow)) << 3) + within;
     h[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GL_LDS v4i16 *)a);
   }
-  const v4i16 lo = h[0], hi = h[1];
-  typedef short v8i16 __attribute__((ext_vector_type(8)));
-  const v8i16 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  const v8i16 v = {h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
 template <bool A_KMAJ, bool B_KMAJ, int MODE>
 __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[kStages][2][kOpElems];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[2][2][kOpElems];
 
   const WsView ws = ws_view(p.ws, p.G);
   if (!ws_usable(ws.hdr, p.G, p.T)) return;
@@ -236,22 +222,17 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
       local = w - g * per;
       MT = p.tiles_i;
     }
-    int it, jt;
-    if (GL_TILE_ORDER == 0) {
-      it = local % MT;
-      jt = local / MT;
-    } else {
-      // bands of kOrdN tile columns; inside a band, blocks of kOrdM tile rows;
-      // inside a block, row tiles fastest
-      const int cb = local / (MT * kOrdN);
-      const int bw = min(kOrdN, NT - cb * kOrdN);
-      const int l2 = local - cb * MT * kOrdN;
-      const int rb = l2 / (kOrdM * bw);
-      const int h = min(kOrdM, MT - rb * kOrdM);
-      const int l3 = l2 - rb * kOrdM * bw;
-      it = rb * kOrdM + l3 % h;
-      jt = cb * kOrdN + l3 / h;
-    }
+    // bands of kOrdN tile columns; inside a band, blocks of kOrdM tile rows; inside
+    // a block, row tiles fastest
+    const int cb = local / (MT * kOrdN);
+    const int bw = min(kOrdN, NT - cb * kOrdN);
+    const int l2 = local - cb * MT * kOrdN;
+    const int rb = l2 / (kOrdM * bw);
+    const int bh = min(kOrdM, MT - rb * kOrdM);
+    const int l3 = l2 - rb * kOrdM * bw;
+    const int it = rb * kOrdM + l3 % bh;
+    const int jt = cb * kOrdN + l3 / bh;
+
     const int64_t g_off = off[g];
     const int64_t g_rows = off[g + 1] - g_off;
     if (MODE == MODE_CONTR && p.accumulate && g_rows == 0) continue;  // main_grad untouched
@@ -274,16 +255,15 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
       pmax = g_rows;
     }
     const int nk = (int)((pmax + kBK - 1) / kBK);
+    const int nfull = (int)(pmax / kBK);  // tiles [0, nfull) are complete; nk - nfull <= 1
 
     Stream<A_KMAJ> sa;
     Stream<B_KMAJ> sb;
     sa.init(a_base, p.lda, a_rv, wave, lane);
     sb.init(b_base, p.ldb, b_rv, wave, lane);
     char *const ring = (char *)&lds[0][0][0];
-    constexpr int kStageBytes = 2 * kOpElems * 2, kOpBytes = kOpElems * 2;
-    const int nfull = (int)(pmax / kBK);  // tiles [0, nfull) are complete; nk - nfull <= 1
     auto issue = [&](int t) {
-      char *st = ring + (t % kStages) * kStageBytes;
+      char *st = ring + (t & 1) * 2 * kOpBytes;
       if (t < nfull) {
         sa.issue_full(t, st, wave);
         sb.issue_full(t, st + kOpBytes, wave);
@@ -291,13 +271,6 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
         sa.issue_masked(t, pmax, st, wave, lane);
         sb.issue_masked(t, pmax, st + kOpBytes, wave, lane);
       }
-    };
-    // Tiles in (lo, hi] whose loads may still be in flight when every tile up to
-    // lo must have landed: only complete tiles count, since a masked tile may
-    // have issued fewer loads.
-    auto inflight_after = [&](int lo, int hi) {
-      const int top = min(hi, nfull - 1);
-      return top > lo ? top - lo : 0;
     };
 
     // -------------------------------------------------------------- main loop
@@ -310,8 +283,8 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
         for (int q = 0; q < 16; ++q) acc[ii][jj][q] = 0.f;
 
     auto load_frags = [&](int t, int ks, bf16x8_t *af, bf16x8_t *bfr) {
-      const uint16_t *ta = lds[t % kStages][0];
-      const uint16_t *tb = lds[t % kStages][1];
+      const uint16_t *ta = lds[t & 1][0];
+      const uint16_t *tb = lds[t & 1][1];
 #pragma unroll
       for (int ii = 0; ii < kNI; ++ii)
         af[ii] = A_KMAJ ? frag_kmaj(ta, wm * kWTM + ii * 32, ks, lane) : frag_mnmaj(ta, wm * kWTM + ii * 32, ks, lane);
@@ -328,62 +301,42 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
           acc[ii][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[jj], af[ii], acc[ii][jj], 0, 0, 0);
     };
 
-    // Pipeline: tiles are issued kStages - 1 ahead; the barrier closing iteration
-    // kt guarantees tile kt + 2 has landed, so tile kt + 1's first fragments are
-    // read during tile kt's last MFMAs and the MFMAs resume right after each
-    // barrier.  One barrier per tile.
-#pragma unroll
-    for (int s = 0; s < kStages - 1; ++s)
-      if (s < nk) issue(s);
-    bf16x8_t f0a[kNI], f0b[kNJ], f1a[kNI], f1b[kNJ];
+    bf16x8_t fa[2][kNI], fb[2][kNJ];
     if (nk > 0) {
-      wait_vm_tiles(inflight_after(min(1, nk - 1), min(2, nk - 1)));
+      issue(0);
+      wait_vm0();
       wait_lgkm0();
       __builtin_amdgcn_s_barrier();
-      load_frags(0, 0, f0a, f0b);
+      load_frags(0, 0, fa[0], fb[0]);
     }
-    int kt = 0;
-    // steady state: the tile issued this iteration is complete and a next tile
-    // exists -- straight-line code, scheduled as interleaved MFMA / memory groups
-    for (; kt + kStages - 1 < nfull; ++kt) {
-      char *st = ring + ((kt + kStages - 1) % kStages) * kStageBytes;
-      sa.issue_full(kt + kStages - 1, st, wave);
-      sb.issue_full(kt + kStages - 1, st + kOpBytes, wave);
-      load_frags(kt, 1, f1a, f1b);
-      mfmas(f0a, f0b);
-      load_frags(kt + 1, 0, f0a, f0b);
-      mfmas(f1a, f1b);
-      if (GL_INTERLEAVE) {
-        // 16 MFMAs; between them the 2 kQ direct loads and the 2 (kNI + kNJ)
-        // fragment reads (fragment reads of tile kt + 1 can only follow the
-        // eighth MFMA, the last reader of the registers they refill)
-#pragma unroll
-        for (int i = 0; i < 2 * kQ; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-#pragma unroll
-        for (int i = 2 * kQ; i < 16; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
+    // One tile per iteration; fragment set (ks & 1) feeds MFMA step ks while set
+    // (ks + 1) & 1 is refilled.  The barrier before the last step makes tile kt + 1
+    // visible and frees the stage tile kt - 1 used for the loads of tile kt + 2.
+    static_assert((kKS & 1) == 0, "step 0 of every tile must read fragment set 0");
+    auto body = [&](int kt, bool steady) {
+      if (steady) {
+        char *st = ring + ((kt + 1) & 1) * 2 * kOpBytes;
+        sa.issue_full(kt + 1, st, wave);
+        sb.issue_full(kt + 1, st + kOpBytes, wave);
+      } else if (kt + 1 < nk) {
+        issue(kt + 1);
       }
-      wait_vm_tiles(1);
+#pragma unroll
+      for (int ks = 0; ks < kKS - 1; ++ks) {
+        load_frags(kt, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+        mfmas(fa[ks & 1], fb[ks & 1]);
+      }
+      wait_vm0();
       wait_lgkm0();
       __builtin_amdgcn_s_barrier();
-    }
-    for (; kt < nk; ++kt) {
-      if (kt + kStages - 1 < nk) issue(kt + kStages - 1);
-      load_frags(kt, 1, f1a, f1b);
-      mfmas(f0a, f0b);
-      if (kt + 1 < nk) load_frags(kt + 1, 0, f0a, f0b);
-      mfmas(f1a, f1b);
-      wait_vm_tiles(inflight_after(kt + 2, min(kt + kStages - 1, nk - 1)));
-      wait_lgkm0();
-      __builtin_amdgcn_s_barrier();
-    }
-    __builtin_amdgcn_s_barrier();  // every wave is done with the ring before it is refilled
+      if (steady || kt + 1 < nk) load_frags(kt + 1, 0, fa[0], fb[0]);
+      mfmas(fa[(kKS - 1) & 1], fb[(kKS - 1) & 1]);
+    };
+
+    int kt = 0;
+    for (; kt + 1 < nfull; ++kt) body(kt, true);  // tile kt + 1 complete: straight-line body
+    for (; kt < nk; ++kt) body(kt, false);
+    __builtin_amdgcn_s_barrier();  // every wave is done with the stages before they are refilled
 
     // --------------------------------------------------------------- epilogue
     // lane holds C[i][j..j+3] with i = ii*32 + lane%32, j = jj*32 + q4*8 + (lane/32)*4
@@ -461,13 +414,13 @@ static int persistent_grid(int64_t max_items) {
   return (int)(g > 0 ? g : 1);
 }
 
-}  // namespace v2
+}  // namespace mfma_bf16
 
 // forward: y = x W^T (+ b); A = x [T,K], B = W [N,K]
 hipError_t launch_forward_bf16(int G, int64_t K, int64_t N, int64_t T, const uint16_t *x, const uint16_t *w,
                                const uint16_t *const *w_ptrs, const void *bias, const void *const *bias_ptrs,
                                uint16_t *y, const void *ws, hipStream_t s) {
-  using namespace v2;
+  using namespace mfma_bf16;
   Params p{};
   p.A = x; p.lda = K;
   p.B = w; p.B_ptrs = w_ptrs; p.b_gstride = N * K; p.ldb = K;
@@ -485,7 +438,7 @@ hipError_t launch_forward_bf16(int G, int64_t K, int64_t N, int64_t T, const uin
 // dgrad: dx = dy W; A = dy [T,N] (n contiguous), B[j=k][p=n] = W[n][k] (k contiguous)
 hipError_t launch_dgrad_bf16(int G, int64_t K, int64_t N, int64_t T, const uint16_t *dy, const uint16_t *w,
                              const uint16_t *const *w_ptrs, uint16_t *dx, const void *ws, hipStream_t s) {
-  using namespace v2;
+  using namespace mfma_bf16;
   Params p{};
   p.A = dy; p.lda = N;
   p.B = w; p.B_ptrs = w_ptrs; p.b_gstride = N * K; p.ldb = K;
@@ -503,7 +456,7 @@ hipError_t launch_dgrad_bf16(int G, int64_t K, int64_t N, int64_t T, const uint1
 hipError_t launch_wgrad_bf16(int G, int64_t K, int64_t N, int64_t T, const uint16_t *x, const uint16_t *dy,
                              void *dw, void *const *dw_ptrs, int out_f32, int accumulate, const void *ws,
                              hipStream_t s) {
-  using namespace v2;
+  using namespace mfma_bf16;
   Params p{};
   p.A = dy; p.lda = N;
   p.B = x; p.ldb = K;
