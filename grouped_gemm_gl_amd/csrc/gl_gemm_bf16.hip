@@ -87,6 +87,11 @@ struct Params {
   int tiles_i, tiles_j;
   int accumulate;
   int out_f32;
+  // MXFP8 forward only: E8M0 scales, one byte per 32 codes of a row
+  const uint8_t *a_scale;              // [T, K/32]
+  const uint8_t *b_scale;              // [G, N, K/32] stacked, or
+  const uint8_t *const *b_scale_ptrs;  // per-group [N, K/32]
+  int64_t scale_ld;                    // K / 32
 };
 
 // 16-byte slot swizzles for gfx950's LDS (64 banks of 4 bytes; a 16-byte read
@@ -192,9 +197,23 @@ __device__ __forceinline__ bf16x8_t frag_mnmaj(const uint16_t *st, int col0, int
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
-template <bool A_KMAJ, bool B_KMAJ, int MODE>
+// MXFP8 operand fragment for the scaled 32x32x64 MFMA, step s (64 codes) of a
+// 128-code K-major row: lane l holds row l % 32 and, for each of the step's two
+// 32-code scale blocks, 16 codes -- those at byte 16 (l / 32) of the block.
+__device__ __forceinline__ i32x8_t frag_mx(const uint16_t *st, int row0, int s, int lane) {
+  const int r = row0 + (lane & 31), h = lane >> 5;
+  const i32x4_t lo = *(const i32x4_t *)(st + r * kBK + (((4 * s + h) ^ swz_k(r)) << 3));
+  const i32x4_t hi = *(const i32x4_t *)(st + r * kBK + (((4 * s + 2 + h) ^ swz_k(r)) << 3));
+  return (i32x8_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// MX == true: the MXFP8 forward.  Operands are E4M3 codes handled as two-byte
+// units (a 128-byte tile row is 128 codes = 4 scale blocks); each tile also brings
+// the 4 scale bytes of every A and B row into a small LDS area.
+template <bool A_KMAJ, bool B_KMAJ, int MODE, bool MX>
 __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
   __shared__ __attribute__((aligned(1024))) uint16_t lds[2][2][kOpElems];
+  __shared__ __attribute__((aligned(1024))) uint32_t lds_sc[2][2][256];  // MXFP8 scale dwords per row
 
   const WsView ws = ws_view(p.ws, p.G);
   if (!ws_usable(ws.hdr, p.G, p.T)) return;
@@ -262,6 +281,26 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
     sa.init(a_base, p.lda, a_rv, wave, lane);
     sb.init(b_base, p.ldb, b_rv, wave, lane);
     char *const ring = (char *)&lds[0][0][0];
+    // MXFP8: wave w loads the scale dwords (4 blocks = one tile) of 64 rows per
+    // tile -- waves 0-3 the A rows, waves 4-7 the B rows
+    const char *sc_base = nullptr;
+    uint32_t sc_off = 0;
+    if (MX) {
+      const int r = (wave & 3) * 64 + lane;
+      if (wave < 4) {
+        sc_base = (const char *)p.a_scale + (g_off + (int64_t)it * kBM) * p.scale_ld;
+        sc_off = (uint32_t)((r < a_rv ? r : a_rv - 1) * p.scale_ld);
+      } else {
+        const uint8_t *bs = p.b_scale ? p.b_scale + (int64_t)g * p.cols_j * p.scale_ld : p.b_scale_ptrs[g];
+        sc_base = (const char *)bs + (int64_t)jt * kBN * p.scale_ld;
+        sc_off = (uint32_t)((r < b_rv ? r : b_rv - 1) * p.scale_ld);
+      }
+    }
+    auto issue_scales = [&](int t) {
+      if (MX)
+        __builtin_amdgcn_global_load_lds(sc_base + sc_off + 4 * t,
+                                         (GL_LDS void *)&lds_sc[t & 1][wave >> 2][(wave & 3) * 64], 4, 0, 0);
+    };
     auto issue = [&](int t) {
       char *st = ring + (t & 1) * 2 * kOpBytes;
       if (t < nfull) {
@@ -271,6 +310,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
         sa.issue_masked(t, pmax, st, wave, lane);
         sb.issue_masked(t, pmax, st + kOpBytes, wave, lane);
       }
+      issue_scales(t);
     };
 
     // -------------------------------------------------------------- main loop
@@ -301,6 +341,44 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
           acc[ii][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[jj], af[ii], acc[ii][jj], 0, 0, 0);
     };
 
+    if constexpr (MX) {
+      // two scaled 32x32x64 steps per tile; per step the two B fragments are read
+      // first and the A fragments streamed one at a time (32-byte fragments leave
+      // no room for a second fragment set)
+      auto step_mx = [&](int t, int st_, const uint32_t *scl) {
+        const int sh = 8 * (2 * st_ + (lane >> 5));  // this lane's scale block in the step
+        i32x8_t bfr[kNJ];
+#pragma unroll
+        for (int jj = 0; jj < kNJ; ++jj) bfr[jj] = frag_mx(lds[t & 1][1], wn * kWTN + jj * 32, st_, lane);
+#pragma unroll
+        for (int ii = 0; ii < kNI; ++ii) {
+          const i32x8_t af = frag_mx(lds[t & 1][0], wm * kWTM + ii * 32, st_, lane);
+#pragma unroll
+          for (int jj = 0; jj < kNJ; ++jj)
+            acc[ii][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                bfr[jj], af, acc[ii][jj], 0, 0, 0, (int)(scl[kNI + jj] >> sh), 0, (int)(scl[ii] >> sh));
+        }
+      };
+      if (nk > 0) {
+        issue(0);
+        wait_vm0();
+        wait_lgkm0();
+        __builtin_amdgcn_s_barrier();
+      }
+      for (int kt = 0; kt < nk; ++kt) {
+        if (kt + 1 < nk) issue(kt + 1);
+        uint32_t sc[kNI + kNJ];  // scale dwords of this lane's A and B rows for tile kt
+#pragma unroll
+        for (int ii = 0; ii < kNI; ++ii) sc[ii] = lds_sc[kt & 1][0][wm * kWTM + ii * 32 + (lane & 31)];
+#pragma unroll
+        for (int jj = 0; jj < kNJ; ++jj) sc[kNI + jj] = lds_sc[kt & 1][1][wn * kWTN + jj * 32 + (lane & 31)];
+        step_mx(kt, 0, sc);
+        step_mx(kt, 1, sc);
+        wait_vm0();
+        wait_lgkm0();
+        __builtin_amdgcn_s_barrier();
+      }
+    } else {
     bf16x8_t fa[2][kNI], fb[2][kNJ];
     if (nk > 0) {
       issue(0);
@@ -336,6 +414,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
     int kt = 0;
     for (; kt + 1 < nfull; ++kt) body(kt, true);  // tile kt + 1 complete: straight-line body
     for (; kt < nk; ++kt) body(kt, false);
+    }
     __builtin_amdgcn_s_barrier();  // every wave is done with the stages before they are refilled
 
     // --------------------------------------------------------------- epilogue
@@ -430,7 +509,7 @@ hipError_t launch_forward_bf16(int G, int64_t K, int64_t N, int64_t T, const uin
   p.cols_j = N; p.P = K;
   p.tiles_j = (int)((N + kBN - 1) / kBN);
   const int64_t max_items = ((T + kBM - 1) / kBM + G) * p.tiles_j;
-  hipLaunchKernelGGL((gemm_bf16_kernel<true, true, MODE_ROWS>), dim3(persistent_grid(max_items)), dim3(kThreads), 0,
+  hipLaunchKernelGGL((gemm_bf16_kernel<true, true, MODE_ROWS, false>), dim3(persistent_grid(max_items)), dim3(kThreads), 0,
                      s, p);
   return hipGetLastError();
 }
@@ -447,7 +526,7 @@ hipError_t launch_dgrad_bf16(int G, int64_t K, int64_t N, int64_t T, const uint1
   p.cols_j = K; p.P = N;
   p.tiles_j = (int)((K + kBN - 1) / kBN);
   const int64_t max_items = ((T + kBM - 1) / kBM + G) * p.tiles_j;
-  hipLaunchKernelGGL((gemm_bf16_kernel<true, false, MODE_ROWS>), dim3(persistent_grid(max_items)), dim3(kThreads), 0,
+  hipLaunchKernelGGL((gemm_bf16_kernel<true, false, MODE_ROWS, false>), dim3(persistent_grid(max_items)), dim3(kThreads), 0,
                      s, p);
   return hipGetLastError();
 }
@@ -468,8 +547,33 @@ hipError_t launch_wgrad_bf16(int G, int64_t K, int64_t N, int64_t T, const uint1
   p.accumulate = accumulate;
   p.out_f32 = out_f32;
   const int64_t max_items = (int64_t)G * p.tiles_i * p.tiles_j;
-  hipLaunchKernelGGL((gemm_bf16_kernel<false, false, MODE_CONTR>), dim3(persistent_grid(max_items)), dim3(kThreads),
+  hipLaunchKernelGGL((gemm_bf16_kernel<false, false, MODE_CONTR, false>), dim3(persistent_grid(max_items)), dim3(kThreads),
                      0, s, p);
+  return hipGetLastError();
+}
+
+// MXFP8 forward: y = deq(xq) deq(wq)^T (+ b).  Codes travel as two-byte units, so
+// the loads see K/2 units per row; K % 128 == 0 keeps every tile whole and the
+// per-tile scale dwords aligned.
+hipError_t launch_forward_mxfp8(int G, int64_t K, int64_t N, int64_t T, const uint8_t *xq, const uint8_t *xs,
+                                const uint8_t *wq, const uint8_t *const *wq_ptrs, const uint8_t *ws_scale,
+                                const uint8_t *const *ws_scale_ptrs, const void *bias,
+                                const void *const *bias_ptrs, void *y, int out_f32, const void *ws,
+                                hipStream_t s) {
+  using namespace mfma_bf16;
+  Params p{};
+  p.A = (const uint16_t *)xq; p.lda = K / 2;
+  p.B = (const uint16_t *)wq; p.B_ptrs = (const uint16_t *const *)wq_ptrs; p.b_gstride = N * K / 2; p.ldb = K / 2;
+  p.C = y; p.ldc = N;
+  p.bias = bias; p.bias_ptrs = bias_ptrs;
+  p.ws = ws; p.G = G; p.T = T;
+  p.cols_j = N; p.P = K / 2;
+  p.tiles_j = (int)((N + kBN - 1) / kBN);
+  p.out_f32 = out_f32;
+  p.a_scale = xs; p.b_scale = ws_scale; p.b_scale_ptrs = ws_scale_ptrs; p.scale_ld = K / 32;
+  const int64_t max_items = ((T + kBM - 1) / kBM + G) * p.tiles_j;
+  hipLaunchKernelGGL((gemm_bf16_kernel<true, true, MODE_ROWS, true>), dim3(persistent_grid(max_items)),
+                     dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 
