@@ -30,7 +30,14 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 / MXFP8 MFMA
 PEAK_HBM_GBS = 8000.0
 METRIC = "grouped GEMM TFLOP/s (fwd+dgrad+wgrad) and % of MFMA peak, bf16 & MXFP8"
-GEMM_SRC = os.path.join(ROOT, "grouped_gemm_gl_amd", "csrc", "gl_gemm_mfma.hip")
+GEMM_SRC = os.path.join(ROOT, "grouped_gemm_gl_amd", "csrc", "gl_gemm_bf16.hip")
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+# template arguments <A K-major, B K-major, mode, MXFP8> of each pass's GEMM kernel
+PASS_KERNELS = {"forward": "true, true, 0, false", "dgrad": "true, false, 0, false",
+                "wgrad": "false, false, 1, false", "mx_forward": "true, true, 0, true"}
+PASS_WORKLOAD = {"forward": "bf16_train_g8_k4096_n14336", "dgrad": "bf16_train_g8_k4096_n14336",
+                 "wgrad": "bf16_train_g8_k4096_n14336", "mx_forward": "mxfp8_fwd_g32_k4096_n4096"}
+COPY_BYTES = 1 << 30
 
 
 def log(*a):
@@ -44,14 +51,75 @@ def source_hash(path: str) -> str:
 def traffic_for(kernel: str, workload: str):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were taken
     on the current kernel source; otherwise None."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
-        rec = json.load(open(path))[f"{workload}:{kernel}"]
+        rec = json.load(open(TRAFFIC_JSON))[f"{workload}:{kernel}"]
     except Exception:
         return None
     if rec.get("source_sha") != source_hash(GEMM_SRC):
         return None
     return rec.get("bytes_per_launch")
+
+
+def calibrate_copy():
+    """A plain 1 GiB device-to-device copy, three times: the known-size workload
+    that scales the FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    import torch
+
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "launches": 3}))
+
+
+def _pmc_rows(path, counter):
+    import csv
+
+    out = []
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] == counter:
+            out.append((r["Kernel_Name"], float(r["Counter_Value"]),
+                        int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    return out
+
+
+def summarize_pmc(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
+    """Turn two rocprofv3 --pmc runs of the benchmark (FETCH_SIZE, WRITE_SIZE, in KiB
+    per dispatch) into HBM bytes per launch of each pass's GEMM kernel, each counter
+    scaled by what it reads for the plain copy of known size; writes the result into
+    the traffic table keyed by workload and pass, with the kernel source hash."""
+
+    def copy_factor(path, counter):
+        vals = [v for k, v, _ in _pmc_rows(path, counter) if "copy" in k.lower()]
+        if not vals:
+            raise SystemExit(f"no copy kernel with {counter} in {path}")
+        return COPY_BYTES / (sum(vals) / len(vals) * 1024.0)
+
+    ff = copy_factor(copy_fetch_csv, "FETCH_SIZE")
+    fw = copy_factor(copy_write_csv, "WRITE_SIZE")
+    table = json.load(open(TRAFFIC_JSON)) if os.path.exists(TRAFFIC_JSON) else {}
+    sha = source_hash(GEMM_SRC)
+    lines = [f"copy calibration ({COPY_BYTES} B): FETCH_SIZE x{ff:.3f}, WRITE_SIZE x{fw:.3f}"]
+    for name, args in PASS_KERNELS.items():
+        sel = lambda rows: [v for k, v, _ in rows if f"gemm_bf16_kernel<{args}>" in k]
+        fv, wv = sel(_pmc_rows(fetch_csv, "FETCH_SIZE")), sel(_pmc_rows(write_csv, "WRITE_SIZE"))
+        if not fv or not wv:
+            continue
+        fb = sum(fv) / len(fv) * 1024.0 * ff
+        wb = sum(wv) / len(wv) * 1024.0 * fw
+        workload = PASS_WORKLOAD[name]
+        table[f"{workload}:{name}"] = {"bytes_per_launch": round(fb + wb), "fetch_bytes": round(fb),
+                                        "write_bytes": round(wb), "launches": len(fv), "source_sha": sha,
+                                        "fetch_factor": round(ff, 4), "write_factor": round(fw, 4)}
+        lines.append(f"{workload}:{name}: fetch {fb / 1e9:.3f} GB + write {wb / 1e9:.3f} GB per launch "
+                     f"({len(fv)} launches)")
+    os.makedirs(os.path.dirname(TRAFFIC_JSON), exist_ok=True)
+    with open(TRAFFIC_JSON, "w") as f:
+        json.dump(table, f, indent=1, sort_keys=True)
+    print("\n".join(lines))
 
 
 class EventTimer:
@@ -171,7 +239,7 @@ def bench_bf16(torch, gl, synth, steps, warmup):
         passes[k] = d
     dom = max(("forward", "dgrad", "wgrad"), key=lambda k: per[k])
     achieved = flops_pass / (per[dom] * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "kernel": f"gemm_mfma_kernel ({dom})", "achieved": round(achieved, 2),
+    roofline = {"bound": "mfma", "kernel": f"gemm_bf16_kernel<{PASS_KERNELS[dom]}> ({dom})", "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic_for(dom, wl.name),
                 "algorithmic_flops_per_launch": flops_pass}
@@ -214,6 +282,7 @@ def bench_mxfp8(torch, gl, synth, steps, warmup):
         "workload": wl.name,
         "mx_forward_ms": round(per["mx_forward"], 4),
         "mx_forward_tflops": round(tf, 2),
+        "mx_forward_traffic": traffic_for("mx_forward", wl.name),
         "pct_fp8_peak": round(100 * tf / PEAK_FP8_TFLOPS, 2),
         "quantize_x_ms": round(per["quantize_x"], 4),
         "quantize_x_gbs": round(qx_bytes / (per["quantize_x"] * 1e-3) / 1e9, 1),
@@ -231,12 +300,22 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-mxfp8", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB copy (counter calibration)")
+    ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="fold rocprofv3 FETCH_SIZE/WRITE_SIZE CSVs into the traffic table, then exit")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(groups would shard across GPUs as expert parallelism; see the design notes).", file=sys.stderr)
         sys.exit(2)
 
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     import torch
     import grouped_gemm_gl_amd as gl
     import synth
