@@ -97,10 +97,17 @@ int check_buf(const void *p, int64_t T, const char *what) {
   return GL_OK;
 }
 
+// The bf16 GEMM addresses a 256-row stage of an operand with 32-bit byte offsets
+// from the stage's base, so a row may hold at most 2^22 elements.
+constexpr int64_t kMaxBf16Dim = (int64_t)1 << 22;
+
 int check_bf16_dims(gl_dtype d, int64_t K, int64_t N) {
   if (d == GL_BF16 && (K % 8 || N % 8))
     return fail(GL_ERR_SHAPE, "bf16 needs in_features and out_features that are multiples of 8 (got %lld, %lld)",
                 (long long)K, (long long)N);
+  if (d == GL_BF16 && (K > kMaxBf16Dim || N > kMaxBf16Dim))
+    return fail(GL_ERR_SHAPE, "bf16 in_features and out_features must be at most %lld (got %lld, %lld)",
+                (long long)kMaxBf16Dim, (long long)K, (long long)N);
   return GL_OK;
 }
 

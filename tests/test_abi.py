@@ -64,6 +64,7 @@ def fwd(G=4, K=64, N=32, T=32, ind=gl.GL_BF16, outd=gl.GL_BF16, x=FAKE, xs=None,
     (dict(ind=gl.GL_BF16, outd=gl.GL_F32), -2),
     (dict(ind=7, outd=7), -2),
     (dict(K=60), -3), (dict(N=36), -3),             # bf16 rows must be 16-byte multiples
+    (dict(K=(1 << 22) + 8), -3), (dict(N=(1 << 22) + 8), -3),  # bf16 rows above 2^22 elements
     (dict(ind=gl.GL_E4M3, outd=gl.GL_BF16, K=96), -3),
     (dict(ind=gl.GL_E4M3, outd=gl.GL_BF16, K=128, xs=None), -1),
     (dict(ind=gl.GL_E4M3, outd=gl.GL_E4M3, K=128, xs=FAKE), -2),
