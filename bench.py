@@ -30,11 +30,12 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 / MXFP8 MFMA
 PEAK_HBM_GBS = 8000.0
 METRIC = "grouped GEMM TFLOP/s (fwd+dgrad+wgrad) and % of MFMA peak, bf16 & MXFP8"
-GEMM_SRC = os.path.join(ROOT, "grouped_gemm_gl_amd", "csrc", "gl_gemm_bf16.hip")
+GEMM_SRCS = [os.path.join(ROOT, "grouped_gemm_gl_amd", "csrc", f)
+             for f in ("gl_gemm_tile.hpp", "gl_gemm_bf16.hip", "gl_gemm_mxfp8.hip")]
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
-# template arguments <A K-major, B K-major, mode, MXFP8> of each pass's GEMM kernel
-PASS_KERNELS = {"forward": "true, true, 0, false", "dgrad": "true, false, 0, false",
-                "wgrad": "false, false, 1, false", "mx_forward": "true, true, 0, true"}
+# kernel-name fragment of each pass's GEMM (template arguments <A K-major, B K-major, mode>)
+PASS_KERNELS = {"forward": "gemm_bf16_kernel<true, true, 0>", "dgrad": "gemm_bf16_kernel<true, false, 0>",
+                "wgrad": "gemm_bf16_kernel<false, false, 1>", "mx_forward": "gemm_mxfp8_kernel"}
 PASS_WORKLOAD = {"forward": "bf16_train_g8_k4096_n14336", "dgrad": "bf16_train_g8_k4096_n14336",
                  "wgrad": "bf16_train_g8_k4096_n14336", "mx_forward": "mxfp8_fwd_g32_k4096_n4096"}
 COPY_BYTES = 1 << 30
@@ -44,8 +45,11 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def source_hash(path: str) -> str:
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+def source_hash(paths) -> str:
+    h = hashlib.sha256()
+    for path in paths:
+        h.update(open(path, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def traffic_for(kernel: str, workload: str):
@@ -55,7 +59,7 @@ def traffic_for(kernel: str, workload: str):
         rec = json.load(open(TRAFFIC_JSON))[f"{workload}:{kernel}"]
     except Exception:
         return None
-    if rec.get("source_sha") != source_hash(GEMM_SRC):
+    if rec.get("source_sha") != source_hash(GEMM_SRCS):
         return None
     return rec.get("bytes_per_launch")
 
@@ -101,10 +105,10 @@ def summarize_pmc(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
     ff = copy_factor(copy_fetch_csv, "FETCH_SIZE")
     fw = copy_factor(copy_write_csv, "WRITE_SIZE")
     table = json.load(open(TRAFFIC_JSON)) if os.path.exists(TRAFFIC_JSON) else {}
-    sha = source_hash(GEMM_SRC)
+    sha = source_hash(GEMM_SRCS)
     lines = [f"copy calibration ({COPY_BYTES} B): FETCH_SIZE x{ff:.3f}, WRITE_SIZE x{fw:.3f}"]
     for name, args in PASS_KERNELS.items():
-        sel = lambda rows: [v for k, v, _ in rows if f"gemm_bf16_kernel<{args}>" in k]
+        sel = lambda rows: [v for k, v, _ in rows if args in k]
         fv, wv = sel(_pmc_rows(fetch_csv, "FETCH_SIZE")), sel(_pmc_rows(write_csv, "WRITE_SIZE"))
         if not fv or not wv:
             continue
@@ -239,7 +243,7 @@ def bench_bf16(torch, gl, synth, steps, warmup):
         passes[k] = d
     dom = max(("forward", "dgrad", "wgrad"), key=lambda k: per[k])
     achieved = flops_pass / (per[dom] * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "kernel": f"gemm_bf16_kernel<{PASS_KERNELS[dom]}> ({dom})", "achieved": round(achieved, 2),
+    roofline = {"bound": "mfma", "kernel": f"{PASS_KERNELS[dom]} ({dom})", "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic_for(dom, wl.name),
                 "algorithmic_flops_per_launch": flops_pass}

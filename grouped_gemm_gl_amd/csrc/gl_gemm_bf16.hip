@@ -45,217 +45,14 @@
 // neighbouring tiles (8 x 4 blocks of output tiles) that share operand panels in
 // its L2.  In row mode the item -> (group, row tile, column tile) map comes from
 // the row-tile prefix table the offsets kernel left in the workspace.
-#include "gl_common.hpp"
-
-// Stage depth and ring length (tuning parameters; 64 x 2 measured best on MI355X)
-#ifndef GL_BK
-#define GL_BK 64
-#endif
-#ifndef GL_STAGES
-#define GL_STAGES 2
-#endif
+#include "gl_gemm_tile.hpp"
 
 namespace gl {
 
-namespace gemm_bf16 {
-
-constexpr int kBM = 256, kBN = 256;
-constexpr int kWaves = 8, kThreads = 64 * kWaves;
-constexpr int kWN = kWaves / 2;                     // wave grid 2 x 4
-constexpr int kWTM = kBM / 2, kWTN = kBN / kWN;     // wave tile
-constexpr int kNI = kWTM / 32, kNJ = kWTN / 32;     // 32x32 MFMA blocks per wave
-constexpr int kBK = GL_BK;                          // contraction depth of a stage
-constexpr int kS = GL_STAGES;                       // stages in the LDS ring
-constexpr int kKS = kBK / 16;                       // MFMA steps per stage
-constexpr int kRowB = 2 * kBK;                      // bytes of a K-major stage row
-constexpr int kChunks = kRowB / 16;                 // 16-byte chunks per K-major row
-constexpr int kRowsPerPiece = 1024 / kRowB;         // K-major rows per 1 KiB piece
-constexpr int kOpBytes = 256 * kRowB;               // bytes per operand per stage
-constexpr int kStageBytes = 2 * kOpBytes;
-constexpr int kQ = kOpBytes / 1024 / kWaves;        // pieces per wave per operand per stage
-constexpr int kLoadsPerStage = 2 * kQ;              // direct loads per wave per stage
-constexpr int kOrdM = 8, kOrdN = 4;                 // blocked work-item order
-static_assert(kBK == 32 || kBK == 64, "stage depth");
-static_assert(kS >= 2 && kS * kStageBytes <= 160 * 1024, "LDS ring");
-static_assert((kS - 2) * kLoadsPerStage <= 63, "vmcnt range");
-
-enum { MODE_ROWS = 0, MODE_CONTR = 1 };
-
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef short v8i16 __attribute__((ext_vector_type(8)));
-#define GL_LDS __attribute__((address_space(3)))
-
-struct Params {
-  const uint16_t *A;
-  int64_t lda;
-  const uint16_t *B;
-  const uint16_t *const *B_ptrs;
-  int64_t b_gstride;
-  int64_t ldb;
-  void *C;
-  void *const *C_ptrs;
-  int64_t c_gstride;
-  int64_t ldc;
-  const void *bias;
-  const void *const *bias_ptrs;
-  const void *ws;
-  int G;
-  int64_t T;
-  int64_t rows_i, cols_j, P;
-  int tiles_i, tiles_j;
-  int accumulate;
-  int out_f32;
-};
-
-// 16-byte slot swizzles for gfx950's LDS (64 banks of 4 bytes; a 16-byte read
-// serves 16 lanes per cycle, an 8-byte read 32 lanes).
-// K-major rows hold kChunks slots: chunk c of row r sits in slot c ^ swz_k(r).  A
-// fragment read takes one chunk of 16 consecutive rows per cycle; 16 / kChunks
-// consecutive rows share a 256-byte bank window, so the slot must differ across
-// r / (16 / kChunks).
-// MN-major rows are 512 bytes (32 slots): chunk c of contraction row p sits in slot
-// c ^ swz_m(p).  A transpose read serves 4 rows x 64 bytes per 32 lanes; the rows
-// are 512 bytes apart (same banks), so the XOR moves each row's 64 bytes to its own
-// quarter of the 256-byte window.
-__device__ __forceinline__ int swz_k(int r) { return (r / (16 / kChunks)) & (kChunks - 1); }
-__device__ __forceinline__ int swz_m(int p) { return (p & 3) << 2; }
-
-__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0f70); }
-__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xc07f); }
-// s_waitcnt vmcnt(n) (lgkmcnt and expcnt left at their maxima), gfx9 encoding
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N <= 63, "vmcnt");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70);
-}
-
-// Buffer resource over [base, base + 2 GiB): raw (unswizzled, stride 0) addressing,
-// gfx9 data format word.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_at(const char *base) {
-  return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, 0x7fffffff, 0x00020000);
-}
-
-// Direct buffer->LDS loads of one operand, one 256 x kBK tile per stage.  A wave
-// owns the 1 KiB pieces wave, wave + kWaves, ... of each operand stage; lane l of a
-// piece fills bytes [16 l, 16 l + 16) of it.
-template <bool KMAJ>
-struct Stream {
-  const char *base;  // operand tile base for contraction stage 0
-  int64_t step;      // bytes per contraction stage
-  uint32_t off[kQ];  // lane byte offsets of its pieces from the stage's base
-
-  // K-major: element (r, p) at b[r * ld + p]; rows >= rv clamp to rv - 1; a piece
-  // is kRowsPerPiece rows x kRowB bytes.  MN-major: element (r, p) at b[p * ld + r];
-  // a piece is 2 contraction rows x 512 bytes; columns >= rv clamp to the last
-  // valid 8-column chunk (rv is a multiple of 8).
-  __device__ __forceinline__ void init(const uint16_t *b, int64_t ld, int rv, int wave, int lane) {
-    base = (const char *)b;
-    step = KMAJ ? kRowB : (int64_t)kBK * ld * 2;
-#pragma unroll
-    for (int q = 0; q < kQ; ++q) {
-      const int u = wave + kWaves * q;
-      if (KMAJ) {
-        const int R = kRowsPerPiece * u + lane / kChunks;
-        const int c = (lane % kChunks) ^ swz_k(R);
-        const int r = R < rv ? R : rv - 1;
-        off[q] = (uint32_t)(((int64_t)r * ld + c * 8) * 2);
-      } else {
-        const int prow = 2 * u + (lane >> 5);
-        int col = ((lane & 31) ^ swz_m(prow)) * 8;
-        col = col < rv - 8 ? col : rv - 8;
-        off[q] = (uint32_t)(((int64_t)prow * ld + col) * 2);
-      }
-    }
-  }
-
-  // Every contraction index of stage t is valid.
-  __device__ __forceinline__ void issue_full(int t, char *st, int wave) const {
-    const __amdgpu_buffer_rsrc_t r = rsrc_at(base + (int64_t)t * step);
-#pragma unroll
-    for (int q = 0; q < kQ; ++q)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (GL_LDS void *)(st + (wave + kWaves * q) * 1024), 16, off[q], 0, 0,
-                                               0);
-  }
-
-  // The last stage of a contraction: lanes whose piece lies past pmax write zeros
-  // into their LDS slot instead of loading.
-  __device__ __forceinline__ void issue_masked(int t, int64_t pmax, char *st, int wave, int lane) const {
-    const __amdgpu_buffer_rsrc_t r = rsrc_at(base + (int64_t)t * step);
-#pragma unroll
-    for (int q = 0; q < kQ; ++q) {
-      const int u = wave + kWaves * q;
-      char *dst = st + u * 1024;
-      // first contraction index (within the stage) this lane's piece holds
-      const int pfirst =
-          KMAJ ? ((lane % kChunks) ^ swz_k(kRowsPerPiece * u + lane / kChunks)) * 8 : 2 * u + (lane >> 5);
-      if ((int64_t)t * kBK + pfirst < pmax)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (GL_LDS void *)dst, 16, off[q], 0, 0, 0);
-      else
-        *(uint4 *)(dst + lane * 16) = make_uint4(0, 0, 0, 0);
-    }
-  }
-};
-
-// MFMA operand fragment (32 rows/columns x 16 contraction values; lane l holds row
-// l % 32, contraction values 8 (l / 32) + 0..7) for MFMA step ks of a stage.
-__device__ __forceinline__ bf16x8_t frag_kmaj(const char *st, int row0, int ks, int lane) {
-  const int r = row0 + (lane & 31);
-  const int c = 2 * ks + (lane >> 5);
-  return *(const bf16x8_t *)(st + r * kRowB + ((c ^ swz_k(r)) << 4));
-}
-
-__device__ __forceinline__ bf16x8_t frag_mnmaj(const char *st, int col0, int ks, int lane) {
-  // 16-lane groups: lanes 0-15 / 16-31 take columns 0-15 / 16-31, lane halves take
-  // contraction rows 0-7 / 8-15 of the step; lane s of a group names row s / 4 and
-  // columns 4 (s % 4) .. + 3, and the transpose hands lane s column s of those rows.
-  const int s = lane & 15, grp = lane >> 4;
-  const int col = col0 + ((grp & 1) << 4) + ((s & 3) << 2);
-  const int chunk = col >> 3, within = col & 7;
-  v4i16 h[2];
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int prow = ks * 16 + (grp >> 1) * 8 + t * 4 + (s >> 2);
-    const char *a = st + prow * 512 + ((chunk ^ swz_m(prow)) << 4) + within * 2;
-    h[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GL_LDS v4i16 *)a);
-  }
-  const v8i16 v = {h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
-  return __builtin_bit_cast(bf16x8_t, v);
-}
-
-// Stores 4 consecutive output columns of one row: optional bias (per output
-// column), optional accumulate into the existing bf16 or fp32 values.
-__device__ __forceinline__ void store4(char *cbase, int64_t row, int64_t ldc, int64_t col, const char *bias_g,
-                                      int out_f32, int accumulate, float v0, float v1, float v2, float v3) {
-  if (bias_g) {
-    if (out_f32) {
-      const float4 bv = *(const float4 *)(bias_g + col * 4);
-      v0 += bv.x; v1 += bv.y; v2 += bv.z; v3 += bv.w;
-    } else {
-      const uint2 bv = *(const uint2 *)(bias_g + col * 2);
-      v0 += bf16_to_f32(bv.x & 0xffff); v1 += bf16_to_f32(bv.x >> 16);
-      v2 += bf16_to_f32(bv.y & 0xffff); v3 += bf16_to_f32(bv.y >> 16);
-    }
-  }
-  if (out_f32) {
-    float4 *dst = (float4 *)(cbase + (row * ldc + col) * 4);
-    if (accumulate) {
-      const float4 o = *dst;
-      v0 += o.x; v1 += o.y; v2 += o.z; v3 += o.w;
-    }
-    *dst = make_float4(v0, v1, v2, v3);
-  } else {
-    uint2 *dst = (uint2 *)(cbase + (row * ldc + col) * 2);
-    if (accumulate) {
-      const uint2 o = *dst;
-      v0 += bf16_to_f32(o.x & 0xffff); v1 += bf16_to_f32(o.x >> 16);
-      v2 += bf16_to_f32(o.y & 0xffff); v3 += bf16_to_f32(o.y >> 16);
-    }
-    *dst = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
-  }
-}
+namespace gemm {
 
 template <bool A_KMAJ, bool B_KMAJ, int MODE>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(Params p) {
+__global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
   __shared__ __attribute__((aligned(1024))) char lds[kS * kStageBytes];
 
   const WsView ws = ws_view(p.ws, p.G);
@@ -271,67 +68,25 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(Params p) {
   const int first = (grid & 7) == 0 ? (b & 7) * (grid >> 3) + (b >> 3) : b;
 
   for (int w = first; w < total; w += grid) {
-    // ------------------------------------------------------------ decode item
-    int g, local, MT;
-    const int NT = p.tiles_j;
-    if (MODE == MODE_ROWS) {
-      g = find_group(pre, p.G, w / NT);
-      local = w - pre[g] * NT;
-      MT = pre[g + 1] - pre[g];
-    } else {
-      const int per = p.tiles_i * NT;
-      g = w / per;
-      local = w - g * per;
-      MT = p.tiles_i;
-    }
-    // bands of kOrdN tile columns; inside a band, blocks of kOrdM tile rows; inside
-    // a block, row tiles fastest
-    const int cb = local / (MT * kOrdN);
-    const int bw = min(kOrdN, NT - cb * kOrdN);
-    const int l2 = local - cb * MT * kOrdN;
-    const int rb = l2 / (kOrdM * bw);
-    const int bh = min(kOrdM, MT - rb * kOrdM);
-    const int l3 = l2 - rb * kOrdM * bw;
-    const int it = rb * kOrdM + l3 % bh;
-    const int jt = cb * kOrdN + l3 / bh;
-
-    const int64_t g_off = off[g];
-    const int64_t g_rows = off[g + 1] - g_off;
-    if (MODE == MODE_CONTR && p.accumulate && g_rows == 0) continue;  // main_grad untouched
-
-    const uint16_t *a_base, *b_base;
-    int a_rv, b_rv;
-    int64_t pmax;
-    if (MODE == MODE_ROWS) {
-      a_base = p.A + (g_off + (int64_t)it * kBM) * p.lda;
-      a_rv = (int)min64(kBM, g_rows - (int64_t)it * kBM);
-      const uint16_t *bg = p.B ? p.B + (int64_t)g * p.b_gstride : p.B_ptrs[g];
-      b_base = B_KMAJ ? bg + (int64_t)jt * kBN * p.ldb : bg + (int64_t)jt * kBN;
-      b_rv = (int)min64(kBN, p.cols_j - (int64_t)jt * kBN);
-      pmax = p.P;
-    } else {
-      a_base = p.A + g_off * p.lda + (int64_t)it * kBM;
-      a_rv = (int)min64(kBM, p.rows_i - (int64_t)it * kBM);
-      b_base = p.B + g_off * p.ldb + (int64_t)jt * kBN;
-      b_rv = (int)min64(kBN, p.cols_j - (int64_t)jt * kBN);
-      pmax = g_rows;
-    }
+    const Tile t = decode_tile<A_KMAJ, B_KMAJ, MODE>(p, off, pre, w);
+    if (MODE == MODE_CONTR && p.accumulate && t.g_rows == 0) continue;  // main_grad untouched
+    const int64_t pmax = t.pmax;
     const int nk = (int)((pmax + kBK - 1) / kBK);
     const int nfull = (int)(pmax / kBK);  // stages [0, nfull) are complete; nk - nfull <= 1
 
     Stream<A_KMAJ> sa;
     Stream<B_KMAJ> sb;
-    sa.init(a_base, p.lda, a_rv, wave, lane);
-    sb.init(b_base, p.ldb, b_rv, wave, lane);
-    auto stage_ptr = [&](int t) { return lds + (t % kS) * kStageBytes; };
-    auto issue = [&](int t) {
-      char *st = stage_ptr(t);
-      if (t < nfull) {
-        sa.issue_full(t, st, wave);
-        sb.issue_full(t, st + kOpBytes, wave);
+    sa.init(t.a_base, p.lda, t.a_rv, wave, lane);
+    sb.init(t.b_base, p.ldb, t.b_rv, wave, lane);
+    auto stage_ptr = [&](int s) { return lds + (s % kS) * kStageBytes; };
+    auto issue = [&](int s) {
+      char *st = stage_ptr(s);
+      if (s < nfull) {
+        sa.issue_full(s, st, wave);
+        sb.issue_full(s, st + kOpBytes, wave);
       } else {
-        sa.issue_masked(t, pmax, st, wave, lane);
-        sb.issue_masked(t, pmax, st + kOpBytes, wave, lane);
+        sa.issue_masked(s, pmax, st, wave, lane);
+        sb.issue_masked(s, pmax, st + kOpBytes, wave, lane);
       }
     };
 
@@ -344,8 +99,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(Params p) {
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[ii][jj][q] = 0.f;
 
-    auto load_frags = [&](int t, int ks, bf16x8_t *af, bf16x8_t *bfr) {
-      const char *ta = stage_ptr(t);
+    auto load_frags = [&](int s, int ks, bf16x8_t *af, bf16x8_t *bfr) {
+      const char *ta = stage_ptr(s);
       const char *tb = ta + kOpBytes;
 #pragma unroll
       for (int ii = 0; ii < kNI; ++ii)
@@ -365,7 +120,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(Params p) {
 
     bf16x8_t fa[2][kNI], fb[2][kNJ];
     // prologue: stages 0 .. kS-2 in flight, stage 0 visible, step 0 fragments read
-    for (int t = 0; t < kS - 1 && t < nk; ++t) issue(t);
+    for (int s = 0; s < kS - 1 && s < nk; ++s) issue(s);
     if (nk > 0) {
       wait_vm0();
       __builtin_amdgcn_s_barrier();
@@ -414,62 +169,17 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(Params p) {
     for (; kt < nk; ++kt) body(kt, false);
     __builtin_amdgcn_s_barrier();  // every wave is done with the ring before it is refilled
 
-    // --------------------------------------------------------------- epilogue
-    // lane holds C[i][j..j+3] with i = ii*32 + lane%32, j = jj*32 + q4*8 + (lane/32)*4
-    char *cbase;
-    int64_t row0;
-    if (MODE == MODE_ROWS) {
-      cbase = (char *)p.C;
-      row0 = g_off + (int64_t)it * kBM;
-    } else {
-      cbase = p.C ? (char *)p.C + (int64_t)g * p.c_gstride * (p.out_f32 ? 4 : 2) : (char *)p.C_ptrs[g];
-      row0 = (int64_t)it * kBM;
-    }
-    const char *bias_g = nullptr;
-    if (p.bias) bias_g = (const char *)p.bias + (int64_t)g * p.cols_j * (p.out_f32 ? 4 : 2);
-    else if (p.bias_ptrs) bias_g = (const char *)p.bias_ptrs[g];
-#pragma unroll
-    for (int ii = 0; ii < kNI; ++ii) {
-      const int il = wm * kWTM + ii * 32 + (lane & 31);
-      if (il >= a_rv) continue;
-      const int64_t row = row0 + il;
-#pragma unroll
-      for (int jj = 0; jj < kNJ; ++jj) {
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int jl = wn * kWTN + jj * 32 + q4 * 8 + (lane >> 5) * 4;
-          if (jl >= b_rv) continue;
-          store4(cbase, row, p.ldc, (int64_t)jt * kBN + jl, bias_g, p.out_f32, p.accumulate,
-                 acc[ii][jj][q4 * 4 + 0], acc[ii][jj][q4 * 4 + 1], acc[ii][jj][q4 * 4 + 2], acc[ii][jj][q4 * 4 + 3]);
-        }
-      }
-    }
+    store_tile<MODE>(p, t, acc, wm, wn, lane);
   }
 }
 
-// Compute units of the current device (one persistent workgroup per CU).
-static int num_cus() {
-  int dev = 0, n = 0;
-  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) !=
-                                              hipSuccess || n <= 0)
-    n = 256;
-  return n;
-}
-
-static int persistent_grid(int64_t max_items) {
-  const int cus = num_cus();
-  int64_t g = max_items < cus ? max_items : cus;
-  if (g >= 8) g &= ~7;  // keeps the XCD-aware remap a bijection
-  return (int)(g > 0 ? g : 1);
-}
-
-}  // namespace gemm_bf16
+}  // namespace gemm
 
 // forward: y = x W^T (+ b); A = x [T,K], B = W [N,K]
 hipError_t launch_forward_bf16(int G, int64_t K, int64_t N, int64_t T, const uint16_t *x, const uint16_t *w,
                                const uint16_t *const *w_ptrs, const void *bias, const void *const *bias_ptrs,
                                uint16_t *y, const void *ws, hipStream_t s) {
-  using namespace gemm_bf16;
+  using namespace gemm;
   Params p{};
   p.A = x; p.lda = K;
   p.B = w; p.B_ptrs = w_ptrs; p.b_gstride = N * K; p.ldb = K;
@@ -479,14 +189,14 @@ hipError_t launch_forward_bf16(int G, int64_t K, int64_t N, int64_t T, const uin
   p.cols_j = N; p.P = K;
   p.tiles_j = (int)((N + kBN - 1) / kBN);
   const int64_t max_items = ((T + kBM - 1) / kBM + G) * p.tiles_j;
-  hipLaunchKernelGGL((gemm_kernel<true, true, MODE_ROWS>), dim3(persistent_grid(max_items)), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL((gemm_bf16_kernel<true, true, MODE_ROWS>), dim3(persistent_grid(max_items)), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 
 // dgrad: dx = dy W; A = dy [T,N] (n contiguous), B[j=k][p=n] = W[n][k] (k contiguous)
 hipError_t launch_dgrad_bf16(int G, int64_t K, int64_t N, int64_t T, const uint16_t *dy, const uint16_t *w,
                              const uint16_t *const *w_ptrs, uint16_t *dx, const void *ws, hipStream_t s) {
-  using namespace gemm_bf16;
+  using namespace gemm;
   Params p{};
   p.A = dy; p.lda = N;
   p.B = w; p.B_ptrs = w_ptrs; p.b_gstride = N * K; p.ldb = K;
@@ -495,7 +205,7 @@ hipError_t launch_dgrad_bf16(int G, int64_t K, int64_t N, int64_t T, const uint1
   p.cols_j = K; p.P = N;
   p.tiles_j = (int)((K + kBN - 1) / kBN);
   const int64_t max_items = ((T + kBM - 1) / kBM + G) * p.tiles_j;
-  hipLaunchKernelGGL((gemm_kernel<true, false, MODE_ROWS>), dim3(persistent_grid(max_items)), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL((gemm_bf16_kernel<true, false, MODE_ROWS>), dim3(persistent_grid(max_items)), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 
@@ -503,7 +213,7 @@ hipError_t launch_dgrad_bf16(int G, int64_t K, int64_t N, int64_t T, const uint1
 hipError_t launch_wgrad_bf16(int G, int64_t K, int64_t N, int64_t T, const uint16_t *x, const uint16_t *dy,
                              void *dw, void *const *dw_ptrs, int out_f32, int accumulate, const void *ws,
                              hipStream_t s) {
-  using namespace gemm_bf16;
+  using namespace gemm;
   Params p{};
   p.A = dy; p.lda = N;
   p.B = x; p.ldb = K;
@@ -515,7 +225,7 @@ hipError_t launch_wgrad_bf16(int G, int64_t K, int64_t N, int64_t T, const uint1
   p.accumulate = accumulate;
   p.out_f32 = out_f32;
   const int64_t max_items = (int64_t)G * p.tiles_i * p.tiles_j;
-  hipLaunchKernelGGL((gemm_kernel<false, false, MODE_CONTR>), dim3(persistent_grid(max_items)), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL((gemm_bf16_kernel<false, false, MODE_CONTR>), dim3(persistent_grid(max_items)), dim3(kThreads), 0, s,
                      p);
   return hipGetLastError();
 }
