@@ -10,7 +10,9 @@ Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 
 Modules
   grouped_linear  split offsets, grouped forward, dgrad, wgrad, bias grad
-  mxfp8           OCP MX E4M3 block quantizer (E8M0 scales) and its decoder
+  mxfp8           OCP MX E4M3 block quantizer (E8M0 scales), rowwise and columnwise
+                  (per group, stored transposed), its decoder, and the MXFP8 forward,
+                  dgrad and wgrad on dequantized operands
 
 Every function here is pinned by ``tests/test_oracle_*.py`` against something
 other than itself (library identities, autograd, closed forms, hand-worked
@@ -20,4 +22,6 @@ from . import grouped_linear, mxfp8  # noqa: F401
 from .grouped_linear import offsets, forward, dgrad, wgrad, bgrad, group_of_rows  # noqa: F401
 from .mxfp8 import (  # noqa: F401
     e4m3_round, e4m3_encode, e4m3_decode, quantize_mxfp8, dequantize_mxfp8, forward_mxfp8,
+    COLWISE_ALIGN, colwise_offsets, quantize_mxfp8_colwise, quantize_mxfp8_colwise_weights, dgrad_mxfp8,
+    wgrad_mxfp8,
 )

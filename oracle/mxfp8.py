@@ -131,3 +131,107 @@ def forward_mxfp8(xq, xs, wq, ws, b, m_splits, rows=None) -> np.ndarray:
             return dequantize_mxfp8(wq[g], ws[g])
 
     return grouped_linear.forward(x, _Groups(), b, m_splits, rows=rows)
+
+
+# ---------------------------------------------------------------- columnwise
+# The backward pass of the quantized GroupedLinear (page
+# "transformer_engine/pytorch/ops/basic/grouped_linear.py", op_forward / fuser_backward:
+# the input and grad-output quantizers take columnwise usage when the weight needs a
+# gradient, the weight quantizer when the input does; split_quantize quantizes each
+# split on its own) contracts over token rows in wgrad and over out_features in dgrad,
+# so those operands are quantized in blocks of 32 along the rows instead.
+#
+# Layout (a reading of this library, not of the pages): columnwise codes are stored
+# transposed, so the 32 values of a block are contiguous.  For activations split into
+# groups the transposed matrix is [cols, ld]; group g's rows start at column
+# COLWISE_ALIGN-aligned offset poff[g] and are followed by zero padding up to the next
+# multiple of COLWISE_ALIGN.  A group's last block may hold fewer than 32 real rows;
+# the zero padding leaves its amax unchanged, so it is quantized as the padded block.
+# Padding blocks are all zero: codes 0, scale byte 0 (the OCP code of an all-zero
+# block, 2^-127, finite).
+
+COLWISE_ALIGN = 128
+
+
+def colwise_offsets(m_splits) -> np.ndarray:
+    """Start column of each group's rows in the transposed columnwise layout:
+    exclusive prefix of ceil(m_g / 128) * 128, with the total last."""
+    m = np.asarray(m_splits, dtype=np.int64)
+    pad = -(-m // COLWISE_ALIGN) * COLWISE_ALIGN
+    return np.concatenate([[0], np.cumsum(pad)]).astype(np.int64)
+
+
+def quantize_mxfp8_colwise(src, m_splits, ld=None):
+    """Columnwise MXFP8 group quantization of a [T, C] array split into row groups.
+
+    Returns (codes uint8 [C, ld], scales uint8 [C, ld // 32], poff int64 [G + 1]):
+    per group and column, blocks of 32 consecutive rows of the group, stored
+    transposed from column poff[g].  ld defaults to poff[G]; columns past poff[G]
+    are zero here (the library leaves them untouched).
+    """
+    v = np.asarray(src, dtype=np.float64)
+    T, C = v.shape
+    m = np.asarray(m_splits, dtype=np.int64)
+    if m.sum() != T:
+        raise ValueError("split sizes must add up to the row count")
+    off = np.concatenate([[0], np.cumsum(m)])
+    poff = colwise_offsets(m)
+    ld = int(poff[-1]) if ld is None else int(ld)
+    if ld < poff[-1] or ld % BLOCK:
+        raise ValueError("ld must hold every padded group and be a multiple of 32")
+    codes = np.zeros((C, ld), dtype=np.uint8)
+    scales = np.zeros((C, ld // BLOCK), dtype=np.uint8)
+    for g in range(len(m)):
+        width = int(poff[g + 1] - poff[g])
+        if width == 0:
+            continue
+        block = np.zeros((C, width))
+        block[:, : m[g]] = v[off[g]: off[g + 1]].T
+        q, s = quantize_mxfp8(block)
+        codes[:, poff[g]: poff[g + 1]] = q
+        scales[:, poff[g] // BLOCK: poff[g + 1] // BLOCK] = s
+    return codes, scales, poff
+
+
+def quantize_mxfp8_colwise_weights(w):
+    """Columnwise MXFP8 of grouped weights [G, N, K] (blocks of 32 along N, the
+    dgrad contraction), stored transposed: codes [G, K, N], scales [G, K, N // 32]."""
+    w = np.asarray(w, dtype=np.float64)
+    G, N, K = w.shape
+    if N % BLOCK:
+        raise ValueError("N must be a multiple of 32")
+    codes = np.zeros((G, K, N), dtype=np.uint8)
+    scales = np.zeros((G, K, N // BLOCK), dtype=np.uint8)
+    for g in range(G):
+        codes[g], scales[g] = quantize_mxfp8(w[g].T)
+    return codes, scales
+
+
+def dgrad_mxfp8(dyq, dys, wtq, wts, m_splits, rows=None) -> np.ndarray:
+    """MXFP8 grouped dgrad dx_g = dy_g W_g on the dequantized operands: dy from its
+    rowwise codes [T, N] (blocks along N), W_g from its columnwise codes stored
+    transposed [K, N] (per group, or [G, K, N])."""
+    dy = dequantize_mxfp8(dyq, dys)
+
+    class _Groups:
+        def __len__(self):
+            return len(m_splits)
+
+        def __getitem__(self, g):
+            return dequantize_mxfp8(wtq[g], wts[g]).T   # [N, K]
+
+    return grouped_linear.dgrad(dy, _Groups(), m_splits, rows=rows)
+
+
+def wgrad_mxfp8(dytq, dyts, xtq, xts, m_splits, main_grad=None, accumulate: bool = False, groups=None,
+                out_rows=None) -> np.ndarray:
+    """MXFP8 grouped wgrad dW_g = dy_g^T x_g on the dequantized columnwise operands:
+    dy from codes [N, ld] and x from codes [K, ld] in the transposed group layout."""
+    m = np.asarray(m_splits, dtype=np.int64)
+    poff = colwise_offsets(m)
+    dyT = dequantize_mxfp8(dytq, dyts)
+    xT = dequantize_mxfp8(xtq, xts)
+    dy = np.concatenate([dyT[:, poff[g]: poff[g] + m[g]].T for g in range(len(m))], axis=0)
+    x = np.concatenate([xT[:, poff[g]: poff[g] + m[g]].T for g in range(len(m))], axis=0)
+    return grouped_linear.wgrad(x, dy, m, main_grad=main_grad, accumulate=accumulate, groups=groups,
+                                out_rows=out_rows)
