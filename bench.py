@@ -254,47 +254,67 @@ def bench_bf16(torch, gl, synth, steps, warmup):
 
 
 def bench_mxfp8(torch, gl, synth, steps, warmup):
+    """MXFP8 forward and backward on the MXFP8 workload (G=32, K=N=4096, 32768 rows).
+    Weights are quantized once (rowwise for the forward, columnwise for dgrad), as a
+    cached quantized-weight workspace; activations and grad outputs are quantized
+    inside each timed pass."""
     wl = synth.WORKLOADS["mxfp8_fwd_g32_k4096_n4096"]
     dev = torch.device("cuda")
     t0 = time.time()
     m = synth.split_sizes(wl)
-    x, w = synth.x(wl).to(dev), synth.weight(wl).to(dev)
+    x, w, dy = synth.x(wl).to(dev), synth.weight(wl).to(dev), synth.dy(wl).to(dev)
     log(f"mxfp8 inputs generated in {time.time() - t0:.1f}s")
     G, K, N, T = wl.G, wl.K, wl.N, wl.T
     ws = gl.new_workspace(G, dev)
     gl.gl_offsets(torch.from_numpy(m).to(dev), T, ws)
-    xq = torch.empty(T, K, dtype=torch.uint8, device=dev)
-    xs = torch.empty(T, K // 32, dtype=torch.uint8, device=dev)
-    wq = torch.empty(G, N, K, dtype=torch.uint8, device=dev)
-    wsc = torch.empty(G, N, K // 32, dtype=torch.uint8, device=dev)
+    u8 = dict(dtype=torch.uint8, device=dev)
+    xq, xs = torch.empty(T, K, **u8), torch.empty(T, K // 32, **u8)
+    wq, wsc = torch.empty(G, N, K, **u8), torch.empty(G, N, K // 32, **u8)
+    dq, ds = torch.empty(T, N, **u8), torch.empty(T, N // 32, **u8)
+    wtq, wts = torch.empty(G, K, N, **u8), torch.empty(G, K, N // 32, **u8)
+    ld = gl.gl_colwise_ld(G, T)
+    xtq, xts = torch.empty(K, ld, **u8), torch.empty(K, ld // 32, **u8)
+    dytq, dyts = torch.empty(N, ld, **u8), torch.empty(N, ld // 32, **u8)
     y = torch.empty(T, N, dtype=torch.bfloat16, device=dev)
-    gl.gl_group_quantize_mxfp8(w, wq, wsc)  # weights quantized once, as a cached workspace
+    dx = torch.empty(T, K, dtype=torch.bfloat16, device=dev)
+    dw = torch.empty(G, N, K, dtype=torch.bfloat16, device=dev)
+    gl.gl_group_quantize_mxfp8(w, wq, wsc)              # cached quantized weights
+    gl.gl_quantize_mxfp8_colwise_weights(w, wtq, wts)
     timer = EventTimer(torch)
     for i in range(warmup + steps):
         t = timer if i >= warmup else None
         run = (lambda n, f: t.run(n, f)) if t else (lambda n, f: f())
         run("quantize_x", lambda: gl.gl_group_quantize_mxfp8(x, xq, xs))
+        run("quantize_x_colwise", lambda: gl.gl_group_quantize_mxfp8_colwise(x, xtq, xts, ws, G))
         run("quantize_w", lambda: gl.gl_group_quantize_mxfp8(w, wq, wsc))
         run("mx_forward", lambda: gl.gl_forward(xq, wq, y, ws, x_scale=xs, w_scale=wsc))
+        run("quantize_dy", lambda: gl.gl_group_quantize_mxfp8(dy, dq, ds))
+        run("quantize_dy_colwise", lambda: gl.gl_group_quantize_mxfp8_colwise(dy, dytq, dyts, ws, G))
+        run("mx_dgrad", lambda: gl.gl_dgrad_mxfp8(dq, ds, wtq, wts, dx, ws))
+        run("mx_wgrad", lambda: gl.gl_wgrad_mxfp8(dytq, dyts, xtq, xts, dw, ws, T))
     torch.cuda.synchronize()
     per = timer.mean_ms()
     flops = 2.0 * T * N * K
-    tf = flops / (per["mx_forward"] * 1e-3) / 1e12
-    qx_bytes = T * K * 2 + T * K + T * K // 32
-    qw_bytes = G * N * K * 2 + G * N * K + G * N * K // 32
-    return {
-        "workload": wl.name,
-        "mx_forward_ms": round(per["mx_forward"], 4),
-        "mx_forward_tflops": round(tf, 2),
-        "mx_forward_traffic": traffic_for("mx_forward", wl.name),
-        "pct_fp8_peak": round(100 * tf / PEAK_FP8_TFLOPS, 2),
-        "quantize_x_ms": round(per["quantize_x"], 4),
-        "quantize_x_gbs": round(qx_bytes / (per["quantize_x"] * 1e-3) / 1e9, 1),
-        "quantize_w_ms": round(per["quantize_w"], 4),
-        "quantize_w_gbs": round(qw_bytes / (per["quantize_w"] * 1e-3) / 1e9, 1),
-        "quantize_x_plus_forward_tflops": round(flops / ((per["mx_forward"] + per["quantize_x"]) * 1e-3) / 1e12,
-                                                2),
-    }
+    tf = lambda k: round(flops / (per[k] * 1e-3) / 1e12, 2)
+    gbs = lambda k, b: round(b / (per[k] * 1e-3) / 1e9, 1)
+    row_bytes = lambda r, c: r * c * 2 + r * c + r * c // 32     # bf16 in, codes + scales out
+    col_bytes = lambda r, c: r * c * 2 + (r + 127 * G) * c * (1 + 1 / 32)
+    out = {"workload": wl.name}
+    for k in ("mx_forward", "mx_dgrad", "mx_wgrad"):
+        out[f"{k}_ms"] = round(per[k], 4)
+        out[f"{k}_tflops"] = tf(k)
+        out[f"{k}_pct_fp8_peak"] = round(100 * tf(k) / PEAK_FP8_TFLOPS, 2)
+    out["mx_forward_traffic"] = traffic_for("mx_forward", wl.name)
+    out["quantize_gbs"] = {"x": gbs("quantize_x", row_bytes(T, K)), "w": gbs("quantize_w", row_bytes(G * N, K)),
+                           "dy": gbs("quantize_dy", row_bytes(T, N)),
+                           "x_colwise": gbs("quantize_x_colwise", col_bytes(T, K)),
+                           "dy_colwise": gbs("quantize_dy_colwise", col_bytes(T, N))}
+    step_ms = sum(per[k] for k in per if k != "quantize_w")
+    out["mx_step_ms"] = round(step_ms, 4)
+    out["mx_step_tflops"] = round(3 * flops / (step_ms * 1e-3) / 1e12, 2)
+    out["mx_step"] = ("quantize x (rowwise, columnwise), MX forward, quantize dy (rowwise, columnwise), "
+                      "MX dgrad, MX wgrad; weights quantized once")
+    return out
 
 
 def main():

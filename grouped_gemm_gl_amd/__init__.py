@@ -63,6 +63,11 @@ def load():
         "gl_wgrad": (I, [I, I64, I64, I64, I, I, P, P, P, P, I, P, P]),
         "gl_bgrad": (I, [I, I64, I64, I, P, P, P, P, P]),
         "gl_group_quantize_mxfp8": (I, [P, I64, I64, P, P, P]),
+        "gl_colwise_ld": (I64, [I, I64]),
+        "gl_group_quantize_mxfp8_colwise": (I, [P, I64, I, I64, P, P, P, I64, P]),
+        "gl_quantize_mxfp8_colwise_weights": (I, [P, I, I64, I64, P, P, P]),
+        "gl_dgrad_mxfp8": (I, [I, I64, I64, I64, I, P, P, P, P, P, I64, P, P]),
+        "gl_wgrad_mxfp8": (I, [I, I64, I64, I64, I, P, P, P, P, I64, P, P, I, P, P]),
         "gl_last_error": (ctypes.c_char_p, []),
         "gl_version": (ctypes.c_char_p, []),
     }
@@ -236,3 +241,61 @@ def gl_group_quantize_mxfp8(src: Tensor, data: Tensor, scale: Tensor, stream=Non
         raise ValueError("scale must be uint8 with rows * cols/32 elements")
     _check(load().gl_group_quantize_mxfp8(_ptr(src), rows, cols, _ptr(data), _ptr(scale), _stream(stream)))
     return data, scale
+
+
+# ------------------------------------------------------------------ MXFP8 backward
+
+
+def gl_colwise_ld(num_groups: int, total_rows: int) -> int:
+    """Row length of the transposed columnwise activation layout that fits any split."""
+    return int(load().gl_colwise_ld(int(num_groups), int(total_rows)))
+
+
+def gl_group_quantize_mxfp8_colwise(src: Tensor, data_t: Tensor, scale_t: Tensor, workspace: Tensor,
+                                    num_groups: int, stream=None):
+    """Columnwise MXFP8 of bf16 [T, C] per group into data_t [C, ld] / scale_t [C, ld/32]."""
+    T, C = src.shape
+    ld = data_t.shape[1]
+    if src.dtype != torch.bfloat16 or data_t.shape != (C, ld) or scale_t.shape != (C, ld // 32):
+        raise ValueError("src must be bf16 [T, C], data_t [C, ld] and scale_t [C, ld/32]")
+    _check(load().gl_group_quantize_mxfp8_colwise(_ptr(src), C, int(num_groups), T, _ptr(workspace), _ptr(data_t),
+                                                  _ptr(scale_t), ld, _stream(stream)))
+    return data_t, scale_t
+
+
+def gl_quantize_mxfp8_colwise_weights(w: Tensor, data_t: Tensor, scale_t: Tensor, stream=None):
+    """Columnwise MXFP8 of bf16 weights [G, N, K] into data_t [G, K, N] / scale_t [G, K, N/32]."""
+    G, N, K = w.shape
+    if w.dtype != torch.bfloat16 or data_t.shape != (G, K, N) or scale_t.shape != (G, K, N // 32):
+        raise ValueError("w must be bf16 [G, N, K], data_t [G, K, N] and scale_t [G, K, N/32]")
+    _check(load().gl_quantize_mxfp8_colwise_weights(_ptr(w), G, N, K, _ptr(data_t), _ptr(scale_t), _stream(stream)))
+    return data_t, scale_t
+
+
+def gl_dgrad_mxfp8(dy: Tensor, dy_scale: Tensor, w_t: Tensor, w_t_scale: Tensor, dx: Tensor, workspace: Tensor,
+                   stream=None) -> Tensor:
+    """dx[:T] = grouped deq(dy) deq(W_g) from rowwise dy codes and columnwise weight codes [G, K, N]."""
+    G, K, N = w_t.shape
+    T = dy.shape[0]
+    if dy.shape != (T, N) or dx.dim() != 2 or dx.shape[1] != K:
+        raise ValueError("dy must be [T, N] codes and dx [rows >= T, K]")
+    _check(load().gl_dgrad_mxfp8(G, K, N, T, _dtype(dx), _ptr(dy), _ptr(dy_scale), _ptr(w_t), _ptr(w_t_scale),
+                                 _ptr(dx), dx.shape[0], _ptr(workspace), _stream(stream)))
+    return dx
+
+
+def gl_wgrad_mxfp8(dy_t: Tensor, dy_t_scale: Tensor, x_t: Tensor, x_t_scale: Tensor, dw: Grouped,
+                   workspace: Tensor, total_rows: int, *, accumulate: bool = False, stream=None) -> Grouped:
+    """dW_g (+)= deq(dy_g)^T deq(x_g) from columnwise codes dy_t [N, ld] and x_t [K, ld]."""
+    G = dw.shape[0] if isinstance(dw, Tensor) else len(dw)
+    d0 = _first(dw)
+    N, ld = dy_t.shape
+    K = x_t.shape[0]
+    if x_t.shape != (K, ld) or tuple(d0.shape[-2:]) != (N, K):
+        raise ValueError("x_t must be [K, ld] and dw [G, N, K] or G tensors [N, K]")
+    dp, dpp, keep = _grouped(dw, dy_t.device)
+    _check(load().gl_wgrad_mxfp8(G, K, N, int(total_rows), _dtype(d0), _ptr(dy_t), _ptr(dy_t_scale), _ptr(x_t),
+                                 _ptr(x_t_scale), ld, dp, dpp, int(bool(accumulate)), _ptr(workspace),
+                                 _stream(stream)))
+    del keep
+    return dw

@@ -39,6 +39,13 @@ hipError_t launch_bgrad(int G, int64_t N, int64_t T, int f32, const void *dy, vo
                         const void *ws, hipStream_t s);
 hipError_t launch_quantize_mxfp8(const uint16_t *src, int64_t rows, int64_t cols, uint8_t *data, uint8_t *scale,
                                  hipStream_t s);
+hipError_t launch_quantize_mxfp8_colwise(const uint16_t *src, int64_t cols, int G, int64_t total_rows,
+                                         const void *ws, uint8_t *data, uint8_t *scale, int64_t ld, hipStream_t s);
+hipError_t launch_quantize_mxfp8_colwise_weights(const uint16_t *w, int G, int64_t N, int64_t K, uint8_t *data,
+                                                 uint8_t *scale, hipStream_t s);
+hipError_t launch_wgrad_mxfp8(int G, int64_t K, int64_t N, int64_t T, const uint8_t *dyt, const uint8_t *dyt_s,
+                              const uint8_t *xt, const uint8_t *xt_s, int64_t ld, void *dw, void *const *dw_ptrs,
+                              int out_f32, int accumulate, const void *ws, hipStream_t s);
 }  // namespace gl
 
 namespace {
@@ -273,3 +280,100 @@ int gl_group_quantize_mxfp8(const void *src, int64_t rows, int64_t cols, uint8_t
 }
 
 }  // extern "C"
+
+int64_t gl_colwise_ld(int num_groups, int64_t total_rows) {
+  if (num_groups <= 0 || total_rows < 0) return -1;
+  const int64_t need = total_rows + 127 * (int64_t)num_groups;
+  return (need + 127) / 128 * 128;
+}
+
+namespace {
+// The columnwise layout's row length: room for every group's padded rows, and few
+// enough that a 256-row GEMM stage stays within 32-bit byte offsets.
+int check_colwise_ld(int G, int64_t T, int64_t ld) {
+  if (ld % 128 || ld < gl_colwise_ld(G, T))
+    return fail(GL_ERR_SHAPE, "ld must be a multiple of 128 and at least %lld (got %lld)",
+                (long long)gl_colwise_ld(G, T), (long long)ld);
+  if (ld > ((int64_t)1 << 23)) return fail(GL_ERR_SHAPE, "ld must be at most 2^23 (got %lld)", (long long)ld);
+  return GL_OK;
+}
+}  // namespace
+
+int gl_group_quantize_mxfp8_colwise(const void *src, int64_t cols, int num_groups, int64_t total_rows,
+                                    const void *workspace, uint8_t *data_t, uint8_t *scale_t, int64_t ld,
+                                    hipStream_t stream) {
+  const int G = num_groups;
+  if (G <= 0 || total_rows < 0 || cols <= 0)
+    return fail(GL_ERR_ARG, "Invalid sizes (groups %d, rows %lld, cols %lld)", G, (long long)total_rows,
+                (long long)cols);
+  GL_TRY(check_colwise_ld(G, total_rows, ld));
+  if (!workspace) return fail(GL_ERR_ARG, "workspace is NULL");
+  if (total_rows == 0) return ok();
+  if (!src || !data_t || !scale_t) return fail(GL_ERR_ARG, "src, data_t or scale_t is NULL");
+  if (!aligned16(src) || !aligned16(data_t)) return fail(GL_ERR_ARG, "src and data_t must be 16-byte aligned");
+  return hip_result(gl::launch_quantize_mxfp8_colwise((const uint16_t *)src, cols, G, total_rows, workspace, data_t,
+                                                      scale_t, ld, stream),
+                    "gl_group_quantize_mxfp8_colwise");
+}
+
+int gl_quantize_mxfp8_colwise_weights(const void *w, int num_groups, int64_t out_features, int64_t in_features,
+                                      uint8_t *data_t, uint8_t *scale_t, hipStream_t stream) {
+  const int G = num_groups;
+  const int64_t N = out_features, K = in_features;
+  if (G <= 0 || N <= 0 || K <= 0)
+    return fail(GL_ERR_ARG, "Invalid sizes (groups %d, N %lld, K %lld)", G, (long long)N, (long long)K);
+  if (N % 32) return fail(GL_ERR_SHAPE, "out_features must be a multiple of 32 (got %lld)", (long long)N);
+  if (!w || !data_t || !scale_t) return fail(GL_ERR_ARG, "w, data_t or scale_t is NULL");
+  if (!aligned16(data_t)) return fail(GL_ERR_ARG, "data_t must be 16-byte aligned");
+  return hip_result(gl::launch_quantize_mxfp8_colwise_weights((const uint16_t *)w, G, N, K, data_t, scale_t, stream),
+                    "gl_quantize_mxfp8_colwise_weights");
+}
+
+int gl_dgrad_mxfp8(int num_groups, int64_t in_features, int64_t out_features, int64_t total_rows,
+                   gl_dtype out_dtype, const uint8_t *dy, const uint8_t *dy_scale, const uint8_t *w_t,
+                   const uint8_t *w_t_scale, void *dx, int64_t dx_rows, const void *workspace, hipStream_t stream) {
+  const int G = num_groups;
+  const int64_t K = in_features, N = out_features, T = total_rows;
+  GL_TRY(check_sizes(G, K, N, T));
+  if (out_dtype != GL_BF16 && out_dtype != GL_F32)
+    return fail(GL_ERR_DTYPE, "gl_dgrad_mxfp8: out_dtype must be GL_BF16 or GL_F32");
+  if (N % 128) return fail(GL_ERR_SHAPE, "MXFP8 dgrad needs out_features %% 128 == 0 (got %lld)", (long long)N);
+  if (K % 8) return fail(GL_ERR_SHAPE, "MXFP8 dgrad needs in_features %% 8 == 0 (got %lld)", (long long)K);
+  if (!workspace) return fail(GL_ERR_ARG, "workspace is NULL");
+  if (dx_rows < T) return fail(GL_ERR_SHAPE, "dgrad buffer has %lld rows, needs at least %lld", (long long)dx_rows,
+                               (long long)T);
+  if (!w_t || !w_t_scale) return fail(GL_ERR_ARG, "w_t or w_t_scale is NULL");
+  if (!aligned16(w_t) || ((uintptr_t)w_t_scale & 3u)) return fail(GL_ERR_ARG, "w_t / w_t_scale misaligned");
+  GL_TRY(check_buf(dy, T, "dy"));
+  GL_TRY(check_buf(dx, T, "dx"));
+  if (T > 0 && (!dy_scale || ((uintptr_t)dy_scale & 3u))) return fail(GL_ERR_ARG, "dy_scale NULL or misaligned");
+  if (T == 0) return ok();
+  // dx = dy W_g: the MXFP8 forward kernel with contraction N and B = W_g^T [K, N]
+  return hip_result(gl::launch_forward_mxfp8(G, N, K, T, dy, dy_scale, w_t, nullptr, w_t_scale, nullptr, nullptr,
+                                             nullptr, dx, out_dtype == GL_F32, workspace, stream),
+                    "gl_dgrad_mxfp8");
+}
+
+int gl_wgrad_mxfp8(int num_groups, int64_t in_features, int64_t out_features, int64_t total_rows, gl_dtype out_dtype,
+                   const uint8_t *dy_t, const uint8_t *dy_t_scale, const uint8_t *x_t, const uint8_t *x_t_scale,
+                   int64_t ld, void *dw, void *const *dw_ptrs, int accumulate, const void *workspace,
+                   hipStream_t stream) {
+  const int G = num_groups;
+  const int64_t K = in_features, N = out_features, T = total_rows;
+  GL_TRY(check_sizes(G, K, N, T));
+  if (out_dtype != GL_BF16 && out_dtype != GL_F32)
+    return fail(GL_ERR_DTYPE, "gl_wgrad_mxfp8: out_dtype must be GL_BF16 or GL_F32");
+  if (K % 8 || N % 8)
+    return fail(GL_ERR_SHAPE, "MXFP8 wgrad needs in/out_features that are multiples of 8 (got %lld, %lld)",
+                (long long)K, (long long)N);
+  GL_TRY(check_colwise_ld(G, T, ld));
+  if (!workspace) return fail(GL_ERR_ARG, "workspace is NULL");
+  GL_TRY(check_one_form(dw, dw_ptrs, "weight gradient", false));
+  if (accumulate != 0 && accumulate != 1) return fail(GL_ERR_ARG, "accumulate must be 0 or 1");
+  if (!dy_t || !x_t || !dy_t_scale || !x_t_scale) return fail(GL_ERR_ARG, "codes or scales are NULL");
+  if (!aligned16(dy_t) || !aligned16(x_t) || ((uintptr_t)dy_t_scale & 3u) || ((uintptr_t)x_t_scale & 3u))
+    return fail(GL_ERR_ARG, "codes must be 16-byte and scales 4-byte aligned");
+  return hip_result(gl::launch_wgrad_mxfp8(G, K, N, T, dy_t, dy_t_scale, x_t, x_t_scale, ld, dw, dw_ptrs,
+                                           out_dtype == GL_F32, accumulate, workspace, stream),
+                    "gl_wgrad_mxfp8");
+}

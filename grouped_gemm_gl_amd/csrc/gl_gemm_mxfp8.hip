@@ -34,6 +34,9 @@ struct ScaleStream {
   }
 };
 
+// MODE_ROWS: forward (and dgrad on transposed columnwise weight codes);
+// MODE_KCONTR: wgrad on transposed columnwise codes of dy and x.
+template <int MODE>
 __global__ __launch_bounds__(kThreads) void gemm_mxfp8_kernel(Params p) {
   __shared__ __attribute__((aligned(1024))) char lds[kS * kStageBytes];
   __shared__ __attribute__((aligned(1024))) uint32_t lds_sc[kS][2][256];  // scale dwords per tile row
@@ -42,8 +45,9 @@ __global__ __launch_bounds__(kThreads) void gemm_mxfp8_kernel(Params p) {
   if (!ws_usable(ws.hdr, p.G, p.T)) return;
   const int64_t *__restrict__ off = ws.off;
   const int32_t *__restrict__ pre = ws.pre[tile_rows_index(kBM)];
+  const int32_t *__restrict__ cpre = ws.pre[tile_rows_index(128)];
 
-  const int total = pre[p.G] * p.tiles_j;
+  const int total = MODE == MODE_ROWS ? pre[p.G] * p.tiles_j : p.G * p.tiles_i * p.tiles_j;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / kWN, wn = wave % kWN;
@@ -51,18 +55,28 @@ __global__ __launch_bounds__(kThreads) void gemm_mxfp8_kernel(Params p) {
   const int first = (grid & 7) == 0 ? (b & 7) * (grid >> 3) + (b >> 3) : b;
 
   for (int w = first; w < total; w += grid) {
-    const Tile t = decode_tile<true, true, MODE_ROWS>(p, off, pre, w);
-    const int nk = (int)(t.pmax / kBK);  // K % 128 == 0: every stage is complete
+    const Tile t = decode_tile<true, true, MODE>(p, off, pre, w, cpre);
+    if (MODE == MODE_KCONTR && p.accumulate && t.g_rows == 0) continue;  // main_grad untouched
+    // every stage is complete: K % 128 == 0 in row mode, padded groups otherwise
+    const int nk = (int)(t.pmax / kBK);
 
     Stream<true> sa, sb;
     sa.init(t.a_base, p.lda, t.a_rv, wave, lane);
     sb.init(t.b_base, p.ldb, t.b_rv, wave, lane);
     ScaleStream ss;
-    if (wave < 4) {
-      ss.init(p.a_scale + (t.g_off + (int64_t)t.it * kBM) * p.scale_ld, p.scale_ld, t.a_rv, wave * 64 + lane);
-    } else {
-      const uint8_t *bs = p.b_scale ? p.b_scale + (int64_t)t.g * p.cols_j * p.scale_ld : p.b_scale_ptrs[t.g];
-      ss.init(bs + (int64_t)t.jt * kBN * p.scale_ld, p.scale_ld, t.b_rv, (wave - 4) * 64 + lane);
+    if (MODE == MODE_ROWS) {
+      if (wave < 4) {
+        ss.init(p.a_scale + (t.g_off + (int64_t)t.it * kBM) * p.scale_ld, p.scale_ld, t.a_rv, wave * 64 + lane);
+      } else {
+        const uint8_t *bs = p.b_scale ? p.b_scale + (int64_t)t.g * p.cols_j * p.scale_ld : p.b_scale_ptrs[t.g];
+        ss.init(bs + (int64_t)t.jt * kBN * p.scale_ld, p.scale_ld, t.b_rv, (wave - 4) * 64 + lane);
+      }
+    } else {  // scale columns of the group start at 4 per padded 128-element tile
+      const int64_t c0 = 4 * (int64_t)cpre[t.g];
+      if (wave < 4)
+        ss.init(p.a_scale + (int64_t)t.it * kBM * p.scale_ld + c0, p.scale_ld, t.a_rv, wave * 64 + lane);
+      else
+        ss.init(p.b_scale + (int64_t)t.jt * kBN * p.scale_ld + c0, p.scale_ld, t.b_rv, (wave - 4) * 64 + lane);
     }
     auto stage_ptr = [&](int s) { return lds + (s % kS) * kStageBytes; };
     auto issue = [&](int s) {
@@ -121,7 +135,7 @@ __global__ __launch_bounds__(kThreads) void gemm_mxfp8_kernel(Params p) {
       wait_lgkm0();
       __builtin_amdgcn_s_barrier();
     }
-    store_tile<MODE_ROWS>(p, t, acc, wm, wn, lane);
+    store_tile<MODE>(p, t, acc, wm, wn, lane);
   }
 }
 
@@ -147,7 +161,31 @@ hipError_t launch_forward_mxfp8(int G, int64_t K, int64_t N, int64_t T, const ui
   p.out_f32 = out_f32;
   p.a_scale = xs; p.b_scale = ws_scale; p.b_scale_ptrs = ws_scale_ptrs; p.scale_ld = K / 32;
   const int64_t max_items = ((T + kBM - 1) / kBM + G) * p.tiles_j;
-  hipLaunchKernelGGL(gemm_mxfp8_kernel, dim3(persistent_grid(max_items)), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL(gemm_mxfp8_kernel<MODE_ROWS>, dim3(persistent_grid(max_items)), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+// MXFP8 wgrad: dW_g (+)= deq(dy_g)^T deq(x_g) from columnwise codes stored transposed,
+// dyt [N, ld] and xt [K, ld] (group g's rows from column 128 * pre128[g], zero-padded
+// to whole 128-row tiles), scales [N, ld/32] and [K, ld/32].  A[i=n][p] = dyt, B[j=k][p]
+// = xt, both K-major.
+hipError_t launch_wgrad_mxfp8(int G, int64_t K, int64_t N, int64_t T, const uint8_t *dyt, const uint8_t *dyt_s,
+                              const uint8_t *xt, const uint8_t *xt_s, int64_t ld, void *dw, void *const *dw_ptrs,
+                              int out_f32, int accumulate, const void *ws, hipStream_t s) {
+  using namespace gemm;
+  Params p{};
+  p.A = (const uint16_t *)dyt; p.lda = ld / 2;
+  p.B = (const uint16_t *)xt; p.ldb = ld / 2;
+  p.C = dw; p.C_ptrs = dw_ptrs; p.c_gstride = N * K; p.ldc = K;
+  p.ws = ws; p.G = G; p.T = T;
+  p.rows_i = N; p.cols_j = K;
+  p.tiles_i = (int)((N + kBM - 1) / kBM);
+  p.tiles_j = (int)((K + kBN - 1) / kBN);
+  p.accumulate = accumulate;
+  p.out_f32 = out_f32;
+  p.a_scale = dyt_s; p.b_scale = xt_s; p.scale_ld = ld / 32;
+  const int64_t max_items = (int64_t)G * p.tiles_i * p.tiles_j;
+  hipLaunchKernelGGL(gemm_mxfp8_kernel<MODE_KCONTR>, dim3(persistent_grid(max_items)), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 

@@ -28,7 +28,13 @@ constexpr int kOrdM = 8, kOrdN = 4;                 // blocked work-item order
 static_assert(kS >= 2 && kS * kStageBytes <= 160 * 1024, "LDS ring");
 static_assert((kS - 2) * kLoadsPerStage <= 63, "vmcnt range");
 
-enum { MODE_ROWS = 0, MODE_CONTR = 1 };
+// MODE_ROWS: the grouped index is the tile row (forward, dgrad).  MODE_CONTR: the
+// grouped index is the contraction, MN-major operands (bf16 wgrad).  MODE_KCONTR:
+// the grouped index is the contraction, K-major operands whose groups start at
+// 128-aligned contraction offsets and are zero-padded to whole 128-element tiles
+// (MXFP8 wgrad on columnwise codes stored transposed).
+enum { MODE_ROWS = 0, MODE_CONTR = 1, MODE_KCONTR = 2 };
+constexpr int kKcontrUnits = 64;  // one padded 128-code contraction tile, in 2-byte units
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
@@ -233,7 +239,8 @@ struct Tile {
 // inside a band blocks of kOrdM tile rows, inside a block row tiles fastest.
 template <bool A_KMAJ, bool B_KMAJ, int MODE>
 __device__ __forceinline__ Tile decode_tile(const Params &p, const int64_t *__restrict__ off,
-                                            const int32_t *__restrict__ pre, int w) {
+                                            const int32_t *__restrict__ pre, int w,
+                                            const int32_t *__restrict__ cpre = nullptr) {
   Tile t;
   int local, MT;
   const int NT = p.tiles_j;
@@ -264,12 +271,19 @@ __device__ __forceinline__ Tile decode_tile(const Params &p, const int64_t *__re
     t.b_base = B_KMAJ ? bg + (int64_t)t.jt * kBN * p.ldb : bg + (int64_t)t.jt * kBN;
     t.b_rv = (int)min64(kBN, p.cols_j - (int64_t)t.jt * kBN);
     t.pmax = p.P;
-  } else {
+  } else if (MODE == MODE_CONTR) {
     t.a_base = p.A + t.g_off * p.lda + (int64_t)t.it * kBM;
     t.a_rv = (int)min64(kBM, p.rows_i - (int64_t)t.it * kBM);
     t.b_base = p.B + t.g_off * p.ldb + (int64_t)t.jt * kBN;
     t.b_rv = (int)min64(kBN, p.cols_j - (int64_t)t.jt * kBN);
     t.pmax = t.g_rows;
+  } else {  // MODE_KCONTR: cpre = prefix of the groups' padded 128-element tiles
+    const int64_t c0 = (int64_t)cpre[t.g] * kKcontrUnits;
+    t.a_base = p.A + (int64_t)t.it * kBM * p.lda + c0;
+    t.a_rv = (int)min64(kBM, p.rows_i - (int64_t)t.it * kBM);
+    t.b_base = p.B + (int64_t)t.jt * kBN * p.ldb + c0;
+    t.b_rv = (int)min64(kBN, p.cols_j - (int64_t)t.jt * kBN);
+    t.pmax = (int64_t)(cpre[t.g + 1] - cpre[t.g]) * kKcontrUnits;
   }
   return t;
 }

@@ -1,4 +1,7 @@
-// Rowwise MXFP8 quantization: bf16 -> E4M3 codes + one E8M0 scale per 32 elements.
+// MXFP8 quantization: bf16 -> E4M3 codes + one E8M0 scale per 32 elements, rowwise
+// (blocks along a row) and columnwise (blocks down a column, per group, stored
+// transposed; the quantized backward pass of grouped_linear.py takes columnwise
+// usage for the operands whose contraction runs over rows).
 //
 // Format from page "transformer_engine/pytorch/ops/basic/grouped_linear.py"
 // (_quantize_weights_mxfp8: E4M3 data, one scale per 32 elements of the inner
@@ -31,25 +34,15 @@ __device__ __forceinline__ uint32_t e4m3_code(float s) {
   return sign | mag;
 }
 
-__global__ __launch_bounds__(kQThreads) void quantize_mxfp8_kernel(const uint16_t *__restrict__ src,
-                                                                   int64_t nblocks, uint8_t *__restrict__ data,
-                                                                   uint8_t *__restrict__ scale) {
-  const int64_t b = (int64_t)blockIdx.x * kQThreads + threadIdx.x;
-  if (b >= nblocks) return;
-  // blocks are numbered row-major, so block b covers elements [32 b, 32 b + 32)
-  const uint4 *in = (const uint4 *)(src + b * 32);
-  uint4 v[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) v[i] = in[i];
-  const uint32_t *w = (const uint32_t *)v;
+// One block of 32 bf16 values, given as 16 words of two packed values each (element
+// 2i in the low half of w[i]): 32 E4M3 codes packed four per word, and the scale byte.
+__device__ __forceinline__ void quantize_block(const uint32_t *w, uint32_t *out, uint8_t &sbyte) {
   uint32_t amax = 0;  // |bf16| bit patterns order like magnitudes (Inf 0x7f80, NaN above)
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     amax = max(amax, w[i] & 0x7fffu);
     amax = max(amax, (w[i] >> 16) & 0x7fffu);
   }
-  uint32_t out[8];
-  uint8_t sbyte;
   if (amax >= 0x7f80u) {  // Inf or NaN in the block
     sbyte = 0xff;
 #pragma unroll
@@ -79,10 +72,84 @@ __global__ __launch_bounds__(kQThreads) void quantize_mxfp8_kernel(const uint16_
       out[i] = o;
     }
   }
-  uint4 *dst = (uint4 *)(data + b * 32);
-  dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
-  dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
+}
+
+__device__ __forceinline__ void store_block(uint8_t *dst, const uint32_t *out) {
+  uint4 *d = (uint4 *)dst;
+  d[0] = make_uint4(out[0], out[1], out[2], out[3]);
+  d[1] = make_uint4(out[4], out[5], out[6], out[7]);
+}
+
+__global__ __launch_bounds__(kQThreads) void quantize_mxfp8_kernel(const uint16_t *__restrict__ src,
+                                                                   int64_t nblocks, uint8_t *__restrict__ data,
+                                                                   uint8_t *__restrict__ scale) {
+  const int64_t b = (int64_t)blockIdx.x * kQThreads + threadIdx.x;
+  if (b >= nblocks) return;
+  // blocks are numbered row-major, so block b covers elements [32 b, 32 b + 32)
+  const uint4 *in = (const uint4 *)(src + b * 32);
+  uint4 v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = in[i];
+  uint32_t out[8];
+  uint8_t sbyte;
+  quantize_block((const uint32_t *)v, out, sbyte);
+  store_block(data + b * 32, out);
   scale[b] = sbyte;
+}
+
+// Columnwise MXFP8 (blocks of 32 consecutive rows of a column), stored transposed:
+// thread t handles column c = t % cols of padded block b = t / cols.  Consecutive
+// threads take consecutive columns, so each row read is contiguous across a wave.
+//   Group mode (ws != null): rows split by the workspace's offsets; group g's rows
+//   are padded to whole 128-row tiles and its blocks are numbered from 4 pre128[g],
+//   so padded block b lands at output column 32 b of row c of a [cols, ld] matrix.
+//   Rows past a group's end read as zero (padding blocks come out all zero).
+//   Uniform mode (ws == null): groups of urows rows (a multiple of 32) each, group g
+//   stored as its own [cols, urows] matrix at data + g * cols * urows.
+__global__ __launch_bounds__(kQThreads) void quantize_mxfp8_colwise_kernel(
+    const uint16_t *__restrict__ src, int64_t cols, int64_t nblk, const void *ws, int G, int64_t total_rows,
+    int64_t urows, uint8_t *__restrict__ data, uint8_t *__restrict__ scale, int64_t ld) {
+  const int64_t t = (int64_t)blockIdx.x * kQThreads + threadIdx.x;
+  const int64_t c = t % cols, b = t / cols;
+  if (b >= nblk) return;
+  int64_t r0, rend;
+  uint8_t *dst;
+  uint8_t *sdst;
+  if (ws) {
+    const WsView v = ws_view(ws, G);
+    if (!ws_usable(v.hdr, G, total_rows)) return;
+    const int32_t *__restrict__ pre = v.pre[tile_rows_index(128)];
+    if (b >= 4 * (int64_t)pre[G]) return;  // past the last group's padding: untouched
+    int lo = 0, hi = G;  // last g with 4 pre[g] <= b
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (4 * (int64_t)pre[mid] <= b) lo = mid; else hi = mid - 1;
+    }
+    const int g = lo;
+    r0 = v.off[g] + (b - 4 * (int64_t)pre[g]) * 32;
+    rend = v.off[g + 1];
+    dst = data + c * ld + b * 32;
+    sdst = scale + c * (ld / 32) + b;
+  } else {
+    const int64_t per = urows / 32, g = b / per, lb = b - g * per;
+    r0 = g * urows + lb * 32;
+    rend = r0 + 32;
+    dst = data + (g * cols + c) * urows + lb * 32;
+    sdst = scale + (g * cols + c) * per + lb;
+  }
+  uint32_t w[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int64_t r = r0 + 2 * i;
+    const uint32_t lo16 = r < rend ? src[r * cols + c] : 0u;
+    const uint32_t hi16 = r + 1 < rend ? src[(r + 1) * cols + c] : 0u;
+    w[i] = lo16 | (hi16 << 16);
+  }
+  uint32_t out[8];
+  uint8_t sbyte;
+  quantize_block(w, out, sbyte);
+  store_block(dst, out);
+  *sdst = sbyte;
 }
 
 hipError_t launch_quantize_mxfp8(const uint16_t *src, int64_t rows, int64_t cols, uint8_t *data, uint8_t *scale,
@@ -91,6 +158,30 @@ hipError_t launch_quantize_mxfp8(const uint16_t *src, int64_t rows, int64_t cols
   if (nblocks == 0) return hipSuccess;
   const int64_t grid = (nblocks + kQThreads - 1) / kQThreads;
   hipLaunchKernelGGL(quantize_mxfp8_kernel, dim3((unsigned)grid), dim3(kQThreads), 0, s, src, nblocks, data, scale);
+  return hipGetLastError();
+}
+
+// Group mode: ld columns of output per input column (a multiple of 128, at least
+// total_rows + 127 G, so every group's padded rows fit).
+hipError_t launch_quantize_mxfp8_colwise(const uint16_t *src, int64_t cols, int G, int64_t total_rows,
+                                         const void *ws, uint8_t *data, uint8_t *scale, int64_t ld, hipStream_t s) {
+  const int64_t nblk = ld / 32;
+  const int64_t threads = nblk * cols;
+  if (threads == 0) return hipSuccess;
+  hipLaunchKernelGGL(quantize_mxfp8_colwise_kernel, dim3((unsigned)((threads + kQThreads - 1) / kQThreads)),
+                     dim3(kQThreads), 0, s, src, cols, nblk, ws, G, total_rows, (int64_t)0, data, scale, ld);
+  return hipGetLastError();
+}
+
+// Uniform mode for stacked weights [G, N, K] (N % 32 == 0): codes [G, K, N], scales
+// [G, K, N / 32].
+hipError_t launch_quantize_mxfp8_colwise_weights(const uint16_t *w, int G, int64_t N, int64_t K, uint8_t *data,
+                                                 uint8_t *scale, hipStream_t s) {
+  const int64_t nblk = (int64_t)G * (N / 32);
+  const int64_t threads = nblk * K;
+  if (threads == 0) return hipSuccess;
+  hipLaunchKernelGGL(quantize_mxfp8_colwise_kernel, dim3((unsigned)((threads + kQThreads - 1) / kQThreads)),
+                     dim3(kQThreads), 0, s, w, K, nblk, (const void *)nullptr, G, (int64_t)0, N, data, scale, N);
   return hipGetLastError();
 }
 

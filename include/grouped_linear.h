@@ -176,6 +176,73 @@ int gl_group_quantize_mxfp8(const void *src, int64_t rows, int64_t cols, uint8_t
                             uint8_t *scale, hipStream_t stream);
 
 /* Message of the last error on this thread ("" if none). */
+/*
+ * ---------------------------------------------------------------- MXFP8 backward
+ * The quantized backward pass (page "transformer_engine/pytorch/ops/basic/
+ * grouped_linear.py", op_forward and fuser_backward: dgrad runs on the grad output
+ * quantized rowwise and the weights quantized columnwise; wgrad on the input and
+ * the grad output quantized columnwise, each split on its own) contracts over
+ * out_features in dgrad and over token rows in wgrad, so those operands carry
+ * blocks of 32 along the rows.  This library stores columnwise codes transposed, so
+ * a block's 32 codes are contiguous (the scale rule is the rowwise one, OCP MX v1.0):
+ *   activations [T, C] split into groups -> codes [C, ld] and scales [C, ld / 32];
+ *     group g's rows occupy columns [poff[g], poff[g] + m_g) with
+ *     poff[g] = 128 * sum_{h<g} ceil(m_h / 128); its rows up to the next multiple
+ *     of 128 are zero codes with scale byte 0; a group's last block may hold fewer
+ *     than 32 rows (the zero padding leaves its amax unchanged).
+ *   weights [G, N, K] -> codes [G, K, N] and scales [G, K, N / 32].
+ */
+
+/* Smallest row length ld of the transposed columnwise activation layout that fits
+ * any split of total_rows rows into num_groups groups: T + 127 G rounded up to 128
+ * (-1 for invalid sizes). */
+int64_t gl_colwise_ld(int num_groups, int64_t total_rows);
+
+/*
+ * Columnwise MXFP8 group quantization of bf16 activations src [total_rows, cols]
+ * (x or dy) into the transposed layout above, with the groups of the workspace
+ * written by gl_offsets.  ld: a multiple of 128, at least gl_colwise_ld and at most
+ * 2^23.  Columns past the last group's padding are not written.  data_t 16-byte
+ * aligned.  Split sizes found invalid by gl_offsets: nothing is written.
+ */
+int gl_group_quantize_mxfp8_colwise(const void *src, int64_t cols, int num_groups, int64_t total_rows,
+                                    const void *workspace, uint8_t *data_t, uint8_t *scale_t, int64_t ld,
+                                    hipStream_t stream);
+
+/*
+ * Columnwise MXFP8 of stacked bf16 weights w [G, N, K] (blocks of 32 along N, the
+ * dgrad contraction) into codes [G, K, N] and scales [G, K, N / 32]; N % 32 == 0.
+ */
+int gl_quantize_mxfp8_colwise_weights(const void *w, int num_groups, int64_t out_features, int64_t in_features,
+                                      uint8_t *data_t, uint8_t *scale_t, hipStream_t stream);
+
+/*
+ * MXFP8 grouped dgrad dx = deq(dy) deq(W_g) (page "transformer_engine/pytorch/ops/
+ * basic/grouped_linear.py", fuser_backward "Perform dgrad GEMMs" on quantized
+ * operands), fp32 accumulation.
+ *   dy, dy_scale   rowwise codes [T, N] and scales [T, N / 32] (gl_group_quantize_mxfp8)
+ *   w_t, w_t_scale columnwise weight codes [G, K, N] and scales [G, K, N / 32]
+ *   out_dtype      GL_BF16 or GL_F32 for dx [dx_rows, K], dx_rows >= T, rows >= T untouched
+ *   N % 128 == 0, K % 8 == 0.
+ */
+int gl_dgrad_mxfp8(int num_groups, int64_t in_features, int64_t out_features, int64_t total_rows,
+                   gl_dtype out_dtype, const uint8_t *dy, const uint8_t *dy_scale, const uint8_t *w_t,
+                   const uint8_t *w_t_scale, void *dx, int64_t dx_rows, const void *workspace, hipStream_t stream);
+
+/*
+ * MXFP8 grouped wgrad dW_g (+)= deq(dy_g)^T deq(x_g) (page "transformer_engine/
+ * pytorch/ops/basic/grouped_linear.py", fuser_backward "Perform wgrad GEMMs" on
+ * quantized operands), fp32 accumulation, from columnwise codes in the transposed
+ * group layout: dy_t [N, ld] / dy_t_scale [N, ld / 32], x_t [K, ld] / x_t_scale
+ * [K, ld / 32] (gl_group_quantize_mxfp8_colwise with the same workspace and ld).
+ * dw / dw_ptrs, out_dtype and accumulate as in gl_wgrad (an empty group: zeros, or
+ * untouched when accumulating).  K % 8 == 0, N % 8 == 0.
+ */
+int gl_wgrad_mxfp8(int num_groups, int64_t in_features, int64_t out_features, int64_t total_rows, gl_dtype out_dtype,
+                   const uint8_t *dy_t, const uint8_t *dy_t_scale, const uint8_t *x_t, const uint8_t *x_t_scale,
+                   int64_t ld, void *dw, void *const *dw_ptrs, int accumulate, const void *workspace,
+                   hipStream_t stream);
+
 const char *gl_last_error(void);
 
 /* Library identification string. */

@@ -92,6 +92,20 @@ def test_other_entry_points_reject():
     assert lib.gl_group_quantize_mxfp8(FAKE, -1, 64, FAKE2, FAKE2, None) == -1
     assert lib.gl_group_quantize_mxfp8(FAKE + 2, 4, 64, FAKE2, FAKE2, None) == -1
     assert lib.gl_read_status(None, None, None) == -1
+    # MXFP8 backward: layout and shape rules
+    ld = lib.gl_colwise_ld(4, 1000)
+    assert ld == 1536 and lib.gl_colwise_ld(0, 10) == -1
+    assert lib.gl_group_quantize_mxfp8_colwise(FAKE, 64, 4, 1000, FAKE, FAKE2, FAKE2, ld - 128, None) == -3
+    assert lib.gl_group_quantize_mxfp8_colwise(FAKE, 64, 4, 1000, FAKE, FAKE2, FAKE2, ld + 64, None) == -3
+    assert lib.gl_group_quantize_mxfp8_colwise(FAKE, 64, 4, 1000, None, FAKE2, FAKE2, ld, None) == -1
+    assert lib.gl_quantize_mxfp8_colwise_weights(FAKE, 2, 48, 64, FAKE2, FAKE2, None) == -3
+    assert lib.gl_dgrad_mxfp8(4, 64, 192, 32, gl.GL_BF16, FAKE, FAKE, FAKE, FAKE, FAKE2, 32, FAKE, None) == -3
+    assert lib.gl_dgrad_mxfp8(4, 64, 256, 32, gl.GL_E4M3, FAKE, FAKE, FAKE, FAKE, FAKE2, 32, FAKE, None) == -2
+    assert lib.gl_dgrad_mxfp8(4, 64, 256, 32, gl.GL_BF16, FAKE, FAKE, FAKE, FAKE, FAKE2, 16, FAKE, None) == -3
+    assert lib.gl_wgrad_mxfp8(4, 64, 32, 1000, gl.GL_F32, FAKE, FAKE, FAKE, FAKE, ld - 128, FAKE2, None, 1, FAKE,
+                              None) == -3
+    assert lib.gl_wgrad_mxfp8(4, 64, 32, 1000, gl.GL_F32, FAKE, FAKE, FAKE, FAKE, ld, FAKE2, FAKE2, 1, FAKE,
+                              None) == -1
 
 
 def test_zero_rows_is_a_no_op_without_device_work():

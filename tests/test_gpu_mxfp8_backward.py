@@ -1,0 +1,177 @@
+"""GPU parity of the MXFP8 backward entry points through the C ABI: columnwise
+group quantization (activations and weights) bit-exact against the oracle, the MXFP8
+dgrad and wgrad within the bf16 tolerance of the oracle on the dequantized operands
+(bit-exact on inputs MX represents exactly), at oracle-sized shapes with ragged and
+empty groups and at the MXFP8 workload's sizes."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import grouped_gemm_gl_amd as gl
+import oracle
+import synth
+from gl_testutil import TOL_BF16, assert_bits_equal, assert_close, nan_tail, to64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+SHAPES = [
+    # (G, K, N, m): N % 128 == 0 for the dgrad contraction; ragged / empty groups
+    (4, 96, 256, [3, 33, 0, 70]),
+    (3, 200, 128, [0, 300, 129]),
+    (1, 64, 384, [200]),
+    (6, 136, 256, [256, 1, 0, 128, 31, 0]),
+]
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def workspace_for(m, T):
+    ws = gl.new_workspace(len(m))
+    gl.gl_offsets(torch.tensor(m, dtype=torch.int64, device=DEV), T, ws)
+    return ws
+
+
+def colwise(src_bf16, m, ws, ld):
+    C = src_bf16.shape[1]
+    q = torch.full((C, ld), 0xAB, dtype=torch.uint8, device=DEV)   # sentinel past the padding
+    s = torch.full((C, ld // 32), 0xAB, dtype=torch.uint8, device=DEV)
+    gl.gl_group_quantize_mxfp8_colwise(src_bf16.to(DEV), q, s, ws, len(m))
+    return q, s
+
+
+@pytest.mark.parametrize("G,K,N,m", SHAPES)
+def test_colwise_quantize_bit_exact(G, K, N, m):
+    say(f"colwise quantize m={m} K={K}")
+    T = sum(m)
+    g = torch.Generator().manual_seed(T + K)
+    x = (torch.randn(T, K, generator=g) * torch.exp(torch.randn(1, K, generator=g) * 3)).to(torch.bfloat16)
+    if T > 40:
+        x[5, 7] = float("inf")      # a non-finite block: scale 0xFF, NaN codes
+        x[20:40, 3] = 0.0
+    ws = workspace_for(m, T)
+    ld = gl.gl_colwise_ld(G, T)
+    q, s = colwise(x, m, ws, ld)
+    rq, rs, poff = oracle.quantize_mxfp8_colwise(to64(x), m, ld=ld)
+    end = int(poff[-1])
+    assert np.array_equal(q[:, :end].cpu().numpy(), rq[:, :end])
+    assert np.array_equal(s[:, : end // 32].cpu().numpy(), rs[:, : end // 32])
+    assert (q[:, end:] == 0xAB).all() and (s[:, end // 32:] == 0xAB).all(), "columns past the padding"
+
+
+def test_colwise_weights_bit_exact():
+    G, N, K = 3, 160, 72
+    g = torch.Generator().manual_seed(1)
+    w = (torch.randn(G, N, K, generator=g) * 0.02).to(torch.bfloat16)
+    q = torch.empty(G, K, N, dtype=torch.uint8, device=DEV)
+    s = torch.empty(G, K, N // 32, dtype=torch.uint8, device=DEV)
+    gl.gl_quantize_mxfp8_colwise_weights(w.to(DEV), q, s)
+    rq, rs = oracle.quantize_mxfp8_colwise_weights(to64(w))
+    assert np.array_equal(q.cpu().numpy(), rq) and np.array_equal(s.cpu().numpy(), rs)
+
+
+def quantized_operands(x, w, dy, m, ws):
+    G, N, K = w.shape
+    T = x.shape[0]
+    ld = gl.gl_colwise_ld(G, T)
+    dq = torch.empty(T, N, dtype=torch.uint8, device=DEV)
+    ds = torch.empty(T, N // 32, dtype=torch.uint8, device=DEV)
+    gl.gl_group_quantize_mxfp8(dy.to(DEV), dq, ds)
+    wtq = torch.empty(G, K, N, dtype=torch.uint8, device=DEV)
+    wts = torch.empty(G, K, N // 32, dtype=torch.uint8, device=DEV)
+    gl.gl_quantize_mxfp8_colwise_weights(w.to(DEV), wtq, wts)
+    dyq, dys = colwise(dy, m, ws, ld)
+    xq, xs = colwise(x, m, ws, ld)
+    return dict(dq=dq, ds=ds, wtq=wtq, wts=wts, dyq=dyq, dys=dys, xq=xq, xs=xs, ld=ld)
+
+
+def check_backward(x, w, dy, m, exact, accumulate, dx_dtype=torch.bfloat16):
+    G, N, K = w.shape
+    T = x.shape[0]
+    ws = workspace_for(m, T)
+    q = quantized_operands(x, w, dy, m, ws)
+    dx = nan_tail(T + 5, K, T, dx_dtype, DEV)
+    gl.gl_dgrad_mxfp8(q["dq"], q["ds"], q["wtq"], q["wts"], dx, ws)
+    mg = torch.randn(G, N, K, generator=torch.Generator().manual_seed(3))
+    dw = mg.to(DEV) if accumulate else torch.full((G, N, K), float("nan"), device=DEV)
+    gl.gl_wgrad_mxfp8(q["dyq"], q["dys"], q["xq"], q["xs"], dw, ws, T, accumulate=accumulate)
+    torch.cuda.synchronize()
+    assert torch.isnan(dx[T:]).all(), "dgrad wrote past the valid rows"
+    c = lambda t: t.cpu().numpy()
+    ref_dx = oracle.dgrad_mxfp8(c(q["dq"]), c(q["ds"]), c(q["wtq"]), c(q["wts"]), m)
+    end = int(oracle.colwise_offsets(m)[-1])
+    ref_dw = oracle.wgrad_mxfp8(c(q["dyq"])[:, :end], c(q["dys"])[:, : end // 32], c(q["xq"])[:, :end],
+                                c(q["xs"])[:, : end // 32], m, main_grad=to64(mg) if accumulate else None,
+                                accumulate=accumulate)
+    if exact:
+        assert np.array_equal(to64(dx[:T]), ref_dx), "dx not exact"
+        assert np.array_equal(to64(dw), ref_dw), "dW not exact"
+    else:
+        assert_close(dx[:T], ref_dx, TOL_BF16, "MXFP8 dx")
+        assert_close(dw, ref_dw, TOL_BF16, "MXFP8 dW")
+
+
+@pytest.mark.parametrize("G,K,N,m", SHAPES)
+@pytest.mark.parametrize("accumulate", [False, True])
+def test_mxfp8_dgrad_wgrad(G, K, N, m, accumulate):
+    say(f"MXFP8 dgrad/wgrad m={m} K={K} N={N} accumulate={accumulate}")
+    T = sum(m)
+    g = torch.Generator().manual_seed(G * 31 + N)
+    x = torch.randn(T, K, generator=g).to(torch.bfloat16)
+    w = (torch.randn(G, N, K, generator=g) * 0.05).to(torch.bfloat16)
+    dy = torch.randn(T, N, generator=g).to(torch.bfloat16)
+    check_backward(x, w, dy, m, exact=False, accumulate=accumulate)
+
+
+def test_mxfp8_backward_exact_on_representable_inputs():
+    # integers in [-14, 14] with a magnitude-8 element opening every block along each
+    # quantization direction: MX quantization is lossless and every fp32 sum exact
+    G, K, N, m = 4, 96, 256, [3, 33, 0, 70]
+    T = sum(m)
+    rng = np.random.default_rng(2)
+    off = np.concatenate([[0], np.cumsum(m)])
+    base = lambda r, c_: rng.integers(-14, 15, size=(r, c_)).astype(np.float32)
+    dy = base(T, N)
+    dy[:, ::32] = 8.0                    # rowwise blocks (dgrad)
+    for a, b in zip(off[:-1], off[1:]):
+        dy[a:b:32, :] = -8.0            # columnwise blocks per group (wgrad); both hold
+    x = base(T, K)
+    for a, b in zip(off[:-1], off[1:]):
+        x[a:b:32, :] = 8.0
+    w = base(G * N, K).reshape(G, N, K)
+    w[:, ::32, :] = 8.0                  # columnwise weight blocks along N
+    to_bf = lambda a: torch.from_numpy(a).to(torch.bfloat16)
+    check_backward(to_bf(x), to_bf(w), to_bf(dy), m, exact=True, accumulate=False, dx_dtype=torch.float32)
+
+
+def test_mxfp8_backward_full_size():
+    wl = synth.WORKLOADS["mxfp8_fwd_g32_k4096_n4096"]
+    say(f"workload {wl.name}: MXFP8 backward at full size")
+    m = synth.split_sizes(wl)
+    G, K, N, T = wl.G, wl.K, wl.N, wl.T
+    x, w = synth.x(wl), synth.weight(wl)
+    dy = synth.dy(wl)
+    ws = workspace_for(m.tolist(), T)
+    q = quantized_operands(x, w, dy, m.tolist(), ws)
+    dx = torch.empty(T, K, dtype=torch.bfloat16, device=DEV)
+    gl.gl_dgrad_mxfp8(q["dq"], q["ds"], q["wtq"], q["wts"], dx, ws)
+    dw = torch.empty(G, N, K, dtype=torch.bfloat16, device=DEV)
+    gl.gl_wgrad_mxfp8(q["dyq"], q["dys"], q["xq"], q["xs"], dw, ws, T)
+    torch.cuda.synchronize()
+    say("  checking samples against the oracle")
+    off = np.concatenate([[0], np.cumsum(m)])
+    rows = np.unique(np.concatenate([off[:-1], off[1:] - 1, np.random.default_rng(0).integers(0, T, 24)]))
+    c = lambda t: t.cpu().numpy()
+    ref_dx = oracle.dgrad_mxfp8(c(q["dq"]), c(q["ds"]), c(q["wtq"]), c(q["wts"]), m, rows=rows)
+    assert_close(dx[torch.from_numpy(rows).to(DEV)], ref_dx, TOL_BF16, "MXFP8 dx rows")
+    groups, nsel = [0, int(np.argmax(m)), G - 1], np.array([0, 1, 2047, N - 1])
+    end = int(oracle.colwise_offsets(m)[-1])
+    # only the selected output rows (n) of dy_t are needed for those wgrad rows
+    dyq = c(q["dyq"][torch.from_numpy(nsel).to(DEV)])[:, :end]
+    dys = c(q["dys"][torch.from_numpy(nsel).to(DEV)])[:, : end // 32]
+    ref_dw = oracle.wgrad_mxfp8(dyq, dys, c(q["xq"])[:, :end], c(q["xs"])[:, : end // 32], m, groups=groups)
+    assert_close(dw[groups][:, torch.from_numpy(nsel).to(DEV)], ref_dw, TOL_BF16, "MXFP8 dW rows")
