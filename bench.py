@@ -33,9 +33,10 @@ METRIC = "grouped GEMM TFLOP/s (fwd+dgrad+wgrad) and % of MFMA peak, bf16 & MXFP
 GEMM_SRCS = [os.path.join(ROOT, "grouped_gemm_gl_amd", "csrc", f)
              for f in ("gl_gemm_tile.hpp", "gl_gemm_bf16.hip", "gl_gemm_mxfp8.hip")]
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
-# kernel-name fragment of each pass's GEMM (template arguments <A K-major, B K-major, mode>)
-PASS_KERNELS = {"forward": "gemm_bf16_kernel<true, true, 0>", "dgrad": "gemm_bf16_kernel<true, false, 0>",
-                "wgrad": "gemm_bf16_kernel<false, false, 1>", "mx_forward": "gemm_mxfp8_kernel"}
+# kernel-name fragment of each pass's GEMM (template arguments <A K-major, B K-major, mode, fp16>)
+PASS_KERNELS = {"forward": "gemm_bf16_kernel<true, true, 0, false>",
+                "dgrad": "gemm_bf16_kernel<true, false, 0, false>",
+                "wgrad": "gemm_bf16_kernel<false, false, 1, false>", "mx_forward": "gemm_mxfp8_kernel<0>"}
 PASS_WORKLOAD = {"forward": "bf16_train_g8_k4096_n14336", "dgrad": "bf16_train_g8_k4096_n14336",
                  "wgrad": "bf16_train_g8_k4096_n14336", "mx_forward": "mxfp8_fwd_g32_k4096_n4096"}
 COPY_BYTES = 1 << 30

@@ -17,11 +17,11 @@ namespace gl {
 hipError_t launch_offsets(const int64_t *m_splits, int G, int64_t total_rows, void *ws, hipStream_t stream);
 hipError_t launch_forward_bf16(int G, int64_t K, int64_t N, int64_t T, const uint16_t *x, const uint16_t *w,
                                const uint16_t *const *w_ptrs, const void *bias, const void *const *bias_ptrs,
-                               uint16_t *y, const void *ws, hipStream_t s);
+                               uint16_t *y, int f16, const void *ws, hipStream_t s);
 hipError_t launch_dgrad_bf16(int G, int64_t K, int64_t N, int64_t T, const uint16_t *dy, const uint16_t *w,
-                             const uint16_t *const *w_ptrs, uint16_t *dx, const void *ws, hipStream_t s);
+                             const uint16_t *const *w_ptrs, uint16_t *dx, int f16, const void *ws, hipStream_t s);
 hipError_t launch_wgrad_bf16(int G, int64_t K, int64_t N, int64_t T, const uint16_t *x, const uint16_t *dy,
-                             void *dw, void *const *dw_ptrs, int out_f32, int accumulate, const void *ws,
+                             void *dw, void *const *dw_ptrs, int out_f32, int accumulate, int f16, const void *ws,
                              hipStream_t s);
 hipError_t launch_forward_mxfp8(int G, int64_t K, int64_t N, int64_t T, const uint8_t *xq, const uint8_t *xs,
                                 const uint8_t *wq, const uint8_t *const *wq_ptrs, const uint8_t *ws_scale,
@@ -35,7 +35,7 @@ hipError_t launch_dgrad_f32(int G, int64_t K, int64_t N, int64_t T, const float 
                             const float *const *w_ptrs, float *dx, const void *ws, hipStream_t s);
 hipError_t launch_wgrad_f32(int G, int64_t K, int64_t N, int64_t T, const float *x, const float *dy, float *dw,
                             float *const *dw_ptrs, int accumulate, const void *ws, hipStream_t s);
-hipError_t launch_bgrad(int G, int64_t N, int64_t T, int f32, const void *dy, void *db, void *const *db_ptrs,
+hipError_t launch_bgrad(int G, int64_t N, int64_t T, int el, const void *dy, void *db, void *const *db_ptrs,
                         const void *ws, hipStream_t s);
 hipError_t launch_quantize_mxfp8(const uint16_t *src, int64_t rows, int64_t cols, uint8_t *data, uint8_t *scale,
                                  hipStream_t s);
@@ -84,10 +84,12 @@ int check_sizes(int G, int64_t K, int64_t N, int64_t T) {
 }
 
 int check_float_dtype(gl_dtype d, const char *what) {
-  if (d == GL_F16) return fail(GL_ERR_UNSUPPORTED, "%s: fp16 is not built in this library", what);
-  if (d != GL_F32 && d != GL_BF16) return fail(GL_ERR_DTYPE, "%s: dtype must be GL_F32 or GL_BF16", what);
+  if (d != GL_F32 && d != GL_BF16 && d != GL_F16)
+    return fail(GL_ERR_DTYPE, "%s: dtype must be GL_F32, GL_BF16 or GL_F16", what);
   return GL_OK;
 }
+
+bool is16(gl_dtype d) { return d == GL_BF16 || d == GL_F16; }
 
 int check_one_form(const void *stacked, const void *ptrs, const char *what, bool optional) {
   if (stacked && ptrs) return fail(GL_ERR_ARG, "%s: pass either the stacked buffer or the pointer array, not both", what);
@@ -109,11 +111,11 @@ int check_buf(const void *p, int64_t T, const char *what) {
 constexpr int64_t kMaxBf16Dim = (int64_t)1 << 22;
 
 int check_bf16_dims(gl_dtype d, int64_t K, int64_t N) {
-  if (d == GL_BF16 && (K % 8 || N % 8))
-    return fail(GL_ERR_SHAPE, "bf16 needs in_features and out_features that are multiples of 8 (got %lld, %lld)",
+  if (is16(d) && (K % 8 || N % 8))
+    return fail(GL_ERR_SHAPE, "bf16/fp16 need in_features and out_features that are multiples of 8 (got %lld, %lld)",
                 (long long)K, (long long)N);
-  if (d == GL_BF16 && (K > kMaxBf16Dim || N > kMaxBf16Dim))
-    return fail(GL_ERR_SHAPE, "bf16 in_features and out_features must be at most %lld (got %lld, %lld)",
+  if (is16(d) && (K > kMaxBf16Dim || N > kMaxBf16Dim))
+    return fail(GL_ERR_SHAPE, "bf16/fp16 in_features and out_features must be at most %lld (got %lld, %lld)",
                 (long long)kMaxBf16Dim, (long long)K, (long long)N);
   return GL_OK;
 }
@@ -189,14 +191,16 @@ int gl_forward(int num_groups, int64_t in_features, int64_t out_features, int64_
                       "gl_forward");
   }
   GL_TRY(check_float_dtype(in_dtype, "gl_forward"));
-  if (out_dtype != in_dtype) return fail(GL_ERR_DTYPE, "gl_forward: out_dtype must equal in_dtype for fp32/bf16");
+  if (out_dtype != in_dtype)
+    return fail(GL_ERR_DTYPE, "gl_forward: out_dtype must equal in_dtype for fp32/bf16/fp16");
   if (x_scale || w_scale || w_scale_ptrs) return fail(GL_ERR_ARG, "scales are only for GL_E4M3 inputs");
   GL_TRY(check_bf16_dims(in_dtype, K, N));
   if (T == 0) return ok();
   hipError_t e;
-  if (in_dtype == GL_BF16)
+  if (is16(in_dtype))
     e = gl::launch_forward_bf16(G, K, N, T, (const uint16_t *)x, (const uint16_t *)w,
-                                (const uint16_t *const *)w_ptrs, bias, bias_ptrs, (uint16_t *)y, workspace, stream);
+                                (const uint16_t *const *)w_ptrs, bias, bias_ptrs, (uint16_t *)y, in_dtype == GL_F16,
+                                workspace, stream);
   else
     e = gl::launch_forward_f32(G, K, N, T, (const float *)x, (const float *)w, (const float *const *)w_ptrs,
                                (const float *)bias, (const float *const *)bias_ptrs, (float *)y, workspace, stream);
@@ -219,9 +223,9 @@ int gl_dgrad(int num_groups, int64_t in_features, int64_t out_features, int64_t 
   GL_TRY(check_buf(dx, T, "dx"));
   if (T == 0) return ok();
   hipError_t e;
-  if (dtype == GL_BF16)
+  if (is16(dtype))
     e = gl::launch_dgrad_bf16(G, K, N, T, (const uint16_t *)dy, (const uint16_t *)w, (const uint16_t *const *)w_ptrs,
-                              (uint16_t *)dx, workspace, stream);
+                              (uint16_t *)dx, dtype == GL_F16, workspace, stream);
   else
     e = gl::launch_dgrad_f32(G, K, N, T, (const float *)dy, (const float *)w, (const float *const *)w_ptrs,
                              (float *)dx, workspace, stream);
@@ -236,8 +240,8 @@ int gl_wgrad(int num_groups, int64_t in_features, int64_t out_features, int64_t 
   GL_TRY(check_sizes(G, K, N, T));
   GL_TRY(check_float_dtype(in_dtype, "gl_wgrad"));
   GL_TRY(check_float_dtype(out_dtype, "gl_wgrad"));
-  if (in_dtype == GL_F32 && out_dtype != GL_F32)
-    return fail(GL_ERR_DTYPE, "gl_wgrad: fp32 inputs need an fp32 weight gradient");
+  if (out_dtype != GL_F32 && out_dtype != in_dtype)
+    return fail(GL_ERR_DTYPE, "gl_wgrad: the weight gradient is fp32 or the input type");
   GL_TRY(check_bf16_dims(in_dtype, K, N));
   if (!workspace) return fail(GL_ERR_ARG, "workspace is NULL");
   GL_TRY(check_one_form(dw, dw_ptrs, "weight gradient", false));
@@ -245,9 +249,9 @@ int gl_wgrad(int num_groups, int64_t in_features, int64_t out_features, int64_t 
   GL_TRY(check_buf(dy, T, "dy"));
   if (accumulate != 0 && accumulate != 1) return fail(GL_ERR_ARG, "accumulate must be 0 or 1");
   hipError_t e;
-  if (in_dtype == GL_BF16)
+  if (is16(in_dtype))
     e = gl::launch_wgrad_bf16(G, K, N, T, (const uint16_t *)x, (const uint16_t *)dy, dw, dw_ptrs,
-                              out_dtype == GL_F32, accumulate, workspace, stream);
+                              out_dtype == GL_F32, accumulate, in_dtype == GL_F16, workspace, stream);
   else
     e = gl::launch_wgrad_f32(G, K, N, T, (const float *)x, (const float *)dy, (float *)dw, (float *const *)dw_ptrs,
                              accumulate, workspace, stream);
@@ -260,12 +264,14 @@ int gl_bgrad(int num_groups, int64_t out_features, int64_t total_rows, gl_dtype 
   const int64_t N = out_features, T = total_rows;
   GL_TRY(check_sizes(G, 8, N, T));
   GL_TRY(check_float_dtype(dtype, "gl_bgrad"));
-  if (N % (dtype == GL_BF16 ? 8 : 4))
-    return fail(GL_ERR_SHAPE, "gl_bgrad needs out_features %% %d == 0", dtype == GL_BF16 ? 8 : 4);
+  if (N % (is16(dtype) ? 8 : 4))
+    return fail(GL_ERR_SHAPE, "gl_bgrad needs out_features %% %d == 0", is16(dtype) ? 8 : 4);
   if (!workspace) return fail(GL_ERR_ARG, "workspace is NULL");
   GL_TRY(check_one_form(db, db_ptrs, "bias gradient", false));
   GL_TRY(check_buf(dy, T, "dy"));
-  return hip_result(gl::launch_bgrad(G, N, T, dtype == GL_F32, dy, db, db_ptrs, workspace, stream), "gl_bgrad");
+  return hip_result(gl::launch_bgrad(G, N, T, dtype == GL_F32 ? 1 : dtype == GL_F16 ? 2 : 0, dy, db, db_ptrs, workspace,
+                                     stream),
+                    "gl_bgrad");
 }
 
 int gl_group_quantize_mxfp8(const void *src, int64_t rows, int64_t cols, uint8_t *data, uint8_t *scale,

@@ -12,9 +12,12 @@ namespace gl {
 
 constexpr int kBgThreads = 512, kBgWaves = kBgThreads / 64, kBgCols = 512, kBgUnroll = 8;
 
-template <bool F32>
+// element type of dy and db: 0 bf16, 1 fp32, 2 fp16
+enum { BG_BF16 = 0, BG_F32 = 1, BG_F16 = 2 };
+
+template <int EL>
 __device__ __forceinline__ void add16(float *a, const uint4 &v) {
-  if constexpr (F32) {
+  if constexpr (EL == BG_F32) {
     a[0] += __uint_as_float(v.x);
     a[1] += __uint_as_float(v.y);
     a[2] += __uint_as_float(v.z);
@@ -23,19 +26,20 @@ __device__ __forceinline__ void add16(float *a, const uint4 &v) {
     const uint32_t d[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      a[2 * e] += bf16_to_f32(d[e] & 0xffff);
-      a[2 * e + 1] += bf16_to_f32(d[e] >> 16);
+      a[2 * e] += h16_to_f32<EL == BG_F16>(d[e] & 0xffff);
+      a[2 * e + 1] += h16_to_f32<EL == BG_F16>(d[e] >> 16);
     }
   }
 }
 
-template <bool F32>
+template <int EL>
 __global__ __launch_bounds__(kBgThreads) void bgrad_kernel(const void *__restrict__ dy_, void *db_,
                                                            void *const *db_ptrs, int G, int64_t N, int64_t T,
                                                            const void *ws_) {
   __shared__ float part[kBgWaves][kBgCols];
   const WsView ws = ws_view(ws_, G);
   if (!ws_usable(ws.hdr, G, T)) return;
+  constexpr bool F32 = EL == BG_F32;
   constexpr int kEl = F32 ? 4 : 8;  // elements per 16-byte lane load
   constexpr int kEsz = F32 ? 4 : 2;
   const int g = blockIdx.y;
@@ -58,9 +62,9 @@ __global__ __launch_bounds__(kBgThreads) void bgrad_kernel(const void *__restric
 #pragma unroll
         for (int u = 0; u < kBgUnroll; ++u) v[u] = *(const uint4 *)(dy + ((r + u * kBgWaves) * N + col) * kEsz);
 #pragma unroll
-        for (int u = 0; u < kBgUnroll; ++u) add16<F32>(a, v[u]);
+        for (int u = 0; u < kBgUnroll; ++u) add16<EL>(a, v[u]);
       }
-      for (; r < hi; r += kBgWaves) add16<F32>(a, *(const uint4 *)(dy + (r * N + col) * kEsz));
+      for (; r < hi; r += kBgWaves) add16<EL>(a, *(const uint4 *)(dy + (r * N + col) * kEsz));
     }
 #pragma unroll
     for (int e = 0; e < kEl; ++e) part[wave][lc + e] = a[e];
@@ -74,17 +78,20 @@ __global__ __launch_bounds__(kBgThreads) void bgrad_kernel(const void *__restric
     for (int w = 0; w < kBgWaves; ++w) s += part[w][c];
     char *dst = db_ ? (char *)db_ + ((int64_t)g * N + col) * kEsz : (char *)db_ptrs[g] + col * kEsz;
     if constexpr (F32) *(float *)dst = s;
-    else *(uint16_t *)dst = f32_to_bf16(s);
+    else *(uint16_t *)dst = f32_to_h16<EL == BG_F16>(s);
   }
 }
 
-hipError_t launch_bgrad(int G, int64_t N, int64_t T, int f32, const void *dy, void *db, void *const *db_ptrs,
+// el: 0 bf16, 1 fp32, 2 fp16
+hipError_t launch_bgrad(int G, int64_t N, int64_t T, int el, const void *dy, void *db, void *const *db_ptrs,
                         const void *ws, hipStream_t s) {
   dim3 grid((unsigned)((N + kBgCols - 1) / kBgCols), (unsigned)G);
-  if (f32)
-    hipLaunchKernelGGL(bgrad_kernel<true>, grid, dim3(kBgThreads), 0, s, dy, db, db_ptrs, G, N, T, ws);
+  if (el == BG_F32)
+    hipLaunchKernelGGL(bgrad_kernel<BG_F32>, grid, dim3(kBgThreads), 0, s, dy, db, db_ptrs, G, N, T, ws);
+  else if (el == BG_F16)
+    hipLaunchKernelGGL(bgrad_kernel<BG_F16>, grid, dim3(kBgThreads), 0, s, dy, db, db_ptrs, G, N, T, ws);
   else
-    hipLaunchKernelGGL(bgrad_kernel<false>, grid, dim3(kBgThreads), 0, s, dy, db, db_ptrs, G, N, T, ws);
+    hipLaunchKernelGGL(bgrad_kernel<BG_BF16>, grid, dim3(kBgThreads), 0, s, dy, db, db_ptrs, G, N, T, ws);
   return hipGetLastError();
 }
 

@@ -81,6 +81,7 @@ __device__ __forceinline__ int find_group(const int32_t *__restrict__ pre, int G
 
 // ---------------------------------------------------------------- bf16 helpers --
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(8))) int i32x8_t;
@@ -95,6 +96,15 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   u += 0x7fffu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
 }
+
+// fp16 <-> fp32 (the float -> half conversion rounds to nearest even; overflow gives inf)
+__device__ __forceinline__ float f16_to_f32(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+__device__ __forceinline__ uint16_t f32_to_f16(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+// 16-bit storage type of a kernel's inputs / 16-bit outputs: bf16 or fp16
+template <bool F16>
+__device__ __forceinline__ float h16_to_f32(uint16_t h) { return F16 ? f16_to_f32(h) : bf16_to_f32(h); }
+template <bool F16>
+__device__ __forceinline__ uint16_t f32_to_h16(float f) { return F16 ? f32_to_f16(f) : f32_to_bf16(f); }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);

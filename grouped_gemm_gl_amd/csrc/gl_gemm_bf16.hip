@@ -51,7 +51,9 @@ namespace gl {
 
 namespace gemm {
 
-template <bool A_KMAJ, bool B_KMAJ, int MODE>
+// F16: the operands are fp16 (v_mfma_f32_32x32x16_f16) instead of bf16; staging and
+// fragments are the same 16-byte moves of 2-byte elements.
+template <bool A_KMAJ, bool B_KMAJ, int MODE, bool F16>
 __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
   __shared__ __attribute__((aligned(1024))) char lds[kS * kStageBytes];
 
@@ -115,7 +117,10 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
       for (int ii = 0; ii < kNI; ++ii)
 #pragma unroll
         for (int jj = 0; jj < kNJ; ++jj)
-          acc[ii][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[jj], af[ii], acc[ii][jj], 0, 0, 0);
+          acc[ii][jj] = F16 ? __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, bfr[jj]),
+                                                                    __builtin_bit_cast(f16x8_t, af[ii]), acc[ii][jj],
+                                                                    0, 0, 0)
+                            : __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[jj], af[ii], acc[ii][jj], 0, 0, 0);
     };
 
     bf16x8_t fa[2][kNI], fb[2][kNJ];
@@ -169,7 +174,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
     for (; kt < nk; ++kt) body(kt, false);
     __builtin_amdgcn_s_barrier();  // every wave is done with the ring before it is refilled
 
-    store_tile<MODE>(p, t, acc, wm, wn, lane);
+    store_tile<MODE, F16>(p, t, acc, wm, wn, lane);
   }
 }
 
@@ -178,7 +183,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
 // forward: y = x W^T (+ b); A = x [T,K], B = W [N,K]
 hipError_t launch_forward_bf16(int G, int64_t K, int64_t N, int64_t T, const uint16_t *x, const uint16_t *w,
                                const uint16_t *const *w_ptrs, const void *bias, const void *const *bias_ptrs,
-                               uint16_t *y, const void *ws, hipStream_t s) {
+                               uint16_t *y, int f16, const void *ws, hipStream_t s) {
   using namespace gemm;
   Params p{};
   p.A = x; p.lda = K;
@@ -189,13 +194,18 @@ hipError_t launch_forward_bf16(int G, int64_t K, int64_t N, int64_t T, const uin
   p.cols_j = N; p.P = K;
   p.tiles_j = (int)((N + kBN - 1) / kBN);
   const int64_t max_items = ((T + kBM - 1) / kBM + G) * p.tiles_j;
-  hipLaunchKernelGGL((gemm_bf16_kernel<true, true, MODE_ROWS>), dim3(persistent_grid(max_items)), dim3(kThreads), 0, s, p);
+  if (f16)
+    hipLaunchKernelGGL((gemm_bf16_kernel<true, true, MODE_ROWS, true>), dim3(persistent_grid(max_items)),
+                       dim3(kThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL((gemm_bf16_kernel<true, true, MODE_ROWS, false>), dim3(persistent_grid(max_items)),
+                       dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 
 // dgrad: dx = dy W; A = dy [T,N] (n contiguous), B[j=k][p=n] = W[n][k] (k contiguous)
 hipError_t launch_dgrad_bf16(int G, int64_t K, int64_t N, int64_t T, const uint16_t *dy, const uint16_t *w,
-                             const uint16_t *const *w_ptrs, uint16_t *dx, const void *ws, hipStream_t s) {
+                             const uint16_t *const *w_ptrs, uint16_t *dx, int f16, const void *ws, hipStream_t s) {
   using namespace gemm;
   Params p{};
   p.A = dy; p.lda = N;
@@ -205,13 +215,18 @@ hipError_t launch_dgrad_bf16(int G, int64_t K, int64_t N, int64_t T, const uint1
   p.cols_j = K; p.P = N;
   p.tiles_j = (int)((K + kBN - 1) / kBN);
   const int64_t max_items = ((T + kBM - 1) / kBM + G) * p.tiles_j;
-  hipLaunchKernelGGL((gemm_bf16_kernel<true, false, MODE_ROWS>), dim3(persistent_grid(max_items)), dim3(kThreads), 0, s, p);
+  if (f16)
+    hipLaunchKernelGGL((gemm_bf16_kernel<true, false, MODE_ROWS, true>), dim3(persistent_grid(max_items)),
+                       dim3(kThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL((gemm_bf16_kernel<true, false, MODE_ROWS, false>), dim3(persistent_grid(max_items)),
+                       dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 
 // wgrad: dW_g[n][k] = sum_r dy[r][n] x[r][k]; A[i=n][p=r] (n contiguous), B[j=k][p=r] (k contiguous)
 hipError_t launch_wgrad_bf16(int G, int64_t K, int64_t N, int64_t T, const uint16_t *x, const uint16_t *dy,
-                             void *dw, void *const *dw_ptrs, int out_f32, int accumulate, const void *ws,
+                             void *dw, void *const *dw_ptrs, int out_f32, int accumulate, int f16, const void *ws,
                              hipStream_t s) {
   using namespace gemm;
   Params p{};
@@ -225,8 +240,12 @@ hipError_t launch_wgrad_bf16(int G, int64_t K, int64_t N, int64_t T, const uint1
   p.accumulate = accumulate;
   p.out_f32 = out_f32;
   const int64_t max_items = (int64_t)G * p.tiles_i * p.tiles_j;
-  hipLaunchKernelGGL((gemm_bf16_kernel<false, false, MODE_CONTR>), dim3(persistent_grid(max_items)), dim3(kThreads), 0, s,
-                     p);
+  if (f16)
+    hipLaunchKernelGGL((gemm_bf16_kernel<false, false, MODE_CONTR, true>), dim3(persistent_grid(max_items)),
+                       dim3(kThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL((gemm_bf16_kernel<false, false, MODE_CONTR, false>), dim3(persistent_grid(max_items)),
+                       dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 

@@ -183,7 +183,9 @@ __device__ __forceinline__ bf16x8_t frag_mnmaj(const char *st, int col0, int ks,
 }
 
 // Stores 4 consecutive output columns of one row: optional bias (per output
-// column), optional accumulate into the existing bf16 or fp32 values.
+// column, of the output's type), optional accumulate into the existing values.
+// 16-bit outputs are bf16, or fp16 when F16.
+template <bool F16>
 __device__ __forceinline__ void store4(char *cbase, int64_t row, int64_t ldc, int64_t col, const char *bias_g,
                                       int out_f32, int accumulate, float v0, float v1, float v2, float v3) {
   if (bias_g) {
@@ -192,8 +194,8 @@ __device__ __forceinline__ void store4(char *cbase, int64_t row, int64_t ldc, in
       v0 += bv.x; v1 += bv.y; v2 += bv.z; v3 += bv.w;
     } else {
       const uint2 bv = *(const uint2 *)(bias_g + col * 2);
-      v0 += bf16_to_f32(bv.x & 0xffff); v1 += bf16_to_f32(bv.x >> 16);
-      v2 += bf16_to_f32(bv.y & 0xffff); v3 += bf16_to_f32(bv.y >> 16);
+      v0 += h16_to_f32<F16>(bv.x & 0xffff); v1 += h16_to_f32<F16>(bv.x >> 16);
+      v2 += h16_to_f32<F16>(bv.y & 0xffff); v3 += h16_to_f32<F16>(bv.y >> 16);
     }
   }
   if (out_f32) {
@@ -207,10 +209,11 @@ __device__ __forceinline__ void store4(char *cbase, int64_t row, int64_t ldc, in
     uint2 *dst = (uint2 *)(cbase + (row * ldc + col) * 2);
     if (accumulate) {
       const uint2 o = *dst;
-      v0 += bf16_to_f32(o.x & 0xffff); v1 += bf16_to_f32(o.x >> 16);
-      v2 += bf16_to_f32(o.y & 0xffff); v3 += bf16_to_f32(o.y >> 16);
+      v0 += h16_to_f32<F16>(o.x & 0xffff); v1 += h16_to_f32<F16>(o.x >> 16);
+      v2 += h16_to_f32<F16>(o.y & 0xffff); v3 += h16_to_f32<F16>(o.y >> 16);
     }
-    *dst = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
+    *dst = make_uint2((uint32_t)f32_to_h16<F16>(v0) | ((uint32_t)f32_to_h16<F16>(v1) << 16),
+                      (uint32_t)f32_to_h16<F16>(v2) | ((uint32_t)f32_to_h16<F16>(v3) << 16));
   }
 }
 
@@ -291,7 +294,7 @@ __device__ __forceinline__ Tile decode_tile(const Params &p, const int64_t *__re
 // Stores a wave's 128 x 64 block of a tile: lane holds C[i][j..j+3] with
 // i = ii*32 + lane%32, j = jj*32 + q4*8 + (lane/32)*4 (operands were swapped in
 // the MFMAs for that); only rows < a_rv and columns < b_rv are written.
-template <int MODE>
+template <int MODE, bool F16 = false>
 __device__ __forceinline__ void store_tile(const Params &p, const Tile &t, const f32x16_t (&acc)[kNI][kNJ], int wm,
                                            int wn, int lane) {
   char *cbase;
@@ -317,7 +320,7 @@ __device__ __forceinline__ void store_tile(const Params &p, const Tile &t, const
       for (int q4 = 0; q4 < 4; ++q4) {
         const int jl = wn * kWTN + jj * 32 + q4 * 8 + (lane >> 5) * 4;
         if (jl >= t.b_rv) continue;
-        store4(cbase, row, p.ldc, (int64_t)t.jt * kBN + jl, bias_g, p.out_f32, p.accumulate, acc[ii][jj][q4 * 4 + 0],
+        store4<F16>(cbase, row, p.ldc, (int64_t)t.jt * kBN + jl, bias_g, p.out_f32, p.accumulate, acc[ii][jj][q4 * 4 + 0],
                acc[ii][jj][q4 * 4 + 1], acc[ii][jj][q4 * 4 + 2], acc[ii][jj][q4 * 4 + 3]);
       }
     }

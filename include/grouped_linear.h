@@ -53,7 +53,8 @@
 extern "C" {
 #endif
 
-/* Element types.  GL_F16 is accepted by the reference layer but not built here. */
+/* Element types.  GL_F16 goes wherever GL_BF16 does except the MXFP8 quantizers
+ * (whose source is bf16, as on the pages). */
 typedef enum gl_dtype { GL_F32 = 0, GL_BF16 = 1, GL_F16 = 2, GL_E4M3 = 3 } gl_dtype;
 
 enum {
@@ -61,7 +62,7 @@ enum {
   GL_ERR_ARG = -1,         /* bad size, NULL or misaligned pointer, both/neither weight forms */
   GL_ERR_DTYPE = -2,       /* element type not valid for this call */
   GL_ERR_SHAPE = -3,       /* output capacity < total_rows, K/N alignment, K % 32 for MXFP8 */
-  GL_ERR_UNSUPPORTED = -4, /* recognised but not built (fp16) */
+  GL_ERR_UNSUPPORTED = -4, /* reserved: recognised but not provided by this build */
   GL_ERR_HIP = -5          /* a HIP runtime call failed */
 };
 

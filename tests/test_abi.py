@@ -60,7 +60,7 @@ def fwd(G=4, K=64, N=32, T=32, ind=gl.GL_BF16, outd=gl.GL_BF16, x=FAKE, xs=None,
     (dict(w=None), -1), (dict(wp=FAKE), -1),        # neither / both weight forms
     (dict(b=FAKE, bp=FAKE), -1),
     (dict(x=FAKE + 8), -1),                         # misaligned
-    (dict(ind=gl.GL_F16, outd=gl.GL_F16), -4),      # fp16: recognised, not built
+    (dict(ind=gl.GL_F16, outd=gl.GL_BF16), -2),     # fp16 in, bf16 out
     (dict(ind=gl.GL_BF16, outd=gl.GL_F32), -2),
     (dict(ind=7, outd=7), -2),
     (dict(K=60), -3), (dict(N=36), -3),             # bf16 rows must be 16-byte multiples
@@ -82,7 +82,8 @@ def test_other_entry_points_reject():
     assert lib.gl_offsets(FAKE, 4, -1, FAKE, None) == -1
     assert lib.gl_offsets(FAKE, 4, 32, FAKE + 4, None) == -1
     assert lib.gl_dgrad(4, 64, 32, 32, gl.GL_BF16, FAKE, FAKE, None, FAKE2, 16, FAKE, None) == -3
-    assert lib.gl_dgrad(4, 64, 32, 32, gl.GL_F16, FAKE, FAKE, None, FAKE2, 32, FAKE, None) == -4
+    assert lib.gl_dgrad(4, 64, 32, 32, 7, FAKE, FAKE, None, FAKE2, 32, FAKE, None) == -2
+    assert lib.gl_wgrad(4, 64, 32, 32, gl.GL_F16, gl.GL_BF16, FAKE, FAKE, FAKE2, None, 0, FAKE, None) == -2
     assert lib.gl_wgrad(4, 64, 32, 32, gl.GL_F32, gl.GL_BF16, FAKE, FAKE, FAKE2, None, 0, FAKE, None) == -2
     assert lib.gl_wgrad(4, 64, 32, 32, gl.GL_BF16, gl.GL_F32, FAKE, FAKE, None, None, 0, FAKE, None) == -1
     assert lib.gl_wgrad(4, 64, 32, 32, gl.GL_BF16, gl.GL_F32, FAKE, FAKE, FAKE2, None, 2, FAKE, None) == -1
