@@ -312,6 +312,7 @@ int gl_group_quantize_mxfp8_colwise(const void *src, int64_t cols, int num_group
   if (G <= 0 || total_rows < 0 || cols <= 0)
     return fail(GL_ERR_ARG, "Invalid sizes (groups %d, rows %lld, cols %lld)", G, (long long)total_rows,
                 (long long)cols);
+  if (cols % 4) return fail(GL_ERR_SHAPE, "cols must be a multiple of 4 (got %lld)", (long long)cols);
   GL_TRY(check_colwise_ld(G, total_rows, ld));
   if (!workspace) return fail(GL_ERR_ARG, "workspace is NULL");
   if (total_rows == 0) return ok();
@@ -329,7 +330,9 @@ int gl_quantize_mxfp8_colwise_weights(const void *w, int num_groups, int64_t out
   if (G <= 0 || N <= 0 || K <= 0)
     return fail(GL_ERR_ARG, "Invalid sizes (groups %d, N %lld, K %lld)", G, (long long)N, (long long)K);
   if (N % 32) return fail(GL_ERR_SHAPE, "out_features must be a multiple of 32 (got %lld)", (long long)N);
+  if (K % 4) return fail(GL_ERR_SHAPE, "in_features must be a multiple of 4 (got %lld)", (long long)K);
   if (!w || !data_t || !scale_t) return fail(GL_ERR_ARG, "w, data_t or scale_t is NULL");
+  if ((uintptr_t)w & 7u) return fail(GL_ERR_ARG, "w must be 8-byte aligned");
   if (!aligned16(data_t)) return fail(GL_ERR_ARG, "data_t must be 16-byte aligned");
   return hip_result(gl::launch_quantize_mxfp8_colwise_weights((const uint16_t *)w, G, N, K, data_t, scale_t, stream),
                     "gl_quantize_mxfp8_colwise_weights");

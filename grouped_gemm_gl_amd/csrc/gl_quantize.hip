@@ -98,8 +98,9 @@ __global__ __launch_bounds__(kQThreads) void quantize_mxfp8_kernel(const uint16_
 }
 
 // Columnwise MXFP8 (blocks of 32 consecutive rows of a column), stored transposed:
-// thread t handles column c = t % cols of padded block b = t / cols.  Consecutive
-// threads take consecutive columns, so each row read is contiguous across a wave.
+// thread t handles the 4 adjacent columns 4 (t % (cols / 4)) .. + 3 of padded block
+// b = t / (cols / 4), reading 8 bytes per row, so a wave's row read covers 512
+// contiguous bytes.
 //   Group mode (ws != null): rows split by the workspace's offsets; group g's rows
 //   are padded to whole 128-row tiles and its blocks are numbered from 4 pre128[g],
 //   so padded block b lands at output column 32 b of row c of a [cols, ld] matrix.
@@ -109,12 +110,11 @@ __global__ __launch_bounds__(kQThreads) void quantize_mxfp8_kernel(const uint16_
 __global__ __launch_bounds__(kQThreads) void quantize_mxfp8_colwise_kernel(
     const uint16_t *__restrict__ src, int64_t cols, int64_t nblk, const void *ws, int G, int64_t total_rows,
     int64_t urows, uint8_t *__restrict__ data, uint8_t *__restrict__ scale, int64_t ld) {
+  const int64_t quads = cols / 4;
   const int64_t t = (int64_t)blockIdx.x * kQThreads + threadIdx.x;
-  const int64_t c = t % cols, b = t / cols;
+  const int64_t c4 = (t % quads) * 4, b = t / quads;
   if (b >= nblk) return;
-  int64_t r0, rend;
-  uint8_t *dst;
-  uint8_t *sdst;
+  int64_t r0, rend, out_base, out_ld, s_base, s_ld;
   if (ws) {
     const WsView v = ws_view(ws, G);
     if (!ws_usable(v.hdr, G, total_rows)) return;
@@ -128,28 +128,38 @@ __global__ __launch_bounds__(kQThreads) void quantize_mxfp8_colwise_kernel(
     const int g = lo;
     r0 = v.off[g] + (b - 4 * (int64_t)pre[g]) * 32;
     rend = v.off[g + 1];
-    dst = data + c * ld + b * 32;
-    sdst = scale + c * (ld / 32) + b;
+    out_base = b * 32;
+    out_ld = ld;
+    s_base = b;
+    s_ld = ld / 32;
   } else {
     const int64_t per = urows / 32, g = b / per, lb = b - g * per;
     r0 = g * urows + lb * 32;
     rend = r0 + 32;
-    dst = data + (g * cols + c) * urows + lb * 32;
-    sdst = scale + (g * cols + c) * per + lb;
+    out_base = g * cols * urows + lb * 32;
+    out_ld = urows;
+    s_base = g * cols * per + lb;
+    s_ld = per;
   }
-  uint32_t w[16];
+  uint32_t w[4][16];  // per column, 32 rows as 16 words of two packed bf16
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int64_t r = r0 + 2 * i;
-    const uint32_t lo16 = r < rend ? src[r * cols + c] : 0u;
-    const uint32_t hi16 = r + 1 < rend ? src[(r + 1) * cols + c] : 0u;
-    w[i] = lo16 | (hi16 << 16);
+    const uint2 lo = r < rend ? *(const uint2 *)(src + r * cols + c4) : make_uint2(0, 0);
+    const uint2 hi = r + 1 < rend ? *(const uint2 *)(src + (r + 1) * cols + c4) : make_uint2(0, 0);
+    w[0][i] = (lo.x & 0xffffu) | (hi.x << 16);
+    w[1][i] = (lo.x >> 16) | (hi.x & 0xffff0000u);
+    w[2][i] = (lo.y & 0xffffu) | (hi.y << 16);
+    w[3][i] = (lo.y >> 16) | (hi.y & 0xffff0000u);
   }
-  uint32_t out[8];
-  uint8_t sbyte;
-  quantize_block(w, out, sbyte);
-  store_block(dst, out);
-  *sdst = sbyte;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    uint32_t out[8];
+    uint8_t sbyte;
+    quantize_block(w[k], out, sbyte);
+    store_block(data + out_base + (c4 + k) * out_ld, out);
+    scale[s_base + (c4 + k) * s_ld] = sbyte;
+  }
 }
 
 hipError_t launch_quantize_mxfp8(const uint16_t *src, int64_t rows, int64_t cols, uint8_t *data, uint8_t *scale,
@@ -166,7 +176,7 @@ hipError_t launch_quantize_mxfp8(const uint16_t *src, int64_t rows, int64_t cols
 hipError_t launch_quantize_mxfp8_colwise(const uint16_t *src, int64_t cols, int G, int64_t total_rows,
                                          const void *ws, uint8_t *data, uint8_t *scale, int64_t ld, hipStream_t s) {
   const int64_t nblk = ld / 32;
-  const int64_t threads = nblk * cols;
+  const int64_t threads = nblk * (cols / 4);
   if (threads == 0) return hipSuccess;
   hipLaunchKernelGGL(quantize_mxfp8_colwise_kernel, dim3((unsigned)((threads + kQThreads - 1) / kQThreads)),
                      dim3(kQThreads), 0, s, src, cols, nblk, ws, G, total_rows, (int64_t)0, data, scale, ld);
@@ -178,7 +188,7 @@ hipError_t launch_quantize_mxfp8_colwise(const uint16_t *src, int64_t cols, int 
 hipError_t launch_quantize_mxfp8_colwise_weights(const uint16_t *w, int G, int64_t N, int64_t K, uint8_t *data,
                                                  uint8_t *scale, hipStream_t s) {
   const int64_t nblk = (int64_t)G * (N / 32);
-  const int64_t threads = nblk * K;
+  const int64_t threads = nblk * (K / 4);
   if (threads == 0) return hipSuccess;
   hipLaunchKernelGGL(quantize_mxfp8_colwise_kernel, dim3((unsigned)((threads + kQThreads - 1) / kQThreads)),
                      dim3(kQThreads), 0, s, w, K, nblk, (const void *)nullptr, G, (int64_t)0, N, data, scale, N);

@@ -203,8 +203,9 @@ int64_t gl_colwise_ld(int num_groups, int64_t total_rows);
  * Columnwise MXFP8 group quantization of bf16 activations src [total_rows, cols]
  * (x or dy) into the transposed layout above, with the groups of the workspace
  * written by gl_offsets.  ld: a multiple of 128, at least gl_colwise_ld and at most
- * 2^23.  Columns past the last group's padding are not written.  data_t 16-byte
- * aligned.  Split sizes found invalid by gl_offsets: nothing is written.
+ * 2^23; cols % 4 == 0.  Columns past the last group's padding are not written.
+ * src and data_t 16-byte aligned.  Split sizes found invalid by gl_offsets:
+ * nothing is written.
  */
 int gl_group_quantize_mxfp8_colwise(const void *src, int64_t cols, int num_groups, int64_t total_rows,
                                     const void *workspace, uint8_t *data_t, uint8_t *scale_t, int64_t ld,
@@ -212,7 +213,8 @@ int gl_group_quantize_mxfp8_colwise(const void *src, int64_t cols, int num_group
 
 /*
  * Columnwise MXFP8 of stacked bf16 weights w [G, N, K] (blocks of 32 along N, the
- * dgrad contraction) into codes [G, K, N] and scales [G, K, N / 32]; N % 32 == 0.
+ * dgrad contraction) into codes [G, K, N] and scales [G, K, N / 32]; N % 32 == 0,
+ * K % 4 == 0.
  */
 int gl_quantize_mxfp8_colwise_weights(const void *w, int num_groups, int64_t out_features, int64_t in_features,
                                       uint8_t *data_t, uint8_t *scale_t, hipStream_t stream);
