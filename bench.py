@@ -36,9 +36,9 @@ TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 # kernel-name fragment of each pass's GEMM (template arguments <A K-major, B K-major, mode, fp16>)
 PASS_KERNELS = {"forward": "gemm_bf16_kernel<true, true, 0, false>",
                 "dgrad": "gemm_bf16_kernel<true, false, 0, false>",
-                "wgrad": "gemm_bf16_kernel<false, false, 1, false>", "mx_forward": "gemm_mxfp8_kernel<0>"}
+                "wgrad": "gemm_bf16_kernel<false, false, 1, false>"}
 PASS_WORKLOAD = {"forward": "bf16_train_g8_k4096_n14336", "dgrad": "bf16_train_g8_k4096_n14336",
-                 "wgrad": "bf16_train_g8_k4096_n14336", "mx_forward": "mxfp8_fwd_g32_k4096_n4096"}
+                 "wgrad": "bf16_train_g8_k4096_n14336"}
 COPY_BYTES = 1 << 30
 
 
@@ -147,9 +147,10 @@ class EventTimer:
         return {k: sum(s.elapsed_time(e) for s, e in v) / len(v) for k, v in self.pairs.items()}
 
 
-def cpu_baseline(wl, m, x, w, b, dy, budget_s=15.0):
-    """The oracle, as it stands, on whole groups of the same workload until about
-    `budget_s` seconds of CPU work; TFLOP/s over the same 6*m_g*N*K flops."""
+def cpu_baseline(wl, m, x, w, b, dy, min_s=10.0):
+    """The oracle, as it stands, on whole groups of the same workload, cycling
+    through the groups until at least `min_s` seconds of CPU work; TFLOP/s over the
+    same 6*m_g*N*K flops."""
     import numpy as np
     import oracle
 
@@ -159,29 +160,30 @@ def cpu_baseline(wl, m, x, w, b, dy, budget_s=15.0):
     except Exception:  # pragma: no cover
         cores = os.cpu_count() or 1
     off = np.concatenate([[0], np.cumsum(m)])
-    done_flops, t_total, groups = 0.0, 0.0, []
-    for g in range(wl.G):
-        if m[g] == 0:
-            continue
-        lo, hi = int(off[g]), int(off[g + 1])
-        sub_m = [hi - lo]
-        xs = x[lo:hi].double().numpy()
-        dys = dy[lo:hi].double().numpy()
-        wg = w[g:g + 1].double().numpy()
-        bg = b[g:g + 1].double().numpy() if b is not None else None
-        t0 = time.perf_counter()
-        oracle.forward(xs, wg, bg, sub_m)
-        oracle.dgrad(dys, wg, sub_m)
-        oracle.wgrad(xs, dys, sub_m)
-        t_total += time.perf_counter() - t0
-        done_flops += 6.0 * (hi - lo) * wl.N * wl.K
-        groups.append(g)
-        if t_total >= budget_s:
-            break
+    done_flops, t_total, rows = 0.0, 0.0, 0
+    while t_total < min_s:
+        for g in range(wl.G):
+            if m[g] == 0:
+                continue
+            lo, hi = int(off[g]), int(off[g + 1])
+            sub_m = [hi - lo]
+            xs = x[lo:hi].double().numpy()
+            dys = dy[lo:hi].double().numpy()
+            wg = w[g:g + 1].double().numpy()
+            bg = b[g:g + 1].double().numpy() if b is not None else None
+            t0 = time.perf_counter()
+            oracle.forward(xs, wg, bg, sub_m)
+            oracle.dgrad(dys, wg, sub_m)
+            oracle.wgrad(xs, dys, sub_m)
+            t_total += time.perf_counter() - t0
+            done_flops += 6.0 * (hi - lo) * wl.N * wl.K
+            rows += hi - lo
+            if t_total >= min_s:
+                break
     return {"value": round(done_flops / t_total / 1e12, 4), "unit": "TFLOP/s", "cores": int(cores),
             "kind": "oracle",
-            "sample": f"oracle fp64 forward+dgrad+wgrad of groups {groups} ({sum(m[g] for g in groups)} of "
-                      f"{wl.T} rows) of the same workload, {t_total:.1f} s"}
+            "sample": f"oracle fp64 forward+dgrad+wgrad, group by group, over {rows} rows of the same workload "
+                      f"({rows / wl.T:.2f}x its {wl.T} rows), {t_total:.1f} s"}
 
 
 def bench_bf16(torch, gl, synth, steps, warmup):
@@ -305,7 +307,6 @@ def bench_mxfp8(torch, gl, synth, steps, warmup):
         out[f"{k}_ms"] = round(per[k], 4)
         out[f"{k}_tflops"] = tf(k)
         out[f"{k}_pct_fp8_peak"] = round(100 * tf(k) / PEAK_FP8_TFLOPS, 2)
-    out["mx_forward_traffic"] = traffic_for("mx_forward", wl.name)
     out["quantize_gbs"] = {"x": gbs("quantize_x", row_bytes(T, K)), "w": gbs("quantize_w", row_bytes(G * N, K)),
                            "dy": gbs("quantize_dy", row_bytes(T, N)),
                            "x_colwise": gbs("quantize_x_colwise", col_bytes(T, K)),
