@@ -12,6 +12,9 @@ namespace gl {
 //   [32]  int64 offsets[G+1]
 //   then  int32 row-tile prefix tables, one per row-tile height in kTileRows:
 //         pre[g] = sum_{h<g} ceil(m_h / rows), pre[G] = total row tiles.
+//   then  (1 KiB aligned) the split-contraction area of the GEMMs: int32 arrival
+//         counters[kSplitSlots] (zeroed by the offsets kernel, left zero by every
+//         GEMM launch), then kSplitSlots fp32 partial tiles of kPartialBytes each.
 struct WsHeader {
   int32_t status;      // GL_STATUS_* bits, 0 = valid splits
   int32_t num_groups;
@@ -33,15 +36,23 @@ __host__ __device__ inline size_t ws_prefix_byte(int G, int idx) {
   size_t base = 32 + 8 * (size_t)(G + 1);
   return base + (size_t)idx * 4 * (size_t)(G + 1);
 }
+// A GEMM launch splits at most kSplitSlots tile parts over the contraction; each
+// part leaves one 256 x 256 fp32 partial tile.
+constexpr int kSplitSlots = 256;
+constexpr size_t kPartialBytes = 256 * 256 * 4;
+__host__ __device__ inline size_t ws_split_byte(int G) {
+  return (ws_prefix_byte(G, kNumTileRows) + 1023) & ~(size_t)1023;
+}
 __host__ __device__ inline size_t ws_bytes(int G) {
-  size_t b = ws_prefix_byte(G, kNumTileRows);
-  return (b + 255) & ~(size_t)255;
+  return ws_split_byte(G) + 4 * kSplitSlots + (size_t)kSplitSlots * kPartialBytes;
 }
 
 struct WsView {
   WsHeader *hdr;
   const int64_t *off;
   const int32_t *pre[kNumTileRows];
+  int32_t *split_cnt;   // [kSplitSlots]
+  float *split_part;    // [kSplitSlots][kPartialBytes / 4]
 };
 __host__ __device__ inline WsView ws_view(const void *ws, int G) {
   WsView v;
@@ -49,6 +60,8 @@ __host__ __device__ inline WsView ws_view(const void *ws, int G) {
   v.hdr = (WsHeader *)b;
   v.off = (const int64_t *)(b + ws_offsets_byte(G));
   for (int i = 0; i < kNumTileRows; ++i) v.pre[i] = (const int32_t *)(b + ws_prefix_byte(G, i));
+  v.split_cnt = (int32_t *)(b + ws_split_byte(G));
+  v.split_part = (float *)(b + ws_split_byte(G) + 4 * kSplitSlots);
   return v;
 }
 

@@ -68,13 +68,21 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
   const int wm = wave / kWN, wn = wave % kWN;
   const int grid = gridDim.x, b = blockIdx.x;
   const int first = (grid & 7) == 0 ? (b & 7) * (grid >> 3) + (b >> 3) : b;
+  const int nk_rows = (int)((p.P + kBK - 1) / kBK);  // row mode: the same for every tile
 
-  for (int w = first; w < total; w += grid) {
-    const Tile t = decode_tile<A_KMAJ, B_KMAJ, MODE>(p, off, pre, w);
-    if (MODE == MODE_CONTR && p.accumulate && t.g_rows == 0) continue;  // main_grad untouched
+  // One work item: the whole contraction of a tile, or (SPLIT) part `part` of S of
+  // the u-th split tile.
+  auto item = [&](int tile, int part, int S, int u, auto split_tag) __attribute__((always_inline)) {
+    constexpr bool SPLIT = decltype(split_tag)::value;
+    const Tile t = decode_tile<A_KMAJ, B_KMAJ, MODE>(p, off, pre, tile);
+    if (MODE == MODE_CONTR && p.accumulate && t.g_rows == 0) return;  // main_grad untouched
     const int64_t pmax = t.pmax;
     const int nk = (int)((pmax + kBK - 1) / kBK);
     const int nfull = (int)(pmax / kBK);  // stages [0, nfull) are complete; nk - nfull <= 1
+    // this item's stages [kbeg, kend)
+    const int kbeg = SPLIT ? part * nk / S : 0;
+    const int kend = SPLIT ? (part + 1) * nk / S : nk;
+    const int kfull = SPLIT ? (nfull < kend ? nfull : kend) : nfull;
 
     Stream<A_KMAJ> sa;
     Stream<B_KMAJ> sb;
@@ -124,12 +132,13 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
     };
 
     bf16x8_t fa[2][kNI], fb[2][kNJ];
-    // prologue: stages 0 .. kS-2 in flight, stage 0 visible, step 0 fragments read
-    for (int s = 0; s < kS - 1 && s < nk; ++s) issue(s);
-    if (nk > 0) {
+    // prologue: stages kbeg .. kbeg+kS-2 in flight, stage kbeg visible, its step 0
+    // fragments read
+    for (int s = kbeg; s < kbeg + kS - 1 && s < kend; ++s) issue(s);
+    if (kend > kbeg) {
       wait_vm0();
       __builtin_amdgcn_s_barrier();
-      load_frags(0, 0, fa[0], fb[0]);
+      load_frags(kbeg, 0, fa[0], fb[0]);
     }
     // One stage per iteration; fragment set (ks & 1) feeds MFMA step ks while set
     // (ks + 1) & 1 is refilled.  The barrier before the last step makes stage kt + 1
@@ -144,7 +153,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
         char *st = stage_ptr(kt + kS - 1);
         sa.issue_full(kt + kS - 1, st, wave);
         sb.issue_full(kt + kS - 1, st + kOpBytes, wave);
-      } else if (kt + kS - 1 < nk) {
+      } else if (kt + kS - 1 < kend) {
         issue(kt + kS - 1);
       }
       fence();
@@ -163,19 +172,40 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
         wait_vm0();
       wait_lgkm0();
       __builtin_amdgcn_s_barrier();
-      if (steady || kt + 1 < nk) load_frags(kt + 1, 0, fa[0], fb[0]);
+      if (steady || kt + 1 < kend) load_frags(kt + 1, 0, fa[0], fb[0]);
       fence();
       mfmas(fa[(kKS - 1) & 1], fb[(kKS - 1) & 1]);
       fence();
     };
 
-    int kt = 0;
-    for (; kt + kS - 1 < nfull; ++kt) body(kt, true);  // every stage issued here is complete
-    for (; kt < nk; ++kt) body(kt, false);
+    int kt = kbeg;
+    for (; kt + kS - 1 < kfull; ++kt) body(kt, true);  // every stage issued here is complete
+    for (; kt < kend; ++kt) body(kt, false);
     __builtin_amdgcn_s_barrier();  // every wave is done with the ring before it is refilled
 
+    if constexpr (SPLIT) {
+      // the ring is idle after the loop's last barrier: its first word carries the flag
+      if (!split_finish(ws, u, part, S, acc, (int *)lds)) return;
+    }
     store_tile<MODE, F16>(p, t, acc, wm, wn, lane);
+  };
+
+  // whole tiles, round after round; in row mode the last round may be split
+#ifndef GL_NOSPLIT
+  const int full = MODE == MODE_ROWS ? split_plan(total, grid, nk_rows).full : total;
+#else
+  const int full = total;
+#endif
+  for (int w = first; w < full; w += grid) item(w, 0, 1, 0, std::false_type{});
+#ifndef GL_NOSPLIT
+  if constexpr (MODE == MODE_ROWS) {
+    const int tiles = pre[p.G] * p.tiles_j;
+    const SplitPlan sp = split_plan(tiles, grid, nk_rows);
+    // the parts of the last round: u = first, consecutive u are consecutive tiles
+    if (first < sp.rem * sp.S)
+      item(sp.full + first % sp.rem, first / sp.rem, sp.S, first % sp.rem, std::true_type{});
   }
+#endif
 }
 
 }  // namespace gemm

@@ -4,6 +4,8 @@
 // the pieces fit together.
 #pragma once
 
+#include <type_traits>
+
 #include "gl_common.hpp"
 
 namespace gl {
@@ -289,6 +291,93 @@ __device__ __forceinline__ Tile decode_tile(const Params &p, const int64_t *__re
     t.pmax = (int64_t)(cpre[t.g + 1] - cpre[t.g]) * kKcontrUnits;
   }
   return t;
+}
+
+// ------------------------------------------------------------- split tail --
+// A launch's tiles go round the persistent grid.  When the last round would leave
+// at least half the CUs idle (rem = tiles % grid <= grid / 2), each of those rem
+// tiles is cut into S = grid / rem contraction ranges instead (at most kSplitSlots
+// parts in all, each at least kMinSplitStages stages long), and the parts fill the
+// last round.  Every part writes its fp32 accumulators to a partial slot of the
+// workspace and counts itself in; the part that arrives last adds the S partials
+// in part order -- a fixed order, so the result does not depend on which part
+// finishes last -- and stores the tile.  No workgroup ever waits for another.
+constexpr int kMinSplitStages = 4;
+
+struct SplitPlan {
+  int full;   // items [0, full) are whole tiles
+  int rem;    // tiles [full, full + rem) are split
+  int S;      // parts per split tile (1: nothing is split)
+  int items;  // full + rem * S
+};
+
+// nk: contraction stages of every tile (the same for all tiles of a row-mode launch)
+__device__ __forceinline__ SplitPlan split_plan(int tiles, int grid, int nk) {
+  SplitPlan sp{tiles, 0, 1, tiles};
+  const int rem = tiles % grid;
+  if (rem == 0) return sp;
+  int S = grid / rem;
+  if (S * rem > kSplitSlots) S = kSplitSlots / rem;
+  if (S > nk / kMinSplitStages) S = nk / kMinSplitStages;
+  if (S < 2) return sp;
+  sp.full = tiles - rem;
+  sp.rem = rem;
+  sp.S = S;
+  sp.items = sp.full + rem * S;
+  return sp;
+}
+
+// Part `part` of S of the u-th split tile is done: publish its partial; true when
+// this workgroup arrived last and acc now holds the sum of all parts.  Called by
+// the whole workgroup, as its last work item; `flag` is a workgroup-shared int.
+// (The flag lives inside the kernel's one LDS array: a second __shared__ object
+// makes the compiler wait for every direct-to-LDS load before each LDS read.)  The parts of the last
+// round are items u + rem * part, so a part's CUs on one XCD run neighbouring tiles.
+__device__ __forceinline__ bool split_finish(const WsView &ws, int u, int part, int S, f32x16_t (&acc)[kNI][kNJ],
+                                             int *flag) {
+  const int tid = threadIdx.x;
+  constexpr size_t kSlotF4 = kPartialBytes / 16;
+  float4 *slots = (float4 *)ws.split_part + (size_t)u * S * kSlotF4;
+  float4 *mine = slots + (size_t)part * kSlotF4;
+#pragma unroll
+  for (int ii = 0; ii < kNI; ++ii)
+#pragma unroll
+    for (int jj = 0; jj < kNJ; ++jj)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        mine[((ii * kNJ + jj) * 4 + c) * kThreads + tid] =
+            make_float4(acc[ii][jj][4 * c], acc[ii][jj][4 * c + 1], acc[ii][jj][4 * c + 2], acc[ii][jj][4 * c + 3]);
+  __threadfence();  // release: the partial is visible device-wide before the count
+  __syncthreads();
+  if (tid == 0) {
+    const int old = __hip_atomic_fetch_add(ws.split_cnt + u, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    const int last = old == S - 1;
+    if (last) __hip_atomic_store(ws.split_cnt + u, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *flag = last;
+  }
+  __syncthreads();
+  // the same value in every lane; read as wave-uniform so control flow stays uniform
+  if (!__builtin_amdgcn_readfirstlane(*flag)) return false;
+  __threadfence();  // acquire: every part's partial
+  for (int s = 0; s < S; ++s) {
+    const float4 *src = slots + (size_t)s * kSlotF4;
+#pragma unroll
+    for (int ii = 0; ii < kNI; ++ii)
+#pragma unroll
+      for (int jj = 0; jj < kNJ; ++jj)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const float4 o = src[((ii * kNJ + jj) * 4 + c) * kThreads + tid];
+          if (s == 0) {
+            acc[ii][jj][4 * c] = o.x; acc[ii][jj][4 * c + 1] = o.y;
+            acc[ii][jj][4 * c + 2] = o.z; acc[ii][jj][4 * c + 3] = o.w;
+          } else {
+            acc[ii][jj][4 * c] += o.x; acc[ii][jj][4 * c + 1] += o.y;
+            acc[ii][jj][4 * c + 2] += o.z; acc[ii][jj][4 * c + 3] += o.w;
+          }
+        }
+  }
+  return true;
 }
 
 // Stores a wave's 128 x 64 block of a tile: lane holds C[i][j..j+3] with

@@ -37,6 +37,7 @@ __global__ __launch_bounds__(kScanThreads) void offsets_kernel(const int64_t *__
   __shared__ int s_bad;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (tid == 0) s_bad = 0;
+  for (int i = tid; i < kSplitSlots; i += kScanThreads) v.split_cnt[i] = 0;
   __syncthreads();
 
   int64_t carry = 0;

@@ -73,7 +73,16 @@ enum {
   GL_STATUS_WORKSPACE = 4       /* a later call named a workspace built for other G / T */
 };
 
-/* Bytes of device workspace a call sequence over num_groups groups needs (>= 256). */
+/*
+ * Bytes of device workspace a call sequence over num_groups groups needs: the
+ * offsets, the per-group row-tile tables and the status word (a few KiB), plus a
+ * fixed area of 256 fp32 partial tiles of 256 x 256 and their arrival counters
+ * (64 MiB + 1 KiB) where a GEMM launch whose last round of tiles would leave most
+ * CUs idle splits those tiles over the contraction.  The split result is the same
+ * on every run (partials are added in a fixed order).  One workspace serves one
+ * call sequence at a time: calls that use the same workspace must not overlap
+ * (same stream, or ordered by events).
+ */
 size_t gl_workspace_size(int num_groups);
 
 /*
