@@ -258,9 +258,10 @@ def bench_bf16(torch, gl, synth, steps, warmup):
 
 def bench_mxfp8(torch, gl, synth, steps, warmup):
     """MXFP8 forward and backward on the MXFP8 workload (G=32, K=N=4096, 32768 rows).
-    Weights are quantized once (rowwise for the forward, columnwise for dgrad), as a
-    cached quantized-weight workspace; activations and grad outputs are quantized
-    inside each timed pass."""
+    Weights are quantized once (rowwise for the forward, columnwise for dgrad) into a
+    cached workspace, whose refresh call runs in every step with its no-op flag set;
+    activations and grad outputs are quantized inside each timed pass, x together
+    with the split-offset scan in one launch."""
     wl = synth.WORKLOADS["mxfp8_fwd_g32_k4096_n4096"]
     dev = torch.device("cuda")
     t0 = time.time()
@@ -269,7 +270,10 @@ def bench_mxfp8(torch, gl, synth, steps, warmup):
     log(f"mxfp8 inputs generated in {time.time() - t0:.1f}s")
     G, K, N, T = wl.G, wl.K, wl.N, wl.T
     ws = gl.new_workspace(G, dev)
-    gl.gl_offsets(torch.from_numpy(m).to(dev), T, ws)
+    md = torch.from_numpy(m).to(dev)
+    gl.gl_offsets(md, T, ws)
+    noop_set = torch.ones(1, dtype=torch.int32, device=dev)
+    noop_clear = torch.zeros(1, dtype=torch.int32, device=dev)
     u8 = dict(dtype=torch.uint8, device=dev)
     xq, xs = torch.empty(T, K, **u8), torch.empty(T, K // 32, **u8)
     wq, wsc = torch.empty(G, N, K, **u8), torch.empty(G, N, K // 32, **u8)
@@ -281,20 +285,24 @@ def bench_mxfp8(torch, gl, synth, steps, warmup):
     y = torch.empty(T, N, dtype=torch.bfloat16, device=dev)
     dx = torch.empty(T, K, dtype=torch.bfloat16, device=dev)
     dw = torch.empty(G, N, K, dtype=torch.bfloat16, device=dev)
-    gl.gl_group_quantize_mxfp8(w, wq, wsc)              # cached quantized weights
-    gl.gl_quantize_mxfp8_colwise_weights(w, wtq, wts)
+    gl.gl_quantize_mxfp8_weights(w, wq, wsc, wtq, wts)   # cached quantized weights
     timer = EventTimer(torch)
     for i in range(warmup + steps):
         t = timer if i >= warmup else None
         run = (lambda n, f: t.run(n, f)) if t else (lambda n, f: f())
-        run("quantize_x", lambda: gl.gl_group_quantize_mxfp8(x, xq, xs))
+        # the step, in training order
+        run("offsets_quantize_x", lambda: gl.gl_offsets_quantize_mxfp8(md, x, ws, xq, xs))
         run("quantize_x_colwise", lambda: gl.gl_group_quantize_mxfp8_colwise(x, xtq, xts, ws, G))
-        run("quantize_w", lambda: gl.gl_group_quantize_mxfp8(w, wq, wsc))
+        run("weights_noop", lambda: gl.gl_quantize_mxfp8_weights(w, wq, wsc, wtq, wts, noop_flag=noop_set))
         run("mx_forward", lambda: gl.gl_forward(xq, wq, y, ws, x_scale=xs, w_scale=wsc))
         run("quantize_dy", lambda: gl.gl_group_quantize_mxfp8(dy, dq, ds))
         run("quantize_dy_colwise", lambda: gl.gl_group_quantize_mxfp8_colwise(dy, dytq, dyts, ws, G))
         run("mx_dgrad", lambda: gl.gl_dgrad_mxfp8(dq, ds, wtq, wts, dx, ws))
         run("mx_wgrad", lambda: gl.gl_wgrad_mxfp8(dytq, dyts, xtq, xts, dw, ws, T))
+        # quantizers on their own, each on an input no pass just read (no cache warmth)
+        run("quantize_w", lambda: gl.gl_group_quantize_mxfp8(w, wq, wsc))
+        run("quantize_x", lambda: gl.gl_group_quantize_mxfp8(x, xq, xs))
+        run("weights_refresh", lambda: gl.gl_quantize_mxfp8_weights(w, wq, wsc, wtq, wts, noop_flag=noop_clear))
     torch.cuda.synchronize()
     per = timer.mean_ms()
     flops = 2.0 * T * N * K
@@ -310,12 +318,19 @@ def bench_mxfp8(torch, gl, synth, steps, warmup):
     out["quantize_gbs"] = {"x": gbs("quantize_x", row_bytes(T, K)), "w": gbs("quantize_w", row_bytes(G * N, K)),
                            "dy": gbs("quantize_dy", row_bytes(T, N)),
                            "x_colwise": gbs("quantize_x_colwise", col_bytes(T, K)),
-                           "dy_colwise": gbs("quantize_dy_colwise", col_bytes(T, N))}
-    step_ms = sum(per[k] for k in per if k != "quantize_w")
+                           "dy_colwise": gbs("quantize_dy_colwise", col_bytes(T, N)),
+                           "offsets_and_x": gbs("offsets_quantize_x", row_bytes(T, K)),
+                           "w_rowwise_and_colwise": gbs("weights_refresh", G * N * K * (2 + 2 * (1 + 1 / 32)))}
+    out["launch_us"] = {"offsets_quantize_x": round(per["offsets_quantize_x"] * 1e3, 1),
+                        "quantize_x": round(per["quantize_x"] * 1e3, 1),
+                        "weights_with_noop_flag_set": round(per["weights_noop"] * 1e3, 1)}
+    step = ("offsets_quantize_x", "quantize_x_colwise", "weights_noop", "mx_forward", "quantize_dy",
+            "quantize_dy_colwise", "mx_dgrad", "mx_wgrad")
+    step_ms = sum(per[k] for k in step)
     out["mx_step_ms"] = round(step_ms, 4)
     out["mx_step_tflops"] = round(3 * flops / (step_ms * 1e-3) / 1e12, 2)
-    out["mx_step"] = ("quantize x (rowwise, columnwise), MX forward, quantize dy (rowwise, columnwise), "
-                      "MX dgrad, MX wgrad; weights quantized once")
+    out["mx_step"] = ("offsets + quantize x (one launch), quantize x columnwise, cached-weight refresh skipped "
+                      "by its no-op flag, MX forward, quantize dy (rowwise, columnwise), MX dgrad, MX wgrad")
     return out
 
 

@@ -66,6 +66,8 @@ def load():
         "gl_colwise_ld": (I64, [I, I64]),
         "gl_group_quantize_mxfp8_colwise": (I, [P, I64, I, I64, P, P, P, I64, P]),
         "gl_quantize_mxfp8_colwise_weights": (I, [P, I, I64, I64, P, P, P]),
+        "gl_offsets_quantize_mxfp8": (I, [P, I, I64, P, P, I64, P, P, P]),
+        "gl_quantize_mxfp8_weights": (I, [P, I, I64, I64, P, P, P, P, P, P]),
         "gl_dgrad_mxfp8": (I, [I, I64, I64, I64, I, P, P, P, P, P, I64, P, P]),
         "gl_wgrad_mxfp8": (I, [I, I64, I64, I64, I, P, P, P, P, I64, P, P, I, P, P]),
         "gl_last_error": (ctypes.c_char_p, []),
@@ -270,6 +272,41 @@ def gl_quantize_mxfp8_colwise_weights(w: Tensor, data_t: Tensor, scale_t: Tensor
         raise ValueError("w must be bf16 [G, N, K], data_t [G, K, N] and scale_t [G, K, N/32]")
     _check(load().gl_quantize_mxfp8_colwise_weights(_ptr(w), G, N, K, _ptr(data_t), _ptr(scale_t), _stream(stream)))
     return data_t, scale_t
+
+
+def gl_offsets_quantize_mxfp8(m_splits: Tensor, x: Tensor, workspace: Tensor, data: Tensor, scale: Tensor,
+                              stream=None):
+    """One launch: the split-offset scan into ``workspace`` and rowwise MXFP8 of the
+    bf16 activations x [T, K] into data [T, K] / scale [T, K/32]."""
+    if m_splits.dtype != torch.int64:
+        raise ValueError("m_splits must be int64")
+    T, K = x.shape
+    if x.dtype != torch.bfloat16 or data.shape != (T, K) or scale.shape != (T, K // 32):
+        raise ValueError("x must be bf16 [T, K], data [T, K] and scale [T, K/32]")
+    _check(load().gl_offsets_quantize_mxfp8(_ptr(m_splits), m_splits.numel(), T, _ptr(workspace), _ptr(x), K,
+                                            _ptr(data), _ptr(scale), _stream(stream)))
+    return data, scale
+
+
+def gl_quantize_mxfp8_weights(w: Tensor, data: Tensor, scale: Tensor, data_t: Tensor = None, scale_t: Tensor = None,
+                              noop_flag: Tensor = None, stream=None):
+    """The weights' MXFP8 workspace in one launch: rowwise data [G, N, K] / scale
+    [G, N, K/32] and, if given, columnwise data_t [G, K, N] / scale_t [G, K, N/32].
+    ``noop_flag`` (device int32, one element): nonzero at run time skips the work."""
+    G, N, K = w.shape
+    if w.dtype != torch.bfloat16 or data.shape != (G, N, K) or scale.shape != (G, N, K // 32):
+        raise ValueError("w must be bf16 [G, N, K], data [G, N, K] and scale [G, N, K/32]")
+    if (data_t is None) != (scale_t is None):
+        raise ValueError("give both data_t and scale_t, or neither")
+    if data_t is not None and (data_t.shape != (G, K, N) or scale_t.shape != (G, K, N // 32)):
+        raise ValueError("data_t must be [G, K, N] and scale_t [G, K, N/32]")
+    if noop_flag is not None and (noop_flag.dtype != torch.int32 or noop_flag.numel() != 1):
+        raise ValueError("noop_flag must be a one-element int32 tensor")
+    _check(load().gl_quantize_mxfp8_weights(_ptr(w), G, N, K, _ptr(data), _ptr(scale),
+                                            _ptr(data_t) if data_t is not None else None,
+                                            _ptr(scale_t) if scale_t is not None else None,
+                                            _ptr(noop_flag) if noop_flag is not None else None, _stream(stream)))
+    return data, scale
 
 
 def gl_dgrad_mxfp8(dy: Tensor, dy_scale: Tensor, w_t: Tensor, w_t_scale: Tensor, dx: Tensor, workspace: Tensor,

@@ -43,6 +43,12 @@ hipError_t launch_quantize_mxfp8_colwise(const uint16_t *src, int64_t cols, int 
                                          const void *ws, uint8_t *data, uint8_t *scale, int64_t ld, hipStream_t s);
 hipError_t launch_quantize_mxfp8_colwise_weights(const uint16_t *w, int G, int64_t N, int64_t K, uint8_t *data,
                                                  uint8_t *scale, hipStream_t s);
+hipError_t launch_offsets_quantize_mxfp8(const int64_t *m_splits, int G, int64_t total_rows, void *ws,
+                                         const uint16_t *src, int64_t cols, uint8_t *data, uint8_t *scale,
+                                         hipStream_t s);
+hipError_t launch_quantize_mxfp8_weights(const uint16_t *w, int G, int64_t N, int64_t K, uint8_t *data,
+                                         uint8_t *scale, uint8_t *data_t, uint8_t *scale_t, const int32_t *noop,
+                                         hipStream_t s);
 hipError_t launch_wgrad_mxfp8(int G, int64_t K, int64_t N, int64_t T, const uint8_t *dyt, const uint8_t *dyt_s,
                               const uint8_t *xt, const uint8_t *xt_s, int64_t ld, void *dw, void *const *dw_ptrs,
                               int out_f32, int accumulate, const void *ws, hipStream_t s);
@@ -321,6 +327,48 @@ int gl_group_quantize_mxfp8_colwise(const void *src, int64_t cols, int num_group
   return hip_result(gl::launch_quantize_mxfp8_colwise((const uint16_t *)src, cols, G, total_rows, workspace, data_t,
                                                       scale_t, ld, stream),
                     "gl_group_quantize_mxfp8_colwise");
+}
+
+int gl_offsets_quantize_mxfp8(const int64_t *m_splits, int num_groups, int64_t total_rows, void *workspace,
+                              const void *x, int64_t in_features, uint8_t *x_data, uint8_t *x_scale,
+                              hipStream_t stream) {
+  const int64_t K = in_features;
+  if (num_groups <= 0) return fail(GL_ERR_ARG, "Invalid number of groups (%d)", num_groups);
+  if (total_rows < 0 || K <= 0)
+    return fail(GL_ERR_ARG, "Invalid shape (%lld, %lld)", (long long)total_rows, (long long)K);
+  if (K % 32) return fail(GL_ERR_SHAPE, "in_features must be a multiple of 32 (got %lld)", (long long)K);
+  if (total_rows * (K / 32) / 256 >= ((int64_t)1 << 31))
+    return fail(GL_ERR_SHAPE, "x too large for one launch (%lld x %lld)", (long long)total_rows, (long long)K);
+  if (!m_splits || ((uintptr_t)m_splits & 7u)) return fail(GL_ERR_ARG, "m_splits NULL or not 8-byte aligned");
+  if (!workspace || !aligned16(workspace)) return fail(GL_ERR_ARG, "workspace NULL or not 16-byte aligned");
+  if (total_rows > 0) {
+    if (!x || !x_data || !x_scale) return fail(GL_ERR_ARG, "x, x_data or x_scale is NULL");
+    if (!aligned16(x) || !aligned16(x_data)) return fail(GL_ERR_ARG, "x and x_data must be 16-byte aligned");
+  }
+  return hip_result(gl::launch_offsets_quantize_mxfp8(m_splits, num_groups, total_rows, workspace,
+                                                      (const uint16_t *)x, K, x_data, x_scale, stream),
+                    "gl_offsets_quantize_mxfp8");
+}
+
+int gl_quantize_mxfp8_weights(const void *w, int num_groups, int64_t out_features, int64_t in_features,
+                              uint8_t *data, uint8_t *scale, uint8_t *data_t, uint8_t *scale_t,
+                              const int32_t *noop_flag, hipStream_t stream) {
+  const int G = num_groups;
+  const int64_t N = out_features, K = in_features;
+  if (G <= 0 || N <= 0 || K <= 0)
+    return fail(GL_ERR_ARG, "Invalid sizes (groups %d, N %lld, K %lld)", G, (long long)N, (long long)K);
+  if (K % 32) return fail(GL_ERR_SHAPE, "in_features must be a multiple of 32 (got %lld)", (long long)K);
+  if (!w || !data || !scale) return fail(GL_ERR_ARG, "w, data or scale is NULL");
+  if (!aligned16(w) || !aligned16(data)) return fail(GL_ERR_ARG, "w and data must be 16-byte aligned");
+  if ((data_t == nullptr) != (scale_t == nullptr)) return fail(GL_ERR_ARG, "give both data_t and scale_t, or neither");
+  if (data_t) {
+    if (N % 32) return fail(GL_ERR_SHAPE, "columnwise codes need out_features %% 32 == 0 (got %lld)", (long long)N);
+    if (!aligned16(data_t)) return fail(GL_ERR_ARG, "data_t must be 16-byte aligned");
+  }
+  if (noop_flag && ((uintptr_t)noop_flag & 3u)) return fail(GL_ERR_ARG, "noop_flag must be 4-byte aligned");
+  return hip_result(gl::launch_quantize_mxfp8_weights((const uint16_t *)w, G, N, K, data, scale, data_t, scale_t,
+                                                      noop_flag, stream),
+                    "gl_quantize_mxfp8_weights");
 }
 
 int gl_quantize_mxfp8_colwise_weights(const void *w, int num_groups, int64_t out_features, int64_t in_features,

@@ -10,7 +10,7 @@
 // 448.  HBM-bound: each thread owns one 32-element block (64 bytes in, 32 + 1 out),
 // so a wave streams 4 KiB of contiguous input.  Everything is exact integer /
 // power-of-two arithmetic, bit-identical to the rule.
-#include "gl_common.hpp"
+#include "gl_offsets.hpp"
 
 namespace gl {
 
@@ -80,12 +80,10 @@ __device__ __forceinline__ void store_block(uint8_t *dst, const uint32_t *out) {
   d[1] = make_uint4(out[4], out[5], out[6], out[7]);
 }
 
-__global__ __launch_bounds__(kQThreads) void quantize_mxfp8_kernel(const uint16_t *__restrict__ src,
-                                                                   int64_t nblocks, uint8_t *__restrict__ data,
-                                                                   uint8_t *__restrict__ scale) {
-  const int64_t b = (int64_t)blockIdx.x * kQThreads + threadIdx.x;
-  if (b >= nblocks) return;
-  // blocks are numbered row-major, so block b covers elements [32 b, 32 b + 32)
+// Rowwise block b (blocks are numbered row-major, so block b covers elements
+// [32 b, 32 b + 32) of the matrix).
+__device__ __forceinline__ void quantize_row_block(const uint16_t *__restrict__ src, int64_t b,
+                                                   uint8_t *__restrict__ data, uint8_t *__restrict__ scale) {
   const uint4 *in = (const uint4 *)(src + b * 32);
   uint4 v[4];
 #pragma unroll
@@ -95,6 +93,29 @@ __global__ __launch_bounds__(kQThreads) void quantize_mxfp8_kernel(const uint16_
   quantize_block((const uint32_t *)v, out, sbyte);
   store_block(data + b * 32, out);
   scale[b] = sbyte;
+}
+
+__global__ __launch_bounds__(kQThreads) void quantize_mxfp8_kernel(const uint16_t *__restrict__ src,
+                                                                   int64_t nblocks, uint8_t *__restrict__ data,
+                                                                   uint8_t *__restrict__ scale) {
+  const int64_t b = (int64_t)blockIdx.x * kQThreads + threadIdx.x;
+  if (b < nblocks) quantize_row_block(src, b, data, scale);
+}
+
+// Fused split-offset scan and rowwise activation quantization, one launch of
+// kQThreads-thread workgroups: the first wave of workgroup 0 runs the scan (the
+// quantization does not depend on the splits), every thread of the other
+// workgroups quantizes one block.  The kernel uses no LDS (an LDS allocation per
+// workgroup slows the dispatch of these short workgroups).
+__global__ __launch_bounds__(kQThreads) void offsets_quantize_mxfp8_kernel(
+    const int64_t *__restrict__ m_splits, int G, int64_t total_rows, void *ws, const uint16_t *__restrict__ src,
+    int64_t nblocks, uint8_t *__restrict__ data, uint8_t *__restrict__ scale) {
+  if (blockIdx.x == 0) {
+    if (threadIdx.x < 64) offsets_wave(m_splits, G, total_rows, ws);
+    return;
+  }
+  const int64_t b = (int64_t)(blockIdx.x - 1) * kQThreads + threadIdx.x;
+  if (b < nblocks) quantize_row_block(src, b, data, scale);
 }
 
 // Columnwise MXFP8 (blocks of 32 consecutive rows of a column), stored transposed:
@@ -107,11 +128,11 @@ __global__ __launch_bounds__(kQThreads) void quantize_mxfp8_kernel(const uint16_
 //   Rows past a group's end read as zero (padding blocks come out all zero).
 //   Uniform mode (ws == null): groups of urows rows (a multiple of 32) each, group g
 //   stored as its own [cols, urows] matrix at data + g * cols * urows.
-__global__ __launch_bounds__(kQThreads) void quantize_mxfp8_colwise_kernel(
-    const uint16_t *__restrict__ src, int64_t cols, int64_t nblk, const void *ws, int G, int64_t total_rows,
-    int64_t urows, uint8_t *__restrict__ data, uint8_t *__restrict__ scale, int64_t ld) {
+__device__ __forceinline__ void quantize_colwise_thread(int64_t t, const uint16_t *__restrict__ src, int64_t cols,
+                                                        int64_t nblk, const void *ws, int G, int64_t total_rows,
+                                                        int64_t urows, uint8_t *__restrict__ data,
+                                                        uint8_t *__restrict__ scale, int64_t ld) {
   const int64_t quads = cols / 4;
-  const int64_t t = (int64_t)blockIdx.x * kQThreads + threadIdx.x;
   const int64_t c4 = (t % quads) * 4, b = t / quads;
   if (b >= nblk) return;
   int64_t r0, rend, out_base, out_ld, s_base, s_ld;
@@ -162,12 +183,65 @@ __global__ __launch_bounds__(kQThreads) void quantize_mxfp8_colwise_kernel(
   }
 }
 
+__global__ __launch_bounds__(kQThreads) void quantize_mxfp8_colwise_kernel(
+    const uint16_t *__restrict__ src, int64_t cols, int64_t nblk, const void *ws, int G, int64_t total_rows,
+    int64_t urows, uint8_t *__restrict__ data, uint8_t *__restrict__ scale, int64_t ld) {
+  quantize_colwise_thread((int64_t)blockIdx.x * kQThreads + threadIdx.x, src, cols, nblk, ws, G, total_rows, urows,
+                          data, scale, ld);
+}
+
+// The weights' MXFP8 workspace in one launch: rowwise codes of w [G*N, K] (forward
+// operand, row_threads threads of one block each) and, when data_t is set, the
+// columnwise codes [G, K, N] (dgrad operand, col_threads threads), walked
+// grid-stride over one index space.  A nonzero *noop (device flag, may be null)
+// makes every workgroup return at once, leaving the workspace as it was; the grid
+// is bounded so that a skipped refresh costs one small launch.
+__global__ __launch_bounds__(kQThreads) void quantize_mxfp8_weights_kernel(
+    const uint16_t *__restrict__ w, int G, int64_t N, int64_t K, int64_t row_threads, int64_t col_threads,
+    uint8_t *__restrict__ data, uint8_t *__restrict__ scale, uint8_t *__restrict__ data_t,
+    uint8_t *__restrict__ scale_t, const int32_t *__restrict__ noop) {
+  if (noop && *noop) return;
+  const int64_t stride = (int64_t)gridDim.x * kQThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kQThreads + threadIdx.x; i < row_threads + col_threads; i += stride) {
+    if (i < row_threads)
+      quantize_row_block(w, i, data, scale);
+    else
+      quantize_colwise_thread(i - row_threads, w, K, (int64_t)G * (N / 32), nullptr, G, 0, N, data_t, scale_t, N);
+  }
+}
+
 hipError_t launch_quantize_mxfp8(const uint16_t *src, int64_t rows, int64_t cols, uint8_t *data, uint8_t *scale,
                                  hipStream_t s) {
   const int64_t nblocks = rows * (cols / 32);
   if (nblocks == 0) return hipSuccess;
   const int64_t grid = (nblocks + kQThreads - 1) / kQThreads;
   hipLaunchKernelGGL(quantize_mxfp8_kernel, dim3((unsigned)grid), dim3(kQThreads), 0, s, src, nblocks, data, scale);
+  return hipGetLastError();
+}
+
+// Workgroups of the grid-stride weight refresh: enough to fill the chip several
+// times, few enough that a launch skipped by its no-op flag is cheap.
+constexpr int64_t kQuantizeWgs = 8192;
+
+hipError_t launch_offsets_quantize_mxfp8(const int64_t *m_splits, int G, int64_t total_rows, void *ws,
+                                         const uint16_t *src, int64_t cols, uint8_t *data, uint8_t *scale,
+                                         hipStream_t s) {
+  const int64_t nblocks = total_rows * (cols / 32);
+  const int64_t grid = 1 + (nblocks + kQThreads - 1) / kQThreads;
+  hipLaunchKernelGGL(offsets_quantize_mxfp8_kernel, dim3((unsigned)grid), dim3(kQThreads), 0, s, m_splits, G,
+                     total_rows, ws, src, nblocks, data, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_mxfp8_weights(const uint16_t *w, int G, int64_t N, int64_t K, uint8_t *data,
+                                         uint8_t *scale, uint8_t *data_t, uint8_t *scale_t, const int32_t *noop,
+                                         hipStream_t s) {
+  const int64_t row_threads = (int64_t)G * N * (K / 32);
+  const int64_t col_threads = data_t ? (int64_t)G * (N / 32) * (K / 4) : 0;
+  const int64_t wgs = (row_threads + col_threads + kQThreads - 1) / kQThreads;
+  const int64_t grid = wgs < kQuantizeWgs ? wgs : kQuantizeWgs;
+  hipLaunchKernelGGL(quantize_mxfp8_weights_kernel, dim3((unsigned)(grid > 0 ? grid : 1)), dim3(kQThreads), 0, s,
+                     w, G, N, K, row_threads, col_threads, data, scale, data_t, scale_t, noop);
   return hipGetLastError();
 }
 

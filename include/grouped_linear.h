@@ -221,6 +221,40 @@ int gl_group_quantize_mxfp8_colwise(const void *src, int64_t cols, int num_group
                                     hipStream_t stream);
 
 /*
+ * Split-offset scan and rowwise MXFP8 quantization of the activations in one launch
+ * (page "Single parameter for GroupedLinear module", review comments: compute the
+ * tensor offsets in the same kernel rather than a separate cumsum; the grouped
+ * MXFP8 forward quantizes x per split, page "Improve device-init grouped linear
+ * module with single grouped weight support").  Exactly gl_offsets followed by
+ * gl_group_quantize_mxfp8(x, total_rows, in_features, ...): the workspace gets the
+ * offsets, tile tables and status word, and x [T, K] (bf16, K % 32 == 0) its codes
+ * x_data [T, K] and scales x_scale [T, K / 32].  Rowwise blocks never straddle
+ * rows, so the quantization is written even when the splits are found invalid
+ * (the status word then stops every later kernel).  x and x_data 16-byte aligned.
+ */
+int gl_offsets_quantize_mxfp8(const int64_t *m_splits, int num_groups, int64_t total_rows, void *workspace,
+                              const void *x, int64_t in_features, uint8_t *x_data, uint8_t *x_scale,
+                              hipStream_t stream);
+
+/*
+ * The MXFP8 weight workspace, refreshed in one launch and skippable on the device
+ * (page "Improve device-init grouped linear module with single grouped weight
+ * support": group_quantize writes into a cached output in place and takes a
+ * noop_flag, so a captured graph can replay the weight quantization without new
+ * pointers).  w: stacked bf16 [G, N, K], K % 32 == 0, 16-byte aligned.
+ *   data, scale      rowwise codes [G, N, K] and scales [G, N, K / 32] (the forward
+ *                    operand, as gl_group_quantize_mxfp8 of w viewed as [G*N, K])
+ *   data_t, scale_t  columnwise codes [G, K, N] and scales [G, K, N / 32] (the dgrad
+ *                    operand, as gl_quantize_mxfp8_colwise_weights), or both NULL;
+ *                    needs N % 32 == 0
+ *   noop_flag        device int32, or NULL: when it holds a nonzero value at run
+ *                    time nothing is written and the workspace keeps its contents
+ */
+int gl_quantize_mxfp8_weights(const void *w, int num_groups, int64_t out_features, int64_t in_features,
+                              uint8_t *data, uint8_t *scale, uint8_t *data_t, uint8_t *scale_t,
+                              const int32_t *noop_flag, hipStream_t stream);
+
+/*
  * Columnwise MXFP8 of stacked bf16 weights w [G, N, K] (blocks of 32 along N, the
  * dgrad contraction) into codes [G, K, N] and scales [G, K, N / 32]; N % 32 == 0,
  * K % 4 == 0.

@@ -107,6 +107,18 @@ def test_other_entry_points_reject():
                               None) == -3
     assert lib.gl_wgrad_mxfp8(4, 64, 32, 1000, gl.GL_F32, FAKE, FAKE, FAKE, FAKE, ld, FAKE2, FAKE2, 1, FAKE,
                               None) == -1
+    # fused offsets + activation quantize
+    assert lib.gl_offsets_quantize_mxfp8(FAKE, 0, 32, FAKE, FAKE, 64, FAKE2, FAKE2, None) == -1
+    assert lib.gl_offsets_quantize_mxfp8(FAKE, 4, 32, FAKE, FAKE, 48, FAKE2, FAKE2, None) == -3
+    assert lib.gl_offsets_quantize_mxfp8(FAKE + 4, 4, 32, FAKE, FAKE, 64, FAKE2, FAKE2, None) == -1
+    assert lib.gl_offsets_quantize_mxfp8(FAKE, 4, 32, FAKE, None, 64, FAKE2, FAKE2, None) == -1
+    assert lib.gl_offsets_quantize_mxfp8(FAKE, 4, 32, FAKE, FAKE + 8, 64, FAKE2, FAKE2, None) == -1
+    # cached weight workspace
+    assert lib.gl_quantize_mxfp8_weights(FAKE, 2, 64, 48, FAKE2, FAKE2, None, None, None, None) == -3
+    assert lib.gl_quantize_mxfp8_weights(FAKE, 2, 64, 64, FAKE2, FAKE2, FAKE2, None, None, None) == -1
+    assert lib.gl_quantize_mxfp8_weights(FAKE, 2, 48, 64, FAKE2, FAKE2, FAKE2, FAKE2, None, None) == -3
+    assert lib.gl_quantize_mxfp8_weights(FAKE, 2, 64, 64, FAKE2, FAKE2, None, None, FAKE + 2, None) == -1
+    assert lib.gl_quantize_mxfp8_weights(FAKE, 0, 64, 64, FAKE2, FAKE2, None, None, None, None) == -1
 
 
 def test_zero_rows_is_a_no_op_without_device_work():
