@@ -61,6 +61,7 @@ def load():
         "gl_forward": (I, [I, I64, I64, I64, I, I, P, P, P, P, P, P, P, P, P, I64, P, P]),
         "gl_dgrad": (I, [I, I64, I64, I64, I, P, P, P, P, I64, P, P]),
         "gl_wgrad": (I, [I, I64, I64, I64, I, I, P, P, P, P, I, P, P]),
+        "gl_wgrad_bgrad": (I, [I, I64, I64, I64, I, I, I, P, P, P, P, I, P, P, P, P]),
         "gl_bgrad": (I, [I, I64, I64, I, P, P, P, P, P]),
         "gl_group_quantize_mxfp8": (I, [P, I64, I64, P, P, P]),
         "gl_colwise_ld": (I64, [I, I64]),
@@ -215,6 +216,27 @@ def gl_wgrad(x: Tensor, dy: Tensor, dw: Grouped, workspace: Tensor, *, accumulat
                            _ptr(workspace), _stream(stream)))
     del keep
     return dw
+
+
+def gl_wgrad_bgrad(x: Tensor, dy: Tensor, dw: Grouped, db: Grouped, workspace: Tensor, *, accumulate: bool = False,
+                   stream=None):
+    """gl_wgrad and the bias gradient of the same dy in one call: db is [G, N] or G
+    tensors [N], of dy's dtype or fp32."""
+    G = dw.shape[0] if isinstance(dw, Tensor) else len(dw)
+    d0 = _first(dw)
+    b0 = _first(db)
+    N, K = d0.shape[-2], d0.shape[-1]
+    T = x.shape[0]
+    if x.shape != (T, K) or dy.shape != (T, N) or x.dtype != dy.dtype:
+        raise ValueError("x must be [T, K] and dy [T, N] with one dtype")
+    if b0.shape[-1] != N or (isinstance(db, Tensor) and db.shape != (G, N)):
+        raise ValueError("db must be [G, N] or G tensors [N]")
+    dp, dpp, keep = _grouped(dw, x.device)
+    bp, bpp, keep_b = _grouped(db, x.device)
+    _check(load().gl_wgrad_bgrad(G, K, N, T, _dtype(x), _dtype(d0), _dtype(b0), _ptr(x), _ptr(dy), dp, dpp,
+                                 int(bool(accumulate)), bp, bpp, _ptr(workspace), _stream(stream)))
+    del keep, keep_b
+    return dw, db
 
 
 def gl_bgrad(dy: Tensor, db: Grouped, workspace: Tensor, stream=None) -> Grouped:

@@ -21,8 +21,8 @@ hipError_t launch_forward_bf16(int G, int64_t K, int64_t N, int64_t T, const uin
 hipError_t launch_dgrad_bf16(int G, int64_t K, int64_t N, int64_t T, const uint16_t *dy, const uint16_t *w,
                              const uint16_t *const *w_ptrs, uint16_t *dx, int f16, const void *ws, hipStream_t s);
 hipError_t launch_wgrad_bf16(int G, int64_t K, int64_t N, int64_t T, const uint16_t *x, const uint16_t *dy,
-                             void *dw, void *const *dw_ptrs, int out_f32, int accumulate, int f16, const void *ws,
-                             hipStream_t s);
+                             void *dw, void *const *dw_ptrs, int out_f32, int accumulate, int f16, void *db,
+                             void *const *db_ptrs, int db_f32, const void *ws, hipStream_t s);
 hipError_t launch_forward_mxfp8(int G, int64_t K, int64_t N, int64_t T, const uint8_t *xq, const uint8_t *xs,
                                 const uint8_t *wq, const uint8_t *const *wq_ptrs, const uint8_t *ws_scale,
                                 const uint8_t *const *ws_scale_ptrs, const void *bias,
@@ -238,9 +238,14 @@ int gl_dgrad(int num_groups, int64_t in_features, int64_t out_features, int64_t 
   return hip_result(e, "gl_dgrad");
 }
 
-int gl_wgrad(int num_groups, int64_t in_features, int64_t out_features, int64_t total_rows, gl_dtype in_dtype,
-             gl_dtype out_dtype, const void *x, const void *dy, void *dw, void *const *dw_ptrs, int accumulate,
-             const void *workspace, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+// gl_wgrad, and with db / db_ptrs set also the bias gradient of the same dy.
+int wgrad_impl(const char *who, int num_groups, int64_t in_features, int64_t out_features, int64_t total_rows,
+               gl_dtype in_dtype, gl_dtype out_dtype, const void *x, const void *dy, void *dw, void *const *dw_ptrs,
+               int accumulate, bool with_db, gl_dtype db_dtype, void *db, void *const *db_ptrs,
+               const void *workspace, hipStream_t stream) {
   const int G = num_groups;
   const int64_t K = in_features, N = out_features, T = total_rows;
   GL_TRY(check_sizes(G, K, N, T));
@@ -254,14 +259,42 @@ int gl_wgrad(int num_groups, int64_t in_features, int64_t out_features, int64_t 
   GL_TRY(check_buf(x, T, "x"));
   GL_TRY(check_buf(dy, T, "dy"));
   if (accumulate != 0 && accumulate != 1) return fail(GL_ERR_ARG, "accumulate must be 0 or 1");
+  if (with_db) {
+    if (db_dtype != GL_F32 && db_dtype != in_dtype)
+      return fail(GL_ERR_DTYPE, "%s: the bias gradient is fp32 or the input type", who);
+    GL_TRY(check_one_form(db, db_ptrs, "bias gradient", false));
+    if (!is16(in_dtype) && N % 4) return fail(GL_ERR_SHAPE, "%s needs out_features %% 4 == 0 for fp32", who);
+  }
   hipError_t e;
-  if (is16(in_dtype))
+  if (is16(in_dtype)) {
     e = gl::launch_wgrad_bf16(G, K, N, T, (const uint16_t *)x, (const uint16_t *)dy, dw, dw_ptrs,
-                              out_dtype == GL_F32, accumulate, in_dtype == GL_F16, workspace, stream);
-  else
+                              out_dtype == GL_F32, accumulate, in_dtype == GL_F16, with_db ? db : nullptr,
+                              with_db ? db_ptrs : nullptr, db_dtype == GL_F32, workspace, stream);
+  } else {
     e = gl::launch_wgrad_f32(G, K, N, T, (const float *)x, (const float *)dy, (float *)dw, (float *const *)dw_ptrs,
                              accumulate, workspace, stream);
-  return hip_result(e, "gl_wgrad");
+    // fp32: the bias gradient is its own (HBM-bound) launch
+    if (e == hipSuccess && with_db) e = gl::launch_bgrad(G, N, T, 1, dy, db, db_ptrs, workspace, stream);
+  }
+  return hip_result(e, who);
+}
+}  // namespace
+
+extern "C" {
+
+int gl_wgrad(int num_groups, int64_t in_features, int64_t out_features, int64_t total_rows, gl_dtype in_dtype,
+             gl_dtype out_dtype, const void *x, const void *dy, void *dw, void *const *dw_ptrs, int accumulate,
+             const void *workspace, hipStream_t stream) {
+  return wgrad_impl("gl_wgrad", num_groups, in_features, out_features, total_rows, in_dtype, out_dtype, x, dy, dw,
+                    dw_ptrs, accumulate, false, GL_F32, nullptr, nullptr, workspace, stream);
+}
+
+int gl_wgrad_bgrad(int num_groups, int64_t in_features, int64_t out_features, int64_t total_rows, gl_dtype in_dtype,
+                   gl_dtype out_dtype, gl_dtype db_dtype, const void *x, const void *dy, void *dw,
+                   void *const *dw_ptrs, int accumulate, void *db, void *const *db_ptrs, const void *workspace,
+                   hipStream_t stream) {
+  return wgrad_impl("gl_wgrad_bgrad", num_groups, in_features, out_features, total_rows, in_dtype, out_dtype, x, dy,
+                    dw, dw_ptrs, accumulate, true, db_dtype, db, db_ptrs, workspace, stream);
 }
 
 int gl_bgrad(int num_groups, int64_t out_features, int64_t total_rows, gl_dtype dtype, const void *dy, void *db,

@@ -53,9 +53,13 @@ namespace gemm {
 
 // F16: the operands are fp16 (v_mfma_f32_32x32x16_f16) instead of bf16; staging and
 // fragments are the same 16-byte moves of 2-byte elements.
-template <bool A_KMAJ, bool B_KMAJ, int MODE, bool F16>
+// BGRAD (wgrad only): the tiles of the first column also produce the bias gradient.
+template <bool A_KMAJ, bool B_KMAJ, int MODE, bool F16, bool BGRAD = false>
 __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
-  __shared__ __attribute__((aligned(1024))) char lds[kS * kStageBytes];
+  // the stage ring; wgrad adds the bias-grad partial sums after it (one LDS object:
+  // a second __shared__ array makes the compiler wait for the direct loads before
+  // every LDS read)
+  __shared__ __attribute__((aligned(1024))) char lds[kS * kStageBytes + (BGRAD ? kDbLdsBytes : 0)];
 
   const WsView ws = ws_view(p.ws, p.G);
   if (!ws_usable(ws.hdr, p.G, p.T)) return;
@@ -71,11 +75,19 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
   const int nk_rows = (int)((p.P + kBK - 1) / kBK);  // row mode: the same for every tile
 
   // One work item: the whole contraction of a tile, or (SPLIT) part `part` of S of
-  // the u-th split tile.
+  // the u-th split tile.  A wgrad tile of the first column, when a bias gradient is
+  // asked for, also sums its dy stages into the bias gradient of its n range (a
+  // uniform run-time switch: a second copy of the loop would cost registers).
   auto item = [&](int tile, int part, int S, int u, auto split_tag) __attribute__((always_inline)) {
     constexpr bool SPLIT = decltype(split_tag)::value;
     const Tile t = decode_tile<A_KMAJ, B_KMAJ, MODE>(p, off, pre, tile);
-    if (MODE == MODE_CONTR && p.accumulate && t.g_rows == 0) return;  // main_grad untouched
+    const bool bgrad = BGRAD && t.jt == 0;
+    float *dbl = (float *)(lds + kS * kStageBytes);  // bias grad partials [kDbGroups][256 columns]
+    if (MODE == MODE_CONTR && p.accumulate && t.g_rows == 0) {  // main_grad untouched
+      if (bgrad) store_bgrad_zero(p, t);
+      return;
+    }
+    if (bgrad) db_zero(dbl);
     const int64_t pmax = t.pmax;
     const int nk = (int)((pmax + kBK - 1) / kBK);
     const int nfull = (int)(pmax / kBK);  // stages [0, nfull) are complete; nk - nfull <= 1
@@ -164,6 +176,8 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
         mfmas(fa[ks & 1], fb[ks & 1]);
         fence();
       }
+      // stage kt stays in its slot until the barrier below
+      if (BGRAD && bgrad) db_stage<F16>(stage_ptr(kt), dbl);
       // stage kt + 1 complete: at most the loads of stages kt + 2 .. kt + kS - 1
       // may still be in flight
       if (steady)
@@ -187,17 +201,13 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
       // the ring is idle after the loop's last barrier: its first word carries the flag
       if (!split_finish(ws, u, part, S, acc, (int *)lds)) return;
     }
+    if (BGRAD && bgrad) store_bgrad<F16>(p, t, dbl);
     store_tile<MODE, F16>(p, t, acc, wm, wn, lane);
   };
 
   // whole tiles, round after round; in row mode the last round may be split
-#ifndef GL_NOSPLIT
   const int full = MODE == MODE_ROWS ? split_plan(total, grid, nk_rows).full : total;
-#else
-  const int full = total;
-#endif
   for (int w = first; w < full; w += grid) item(w, 0, 1, 0, std::false_type{});
-#ifndef GL_NOSPLIT
   if constexpr (MODE == MODE_ROWS) {
     const int tiles = pre[p.G] * p.tiles_j;
     const SplitPlan sp = split_plan(tiles, grid, nk_rows);
@@ -205,7 +215,6 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
     if (first < sp.rem * sp.S)
       item(sp.full + first % sp.rem, first / sp.rem, sp.S, first % sp.rem, std::true_type{});
   }
-#endif
 }
 
 }  // namespace gemm
@@ -256,8 +265,8 @@ hipError_t launch_dgrad_bf16(int G, int64_t K, int64_t N, int64_t T, const uint1
 
 // wgrad: dW_g[n][k] = sum_r dy[r][n] x[r][k]; A[i=n][p=r] (n contiguous), B[j=k][p=r] (k contiguous)
 hipError_t launch_wgrad_bf16(int G, int64_t K, int64_t N, int64_t T, const uint16_t *x, const uint16_t *dy,
-                             void *dw, void *const *dw_ptrs, int out_f32, int accumulate, int f16, const void *ws,
-                             hipStream_t s) {
+                             void *dw, void *const *dw_ptrs, int out_f32, int accumulate, int f16, void *db,
+                             void *const *db_ptrs, int db_f32, const void *ws, hipStream_t s) {
   using namespace gemm;
   Params p{};
   p.A = dy; p.lda = N;
@@ -269,13 +278,18 @@ hipError_t launch_wgrad_bf16(int G, int64_t K, int64_t N, int64_t T, const uint1
   p.tiles_j = (int)((K + kBN - 1) / kBN);
   p.accumulate = accumulate;
   p.out_f32 = out_f32;
+  p.db = db; p.db_ptrs = db_ptrs; p.db_f32 = db_f32;
   const int64_t max_items = (int64_t)G * p.tiles_i * p.tiles_j;
-  if (f16)
-    hipLaunchKernelGGL((gemm_bf16_kernel<false, false, MODE_CONTR, true>), dim3(persistent_grid(max_items)),
-                       dim3(kThreads), 0, s, p);
+  const dim3 grid(persistent_grid(max_items)), block(kThreads);
+  const bool bg = db || db_ptrs;
+  if (f16 && bg)
+    hipLaunchKernelGGL((gemm_bf16_kernel<false, false, MODE_CONTR, true, true>), grid, block, 0, s, p);
+  else if (f16)
+    hipLaunchKernelGGL((gemm_bf16_kernel<false, false, MODE_CONTR, true>), grid, block, 0, s, p);
+  else if (bg)
+    hipLaunchKernelGGL((gemm_bf16_kernel<false, false, MODE_CONTR, false, true>), grid, block, 0, s, p);
   else
-    hipLaunchKernelGGL((gemm_bf16_kernel<false, false, MODE_CONTR, false>), dim3(persistent_grid(max_items)),
-                       dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((gemm_bf16_kernel<false, false, MODE_CONTR, false>), grid, block, 0, s, p);
   return hipGetLastError();
 }
 

@@ -67,6 +67,10 @@ struct Params {
   const uint8_t *b_scale;              // [G, N, K/32] stacked, or
   const uint8_t *const *b_scale_ptrs;  // per-group [N, K/32]
   int64_t scale_ld;                    // K / 32
+  // bf16 / fp16 wgrad only: bias gradient of the same dy, stacked [G, N] or per group
+  void *db;
+  void *const *db_ptrs;
+  int db_f32;                          // db is fp32 (else the input's 16-bit type)
 };
 
 // 16-byte slot swizzles for gfx950's LDS (64 banks of 4 bytes; a 16-byte read
@@ -291,6 +295,79 @@ __device__ __forceinline__ Tile decode_tile(const Params &p, const int64_t *__re
     t.pmax = (int64_t)(cpre[t.g + 1] - cpre[t.g]) * kKcontrUnits;
   }
   return t;
+}
+
+// ------------------------------------------------------- bias grad in wgrad --
+// A wgrad tile (n tile it, k tile jt) streams the group's dy[:, n tile] through the
+// ring as its A operand, MN-major: stage row p (a token row) holds the tile's 256
+// n values, 16-byte chunk c in slot c ^ swz_m(p).  The tiles of the first k column
+// also sum those rows: thread (row group rg = tid / 64, 4-column group c = tid % 64)
+// adds rows rg, rg + 8, ..., rg + 56 of every stage into its own 4 fp32 slots of an
+// LDS area [8][256]; at the end the 8 partials of each column are added and stored.
+// db_g = sum over the group's rows of dy, read once for both outputs.  Rows past
+// the group's end are zero in the ring, so they add nothing.  (Four columns per
+// thread keep the extra registers few: the loop runs at the register limit.)
+constexpr int kDbGroups = kThreads / 64;
+constexpr int kDbLdsBytes = kDbGroups * 256 * 4;
+static_assert(kThreads == 512 && kBK == 64, "bias-grad thread mapping");
+
+__device__ __forceinline__ void db_zero(float *dbl) {
+  *(float4 *)(dbl + (threadIdx.x >> 6) * 256 + (threadIdx.x & 63) * 4) = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+template <bool F16>
+__device__ __forceinline__ void db_stage(const char *st, float *dbl) {
+  const int c = threadIdx.x & 63, rg = threadIdx.x >> 6;
+  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+  for (int q = 0; q < kBK / kDbGroups; ++q) {
+    const int r = rg + kDbGroups * q;
+    const uint2 v = *(const uint2 *)(st + r * 512 + (((c >> 1) ^ swz_m(r)) << 4) + (c & 1) * 8);
+    s0 += h16_to_f32<F16>((uint16_t)(v.x & 0xffffu));
+    s1 += h16_to_f32<F16>((uint16_t)(v.x >> 16));
+    s2 += h16_to_f32<F16>((uint16_t)(v.y & 0xffffu));
+    s3 += h16_to_f32<F16>((uint16_t)(v.y >> 16));
+  }
+  float4 *slot = (float4 *)(dbl + rg * 256 + c * 4);
+  float4 a = *slot;
+  a.x += s0; a.y += s1; a.z += s2; a.w += s3;
+  *slot = a;
+}
+
+__device__ __forceinline__ char *db_row(const Params &p, int g) {
+  return p.db ? (char *)p.db + (int64_t)g * p.rows_i * (p.db_f32 ? 4 : 2) : (char *)p.db_ptrs[g];
+}
+
+// Adds the kDbGroups partials of each column and stores db[g][n tile]; whole workgroup.
+template <bool F16>
+__device__ __forceinline__ void store_bgrad(const Params &p, const Tile &t, const float *dbl) {
+  __syncthreads();  // every thread's last stage is in the partials
+  const int col = threadIdx.x;
+  if (col < t.a_rv) {
+    float v = 0.f;
+#pragma unroll
+    for (int rg = 0; rg < kDbGroups; ++rg) v += dbl[rg * 256 + col];
+    char *row = db_row(p, t.g);
+    const int64_t n = (int64_t)t.it * kBM + col;
+    if (p.db_f32)
+      ((float *)row)[n] = v;
+    else
+      ((uint16_t *)row)[n] = f32_to_h16<F16>(v);
+  }
+  __syncthreads();  // the partials area is free for the next tile
+}
+
+// An empty group whose wgrad is skipped (accumulate mode) still has db = 0.
+__device__ __forceinline__ void store_bgrad_zero(const Params &p, const Tile &t) {
+  const int col = threadIdx.x;
+  if (col < t.a_rv) {
+    char *row = db_row(p, t.g);
+    const int64_t n = (int64_t)t.it * kBM + col;
+    if (p.db_f32)
+      ((float *)row)[n] = 0.f;
+    else
+      ((uint16_t *)row)[n] = 0;
+  }
 }
 
 // ------------------------------------------------------------- split tail --

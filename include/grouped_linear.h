@@ -170,6 +170,24 @@ int gl_bgrad(int num_groups, int64_t out_features, int64_t total_rows, gl_dtype 
              hipStream_t stream);
 
 /*
+ * gl_wgrad and gl_bgrad of the same dy in one call, dy read once (page
+ * "transformer_engine/pytorch/ops/basic/grouped_linear.py", fuser_backward: the
+ * bias gradient and the wgrad GEMMs both consume the grad output).  For bf16 / fp16
+ * inputs the wgrad tiles of the first column of in_features also add up their dy
+ * stages while those sit in LDS, so no separate pass over dy runs; for fp32 inputs
+ * the bias gradient is a second launch.  Arguments as gl_wgrad, plus
+ *   db_dtype       GL_F32 or in_dtype
+ *   db / db_ptrs   stacked [G, N] or device array of G pointers to [N]; every group
+ *                  gets its column sums (zeros for an empty group, also when
+ *                  accumulate leaves that group's main_grad untouched)
+ * fp32 accumulation in a fixed order (deterministic).
+ */
+int gl_wgrad_bgrad(int num_groups, int64_t in_features, int64_t out_features, int64_t total_rows,
+                   gl_dtype in_dtype, gl_dtype out_dtype, gl_dtype db_dtype, const void *x, const void *dy,
+                   void *dw, void *const *dw_ptrs, int accumulate, void *db, void *const *db_ptrs,
+                   const void *workspace, hipStream_t stream);
+
+/*
  * Rowwise MXFP8 quantization of a bf16 [rows, cols] matrix (page
  * "transformer_engine/pytorch/ops/basic/grouped_linear.py", _quantize_weights_mxfp8:
  * E4M3 data with one scale per 32 elements along the inner dimension; the scale

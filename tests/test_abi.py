@@ -107,6 +107,15 @@ def test_other_entry_points_reject():
                               None) == -3
     assert lib.gl_wgrad_mxfp8(4, 64, 32, 1000, gl.GL_F32, FAKE, FAKE, FAKE, FAKE, ld, FAKE2, FAKE2, 1, FAKE,
                               None) == -1
+    # wgrad + bias grad in one call
+    assert lib.gl_wgrad_bgrad(4, 64, 32, 32, gl.GL_BF16, gl.GL_BF16, gl.GL_F16, FAKE, FAKE, FAKE2, None, 0,
+                              FAKE2, None, FAKE, None) == -2
+    assert lib.gl_wgrad_bgrad(4, 64, 32, 32, gl.GL_BF16, gl.GL_BF16, gl.GL_BF16, FAKE, FAKE, FAKE2, None, 0,
+                              None, None, FAKE, None) == -1
+    assert lib.gl_wgrad_bgrad(4, 64, 32, 32, gl.GL_BF16, gl.GL_BF16, gl.GL_F32, FAKE, FAKE, FAKE2, None, 0,
+                              FAKE2, FAKE2, FAKE, None) == -1
+    assert lib.gl_wgrad_bgrad(4, 64, 30, 32, gl.GL_F32, gl.GL_F32, gl.GL_F32, FAKE, FAKE, FAKE2, None, 0,
+                              FAKE2, None, FAKE, None) == -3
     # fused offsets + activation quantize
     assert lib.gl_offsets_quantize_mxfp8(FAKE, 0, 32, FAKE, FAKE, 64, FAKE2, FAKE2, None) == -1
     assert lib.gl_offsets_quantize_mxfp8(FAKE, 4, 32, FAKE, FAKE, 48, FAKE2, FAKE2, None) == -3
