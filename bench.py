@@ -105,7 +105,9 @@ def summarize_pmc(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
 
     ff = copy_factor(copy_fetch_csv, "FETCH_SIZE")
     fw = copy_factor(copy_write_csv, "WRITE_SIZE")
+    # entries of other workloads survive; this workload's passes are rewritten
     table = json.load(open(TRAFFIC_JSON)) if os.path.exists(TRAFFIC_JSON) else {}
+    table = {k: v for k, v in table.items() if k.split(":")[0] not in set(PASS_WORKLOAD.values())}
     sha = source_hash(GEMM_SRCS)
     lines = [f"copy calibration ({COPY_BYTES} B): FETCH_SIZE x{ff:.3f}, WRITE_SIZE x{fw:.3f}"]
     for name, args in PASS_KERNELS.items():
