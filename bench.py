@@ -340,12 +340,54 @@ def bench_mxfp8(torch, gl, synth, steps, warmup):
     return out
 
 
+def bench_mlp(torch, gl, steps, warmup):
+    """Grouped MLP (FC1 -> SwiGLU -> FC2) on the 8-group token split: FC1 has the
+    8-group workload's shape (K=4096 -> 2F=14336), FC2 maps F=7168 -> N=4096.
+    Forward and backward (with both bias grads fused into the wgrads) per step."""
+    import synth
+    wl = synth.WORKLOADS["bf16_train_g8_k4096_n14336"]
+    dev = torch.device("cuda")
+    G, T, K, F, N = wl.G, wl.T, wl.K, wl.N // 2, wl.K
+    m = synth.split_sizes(wl)
+    g = torch.Generator(device=dev).manual_seed(5)
+    bf = torch.bfloat16
+    r = lambda *s, std=1.0: (torch.randn(*s, generator=g, device=dev) * std).to(bf)
+    x, dy = r(T, K), r(T, N)
+    w1, b1, w2, b2 = r(G, 2 * F, K, std=0.02), r(G, 2 * F, std=0.1), r(G, N, F, std=0.02), r(G, N, std=0.1)
+    h, a, y = (torch.empty(T, c, dtype=bf, device=dev) for c in (2 * F, F, N))
+    da, dh, dx = (torch.empty(T, c, dtype=bf, device=dev) for c in (F, 2 * F, K))
+    dw1, dw2 = torch.empty_like(w1), torch.empty_like(w2)
+    db1, db2 = torch.empty_like(b1), torch.empty_like(b2)
+    ws = gl.new_workspace(G, dev)
+    gl.gl_offsets(torch.from_numpy(m).to(dev), T, ws)
+    timer = EventTimer(torch)
+    for i in range(warmup + steps):
+        run = (lambda n, f: timer.run(n, f)) if i >= warmup else (lambda n, f: f())
+        run("forward", lambda: gl.gl_grouped_mlp_forward(x, w1, w2, h, a, y, ws, b1=b1, b2=b2))
+        run("backward", lambda: gl.gl_grouped_mlp_backward(x, w1, w2, h, a, dy, da, dh, dx, dw1, dw2, ws,
+                                                           db1=db1, db2=db2))
+        run("swiglu_forward", lambda: gl.gl_swiglu_forward(h, a))
+        run("swiglu_backward", lambda: gl.gl_swiglu_backward(h, da, dh))
+    torch.cuda.synchronize()
+    per = timer.mean_ms()
+    fwd_flops = 2.0 * T * (K * 2 * F + F * N)
+    tf = lambda fl, ms: round(fl / (ms * 1e-3) / 1e12, 2)
+    return {"config": {"num_groups": G, "total_rows": T, "in_features": K, "ffn_features": F, "out_features": N,
+                       "activation": "swiglu", "bias": True},
+            "forward_ms": round(per["forward"], 4), "forward_tflops": tf(fwd_flops, per["forward"]),
+            "backward_ms": round(per["backward"], 4), "backward_tflops": tf(2 * fwd_flops, per["backward"]),
+            "step_tflops": tf(3 * fwd_flops, per["forward"] + per["backward"]),
+            "swiglu_gbs": {"forward": round(T * 3 * F * 2 / (per["swiglu_forward"] * 1e-3) / 1e9, 1),
+                           "backward": round(T * 5 * F * 2 / (per["swiglu_backward"] * 1e-3) / 1e9, 1)}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-mxfp8", action="store_true")
+    ap.add_argument("--no-mlp", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB copy (counter calibration)")
@@ -392,6 +434,8 @@ def main():
     }
     if not args.no_mxfp8:
         out["mxfp8"] = bench_mxfp8(torch, gl, synth, max(5, args.steps // 2), 2)
+    if not args.no_mlp:
+        out["grouped_mlp"] = bench_mlp(torch, gl, max(5, args.steps // 2), 2)
     if not args.no_cpu_baseline:
         x, w, b, dy = host_inputs
         out["cpu_baseline"] = cpu_baseline(wl, m.tolist(), x, w, b, dy)

@@ -68,6 +68,10 @@ def load():
         "gl_group_quantize_mxfp8_colwise": (I, [P, I64, I, I64, P, P, P, I64, P]),
         "gl_quantize_mxfp8_colwise_weights": (I, [P, I, I64, I64, P, P, P]),
         "gl_offsets_quantize_mxfp8": (I, [P, I, I64, P, P, I64, P, P, P]),
+        "gl_swiglu_forward": (I, [I64, I64, I, P, P, P]),
+        "gl_swiglu_backward": (I, [I64, I64, I, P, P, P, P]),
+        "gl_grouped_mlp_forward": (I, [I, I64, I64, I64, I64, I] + [P] * 12 + [I64, P, P]),
+        "gl_grouped_mlp_backward": (I, [I, I64, I64, I64, I64, I, I] + [P] * 11 + [I64] + [P] * 8 + [I, P, P]),
         "gl_quantize_mxfp8_weights": (I, [P, I, I64, I64, P, P, P, P, P, P]),
         "gl_dgrad_mxfp8": (I, [I, I64, I64, I64, I, P, P, P, P, P, I64, P, P]),
         "gl_wgrad_mxfp8": (I, [I, I64, I64, I64, I, P, P, P, P, I64, P, P, I, P, P]),
@@ -329,6 +333,70 @@ def gl_quantize_mxfp8_weights(w: Tensor, data: Tensor, scale: Tensor, data_t: Te
                                             _ptr(scale_t) if scale_t is not None else None,
                                             _ptr(noop_flag) if noop_flag is not None else None, _stream(stream)))
     return data, scale
+
+
+def gl_swiglu_forward(h: Tensor, a: Tensor, stream=None) -> Tensor:
+    """a [T, F] = silu(h[:, :F]) * h[:, F:] for h [T, 2F]."""
+    T, F2 = h.shape
+    if a.shape != (T, F2 // 2) or a.dtype != h.dtype or F2 % 2:
+        raise ValueError("h must be [T, 2F] and a [T, F] of h's dtype")
+    _check(load().gl_swiglu_forward(T, F2 // 2, _dtype(h), _ptr(h), _ptr(a), _stream(stream)))
+    return a
+
+
+def gl_swiglu_backward(h: Tensor, da: Tensor, dh: Tensor, stream=None) -> Tensor:
+    """dh [T, 2F]: the gradient of gl_swiglu_forward at h for the upstream gradient da [T, F]."""
+    T, F2 = h.shape
+    if da.shape != (T, F2 // 2) or dh.shape != h.shape or not (da.dtype == dh.dtype == h.dtype):
+        raise ValueError("h and dh must be [T, 2F] and da [T, F], one dtype")
+    _check(load().gl_swiglu_backward(T, F2 // 2, _dtype(h), _ptr(h), _ptr(da), _ptr(dh), _stream(stream)))
+    return dh
+
+
+def gl_grouped_mlp_forward(x: Tensor, w1: Grouped, w2: Grouped, h: Tensor, a: Tensor, y: Tensor, workspace: Tensor,
+                           b1: Grouped = None, b2: Grouped = None, stream=None) -> Tensor:
+    """y[:T] = FC2(SwiGLU(FC1(x))) per group; h [T, 2F] and a [T, F] receive the
+    intermediates (kept for the backward); y may have more rows than T."""
+    G = w1.shape[0] if isinstance(w1, Tensor) else len(w1)
+    F2, K = _first(w1).shape[-2:]
+    N = _first(w2).shape[-2]
+    T = x.shape[0]
+    if x.shape != (T, K) or h.shape != (T, F2) or a.shape != (T, F2 // 2) or y.dim() != 2 or y.shape[1] != N:
+        raise ValueError("shapes: x [T, K], w1 [G, 2F, K], w2 [G, N, F], h [T, 2F], a [T, F], y [rows >= T, N]")
+    p1, pp1, k1 = _grouped(w1, x.device)
+    p2, pp2, k2 = _grouped(w2, x.device)
+    q1, qq1, k3 = _grouped(b1, x.device)
+    q2, qq2, k4 = _grouped(b2, x.device)
+    _check(load().gl_grouped_mlp_forward(G, K, F2 // 2, N, T, _dtype(x), _ptr(x), p1, pp1, q1, qq1, p2, pp2, q2, qq2,
+                                         _ptr(h), _ptr(a), _ptr(y), y.shape[0], _ptr(workspace), _stream(stream)))
+    del k1, k2, k3, k4
+    return y
+
+
+def gl_grouped_mlp_backward(x: Tensor, w1: Grouped, w2: Grouped, h: Tensor, a: Tensor, dy: Tensor, da: Tensor,
+                            dh: Tensor, dx: Tensor, dw1: Grouped, dw2: Grouped, workspace: Tensor,
+                            db1: Grouped = None, db2: Grouped = None, *, accumulate: bool = False, stream=None):
+    """Backward of gl_grouped_mlp_forward: dx[:T], dW1, dW2 (of dw1's dtype: the
+    input's or fp32, added into them with ``accumulate``), optional db1, db2; da
+    [T, F] and dh [T, 2F] are scratch."""
+    G = w1.shape[0] if isinstance(w1, Tensor) else len(w1)
+    F2, K = _first(w1).shape[-2:]
+    N = _first(w2).shape[-2]
+    T = x.shape[0]
+    if dy.shape != (T, N) or da.shape != (T, F2 // 2) or dh.shape != (T, F2) or dx.dim() != 2 or dx.shape[1] != K:
+        raise ValueError("shapes: dy [T, N], da [T, F], dh [T, 2F], dx [rows >= T, K]")
+    keep = []
+    ptr = {}
+    for name, g in (("w1", w1), ("w2", w2), ("dw1", dw1), ("dw2", dw2), ("db1", db1), ("db2", db2)):
+        p, pp, k = _grouped(g, x.device)
+        ptr[name] = (p, pp)
+        keep.append(k)
+    _check(load().gl_grouped_mlp_backward(G, K, F2 // 2, N, T, _dtype(x), _dtype(_first(dw1)), _ptr(x), *ptr["w1"],
+                                          *ptr["w2"], _ptr(h), _ptr(a), _ptr(dy), _ptr(da), _ptr(dh), _ptr(dx),
+                                          dx.shape[0], *ptr["dw1"], *ptr["db1"], *ptr["dw2"], *ptr["db2"],
+                                          int(bool(accumulate)), _ptr(workspace), _stream(stream)))
+    del keep
+    return dx
 
 
 def gl_dgrad_mxfp8(dy: Tensor, dy_scale: Tensor, w_t: Tensor, w_t_scale: Tensor, dx: Tensor, workspace: Tensor,

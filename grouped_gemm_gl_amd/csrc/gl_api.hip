@@ -49,6 +49,8 @@ hipError_t launch_offsets_quantize_mxfp8(const int64_t *m_splits, int G, int64_t
 hipError_t launch_quantize_mxfp8_weights(const uint16_t *w, int G, int64_t N, int64_t K, uint8_t *data,
                                          uint8_t *scale, uint8_t *data_t, uint8_t *scale_t, const int32_t *noop,
                                          hipStream_t s);
+hipError_t launch_swiglu_fwd(int el, int64_t T, int64_t F, const void *h, void *a, hipStream_t s);
+hipError_t launch_swiglu_bwd(int el, int64_t T, int64_t F, const void *h, const void *da, void *dh, hipStream_t s);
 hipError_t launch_wgrad_mxfp8(int G, int64_t K, int64_t N, int64_t T, const uint8_t *dyt, const uint8_t *dyt_s,
                               const uint8_t *xt, const uint8_t *xt_s, int64_t ld, void *dw, void *const *dw_ptrs,
                               int out_f32, int accumulate, const void *ws, hipStream_t s);
@@ -166,11 +168,16 @@ int gl_read_status(const void *workspace, int *status, hipStream_t stream) {
   return ok();
 }
 
-int gl_forward(int num_groups, int64_t in_features, int64_t out_features, int64_t total_rows, gl_dtype in_dtype,
-               gl_dtype out_dtype, const void *x, const uint8_t *x_scale, const void *w, const void *const *w_ptrs,
-               const uint8_t *w_scale, const uint8_t *const *w_scale_ptrs, const void *bias,
-               const void *const *bias_ptrs, void *y, int64_t y_rows, const void *workspace,
-               hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+// The entry points' checks, then (launch) the kernels; with launch false only the
+// checks run, so a composite call can check every step before it launches any.
+int forward_impl(int num_groups, int64_t in_features, int64_t out_features, int64_t total_rows, gl_dtype in_dtype,
+                 gl_dtype out_dtype, const void *x, const uint8_t *x_scale, const void *w, const void *const *w_ptrs,
+                 const uint8_t *w_scale, const uint8_t *const *w_scale_ptrs, const void *bias,
+                 const void *const *bias_ptrs, void *y, int64_t y_rows, const void *workspace, hipStream_t stream,
+                 bool launch) {
   const int G = num_groups;
   const int64_t K = in_features, N = out_features, T = total_rows;
   GL_TRY(check_sizes(G, K, N, T));
@@ -190,7 +197,7 @@ int gl_forward(int num_groups, int64_t in_features, int64_t out_features, int64_
     if ((w != nullptr) != (w_scale != nullptr) || (w_ptrs != nullptr) != (w_scale_ptrs != nullptr))
       return fail(GL_ERR_ARG, "weight scales must come in the same form as the weights");
     if (w_scale && ((uintptr_t)w_scale & 3u)) return fail(GL_ERR_ARG, "w_scale not 4-byte aligned");
-    if (T == 0) return ok();
+    if (T == 0 || !launch) return ok();
     return hip_result(gl::launch_forward_mxfp8(G, K, N, T, (const uint8_t *)x, x_scale, (const uint8_t *)w,
                                                (const uint8_t *const *)w_ptrs, w_scale, w_scale_ptrs, bias,
                                                bias_ptrs, y, out_dtype == GL_F32, workspace, stream),
@@ -201,7 +208,7 @@ int gl_forward(int num_groups, int64_t in_features, int64_t out_features, int64_
     return fail(GL_ERR_DTYPE, "gl_forward: out_dtype must equal in_dtype for fp32/bf16/fp16");
   if (x_scale || w_scale || w_scale_ptrs) return fail(GL_ERR_ARG, "scales are only for GL_E4M3 inputs");
   GL_TRY(check_bf16_dims(in_dtype, K, N));
-  if (T == 0) return ok();
+  if (T == 0 || !launch) return ok();
   hipError_t e;
   if (is16(in_dtype))
     e = gl::launch_forward_bf16(G, K, N, T, (const uint16_t *)x, (const uint16_t *)w,
@@ -213,9 +220,9 @@ int gl_forward(int num_groups, int64_t in_features, int64_t out_features, int64_
   return hip_result(e, "gl_forward");
 }
 
-int gl_dgrad(int num_groups, int64_t in_features, int64_t out_features, int64_t total_rows, gl_dtype dtype,
-             const void *dy, const void *w, const void *const *w_ptrs, void *dx, int64_t dx_rows,
-             const void *workspace, hipStream_t stream) {
+int dgrad_impl(int num_groups, int64_t in_features, int64_t out_features, int64_t total_rows, gl_dtype dtype,
+               const void *dy, const void *w, const void *const *w_ptrs, void *dx, int64_t dx_rows,
+               const void *workspace, hipStream_t stream, bool launch) {
   const int G = num_groups;
   const int64_t K = in_features, N = out_features, T = total_rows;
   GL_TRY(check_sizes(G, K, N, T));
@@ -227,7 +234,7 @@ int gl_dgrad(int num_groups, int64_t in_features, int64_t out_features, int64_t 
   GL_TRY(check_one_form(w, w_ptrs, "weight", false));
   GL_TRY(check_buf(dy, T, "dy"));
   GL_TRY(check_buf(dx, T, "dx"));
-  if (T == 0) return ok();
+  if (T == 0 || !launch) return ok();
   hipError_t e;
   if (is16(dtype))
     e = gl::launch_dgrad_bf16(G, K, N, T, (const uint16_t *)dy, (const uint16_t *)w, (const uint16_t *const *)w_ptrs,
@@ -238,14 +245,11 @@ int gl_dgrad(int num_groups, int64_t in_features, int64_t out_features, int64_t 
   return hip_result(e, "gl_dgrad");
 }
 
-}  // extern "C"
-
-namespace {
 // gl_wgrad, and with db / db_ptrs set also the bias gradient of the same dy.
 int wgrad_impl(const char *who, int num_groups, int64_t in_features, int64_t out_features, int64_t total_rows,
                gl_dtype in_dtype, gl_dtype out_dtype, const void *x, const void *dy, void *dw, void *const *dw_ptrs,
                int accumulate, bool with_db, gl_dtype db_dtype, void *db, void *const *db_ptrs,
-               const void *workspace, hipStream_t stream) {
+               const void *workspace, hipStream_t stream, bool launch = true) {
   const int G = num_groups;
   const int64_t K = in_features, N = out_features, T = total_rows;
   GL_TRY(check_sizes(G, K, N, T));
@@ -265,6 +269,7 @@ int wgrad_impl(const char *who, int num_groups, int64_t in_features, int64_t out
     GL_TRY(check_one_form(db, db_ptrs, "bias gradient", false));
     if (!is16(in_dtype) && N % 4) return fail(GL_ERR_SHAPE, "%s needs out_features %% 4 == 0 for fp32", who);
   }
+  if (!launch) return ok();
   hipError_t e;
   if (is16(in_dtype)) {
     e = gl::launch_wgrad_bf16(G, K, N, T, (const uint16_t *)x, (const uint16_t *)dy, dw, dw_ptrs,
@@ -281,6 +286,22 @@ int wgrad_impl(const char *who, int num_groups, int64_t in_features, int64_t out
 }  // namespace
 
 extern "C" {
+
+int gl_forward(int num_groups, int64_t in_features, int64_t out_features, int64_t total_rows, gl_dtype in_dtype,
+               gl_dtype out_dtype, const void *x, const uint8_t *x_scale, const void *w, const void *const *w_ptrs,
+               const uint8_t *w_scale, const uint8_t *const *w_scale_ptrs, const void *bias,
+               const void *const *bias_ptrs, void *y, int64_t y_rows, const void *workspace,
+               hipStream_t stream) {
+  return forward_impl(num_groups, in_features, out_features, total_rows, in_dtype, out_dtype, x, x_scale, w, w_ptrs,
+                      w_scale, w_scale_ptrs, bias, bias_ptrs, y, y_rows, workspace, stream, true);
+}
+
+int gl_dgrad(int num_groups, int64_t in_features, int64_t out_features, int64_t total_rows, gl_dtype dtype,
+             const void *dy, const void *w, const void *const *w_ptrs, void *dx, int64_t dx_rows,
+             const void *workspace, hipStream_t stream) {
+  return dgrad_impl(num_groups, in_features, out_features, total_rows, dtype, dy, w, w_ptrs, dx, dx_rows, workspace,
+                    stream, true);
+}
 
 int gl_wgrad(int num_groups, int64_t in_features, int64_t out_features, int64_t total_rows, gl_dtype in_dtype,
              gl_dtype out_dtype, const void *x, const void *dy, void *dw, void *const *dw_ptrs, int accumulate,
@@ -467,3 +488,99 @@ int gl_wgrad_mxfp8(int num_groups, int64_t in_features, int64_t out_features, in
                                            out_dtype == GL_F32, accumulate, workspace, stream),
                     "gl_wgrad_mxfp8");
 }
+
+// ------------------------------------------------------------------ grouped MLP --
+
+namespace {
+// in1 is the backward's upstream gradient (need_in1), unused in the forward
+int swiglu_check(const char *who, int64_t T, int64_t F, gl_dtype dtype, const void *in0, const void *in1,
+                 const void *out, bool need_in1) {
+  if (T < 0 || F <= 0) return fail(GL_ERR_ARG, "%s: invalid sizes (T %lld, F %lld)", who, (long long)T, (long long)F);
+  GL_TRY(check_float_dtype(dtype, who));
+  const int v = is16(dtype) ? 8 : 4;
+  if (F % v) return fail(GL_ERR_SHAPE, "%s: F must be a multiple of %d (got %lld)", who, v, (long long)F);
+  if (F > ((int64_t)1 << 22)) return fail(GL_ERR_SHAPE, "%s: F must be at most 2^22", who);
+  if (T == 0) return GL_OK;
+  if (!in0 || !out || (need_in1 && !in1)) return fail(GL_ERR_ARG, "%s: a buffer is NULL", who);
+  if (!aligned16(in0) || !aligned16(out) || (in1 && !aligned16(in1)))
+    return fail(GL_ERR_ARG, "%s: buffers must be 16-byte aligned", who);
+  return GL_OK;
+}
+int sw_el(gl_dtype d) { return d == GL_F32 ? 1 : d == GL_F16 ? 2 : 0; }
+}  // namespace
+
+extern "C" {
+
+int gl_swiglu_forward(int64_t total_rows, int64_t F, gl_dtype dtype, const void *h, void *a, hipStream_t stream) {
+  GL_TRY(swiglu_check("gl_swiglu_forward", total_rows, F, dtype, h, nullptr, a, false));
+  if (total_rows == 0) return ok();
+  return hip_result(gl::launch_swiglu_fwd(sw_el(dtype), total_rows, F, h, a, stream), "gl_swiglu_forward");
+}
+
+int gl_swiglu_backward(int64_t total_rows, int64_t F, gl_dtype dtype, const void *h, const void *da, void *dh,
+                       hipStream_t stream) {
+  GL_TRY(swiglu_check("gl_swiglu_backward", total_rows, F, dtype, h, da, dh, true));
+  if (total_rows == 0) return ok();
+  return hip_result(gl::launch_swiglu_bwd(sw_el(dtype), total_rows, F, h, da, dh, stream), "gl_swiglu_backward");
+}
+
+int gl_grouped_mlp_forward(int num_groups, int64_t in_features, int64_t ffn_features, int64_t out_features,
+                           int64_t total_rows, gl_dtype dtype, const void *x, const void *w1,
+                           const void *const *w1_ptrs, const void *b1, const void *const *b1_ptrs, const void *w2,
+                           const void *const *w2_ptrs, const void *b2, const void *const *b2_ptrs, void *h, void *a,
+                           void *y, int64_t y_rows, const void *workspace, hipStream_t stream) {
+  const int G = num_groups;
+  const int64_t K = in_features, F = ffn_features, N = out_features, T = total_rows;
+  // every step is checked before any is launched
+  GL_TRY(check_float_dtype(dtype, "gl_grouped_mlp_forward"));
+  GL_TRY(swiglu_check("gl_grouped_mlp_forward", T, F, dtype, h, nullptr, a, false));
+  GL_TRY(forward_impl(G, K, 2 * F, T, dtype, dtype, x, nullptr, w1, w1_ptrs, nullptr, nullptr, b1, b1_ptrs, h, T,
+                      workspace, stream, false));
+  GL_TRY(forward_impl(G, F, N, T, dtype, dtype, a, nullptr, w2, w2_ptrs, nullptr, nullptr, b2, b2_ptrs, y, y_rows,
+                      workspace, stream, false));
+  if (T == 0) return ok();
+  GL_TRY(forward_impl(G, K, 2 * F, T, dtype, dtype, x, nullptr, w1, w1_ptrs, nullptr, nullptr, b1, b1_ptrs, h, T,
+                      workspace, stream, true));
+  GL_TRY(hip_result(gl::launch_swiglu_fwd(sw_el(dtype), T, F, h, a, stream), "gl_grouped_mlp_forward"));
+  return forward_impl(G, F, N, T, dtype, dtype, a, nullptr, w2, w2_ptrs, nullptr, nullptr, b2, b2_ptrs, y, y_rows,
+                      workspace, stream, true);
+}
+
+int gl_grouped_mlp_backward(int num_groups, int64_t in_features, int64_t ffn_features, int64_t out_features,
+                            int64_t total_rows, gl_dtype dtype, gl_dtype wgrad_dtype, const void *x, const void *w1,
+                            const void *const *w1_ptrs, const void *w2, const void *const *w2_ptrs, const void *h,
+                            const void *a, const void *dy, void *da, void *dh, void *dx, int64_t dx_rows, void *dw1,
+                            void *const *dw1_ptrs, void *db1, void *const *db1_ptrs, void *dw2,
+                            void *const *dw2_ptrs, void *db2, void *const *db2_ptrs, int accumulate,
+                            const void *workspace, hipStream_t stream) {
+  const int G = num_groups;
+  const int64_t K = in_features, F = ffn_features, N = out_features, T = total_rows;
+  const bool bias1 = db1 || db1_ptrs, bias2 = db2 || db2_ptrs;
+  GL_TRY(check_float_dtype(dtype, "gl_grouped_mlp_backward"));
+  GL_TRY(swiglu_check("gl_grouped_mlp_backward", T, F, dtype, h, da, dh, true));
+  auto fc2_wgrad = [&](bool launch) {
+    return wgrad_impl("gl_grouped_mlp_backward (FC2 wgrad)", G, F, N, T, dtype, wgrad_dtype, a, dy, dw2, dw2_ptrs,
+                      accumulate, bias2, dtype, db2, db2_ptrs, workspace, stream, launch);
+  };
+  auto fc2_dgrad = [&](bool launch) {
+    return dgrad_impl(G, F, N, T, dtype, dy, w2, w2_ptrs, da, T, workspace, stream, launch);
+  };
+  auto fc1_wgrad = [&](bool launch) {
+    return wgrad_impl("gl_grouped_mlp_backward (FC1 wgrad)", G, K, 2 * F, T, dtype, wgrad_dtype, x, dh, dw1,
+                      dw1_ptrs, accumulate, bias1, dtype, db1, db1_ptrs, workspace, stream, launch);
+  };
+  auto fc1_dgrad = [&](bool launch) {
+    return dgrad_impl(G, K, 2 * F, T, dtype, dh, w1, w1_ptrs, dx, dx_rows, workspace, stream, launch);
+  };
+  GL_TRY(fc2_wgrad(false));
+  GL_TRY(fc2_dgrad(false));
+  GL_TRY(fc1_wgrad(false));
+  GL_TRY(fc1_dgrad(false));
+  GL_TRY(fc2_wgrad(true));  // also runs for T == 0: empty groups' weight and bias gradients
+  GL_TRY(fc2_dgrad(true));
+  if (T > 0) GL_TRY(hip_result(gl::launch_swiglu_bwd(sw_el(dtype), T, F, h, da, dh, stream), "gl_grouped_mlp_backward"));
+  GL_TRY(fc1_wgrad(true));
+  return fc1_dgrad(true);
+}
+
+}  // extern "C"

@@ -307,6 +307,58 @@ int gl_wgrad_mxfp8(int num_groups, int64_t in_features, int64_t out_features, in
                    int64_t ld, void *dw, void *const *dw_ptrs, int accumulate, const void *workspace,
                    hipStream_t stream);
 
+/*
+ * Grouped MLP: FC1 -> SwiGLU -> FC2 over the same splits (page "[PyTorch] Add
+ * optional caller-provided output/grad-input buffers to GroupedLinear and fused
+ * grouped MLP": a fused op of two grouped linear layers and an activation, whose
+ * FC2 output and FC1 grad-input may be caller buffers of which only the packed
+ * valid rows are written).  The pages do not name the activation; it is SwiGLU on
+ * the two halves of FC1's output h [T, 2F]: a = silu(h[:, :F]) * h[:, F:], with
+ * silu(v) = v / (1 + exp(-v)), computed in fp32 and rounded once to dtype.
+ *
+ * gl_swiglu_forward: a [T, F] from h [T, 2F].  gl_swiglu_backward: dh [T, 2F] from
+ * h and the upstream gradient da [T, F] (dh_g = da * u * s (1 + g (1 - s)),
+ * dh_u = da * g * s, s = sigmoid(g)).  dtype GL_F32, GL_BF16 or GL_F16; F a multiple
+ * of 8 (16-bit) or 4 (fp32); buffers 16-byte aligned.
+ */
+int gl_swiglu_forward(int64_t total_rows, int64_t ffn_features, gl_dtype dtype, const void *h, void *a,
+                      hipStream_t stream);
+int gl_swiglu_backward(int64_t total_rows, int64_t ffn_features, gl_dtype dtype, const void *h, const void *da,
+                       void *dh, hipStream_t stream);
+
+/*
+ * Grouped MLP forward: h = FC1(x) (+ b1), a = SwiGLU(h), y = FC2(a) (+ b2).
+ *   x [T, K]; w1 / w1_ptrs [G, 2F, K] or G x [2F, K]; b1 / b1_ptrs [G, 2F] or NULL;
+ *   w2 / w2_ptrs [G, N, F] or G x [N, F]; b2 / b2_ptrs [G, N] or NULL
+ *   h [T, 2F], a [T, F]: caller buffers, kept for the backward
+ *   y [y_rows, N], y_rows >= T: rows >= T are never written
+ * All tensors of dtype (GL_F32, GL_BF16 or GL_F16).  Every step is checked before
+ * any kernel is launched; the rules of gl_forward apply to both GEMMs.
+ */
+int gl_grouped_mlp_forward(int num_groups, int64_t in_features, int64_t ffn_features, int64_t out_features,
+                           int64_t total_rows, gl_dtype dtype, const void *x, const void *w1,
+                           const void *const *w1_ptrs, const void *b1, const void *const *b1_ptrs, const void *w2,
+                           const void *const *w2_ptrs, const void *b2, const void *const *b2_ptrs, void *h, void *a,
+                           void *y, int64_t y_rows, const void *workspace, hipStream_t stream);
+
+/*
+ * Grouped MLP backward, given the forward's x, h, a and the grad output dy [T, N]:
+ *   FC2: dW2_g (+)= dy_g^T a_g and db2 (fused, one pass over dy); da = dy W2_g
+ *   SwiGLU: dh from h and da
+ *   FC1: dW1_g (+)= dh_g^T x_g and db1 (fused); dx = dh W1_g
+ *   da [T, F], dh [T, 2F]: caller scratch; dx [dx_rows, K], dx_rows >= T, rows >= T
+ *   never written; dw1 / dw2 stacked or per-group, of wgrad_dtype (GL_F32 or dtype),
+ *   accumulate as in gl_wgrad; db1 / db2 of dtype, stacked or per-group, both forms
+ *   NULL to skip a bias gradient.  Every step is checked before any is launched.
+ */
+int gl_grouped_mlp_backward(int num_groups, int64_t in_features, int64_t ffn_features, int64_t out_features,
+                            int64_t total_rows, gl_dtype dtype, gl_dtype wgrad_dtype, const void *x, const void *w1,
+                            const void *const *w1_ptrs, const void *w2, const void *const *w2_ptrs, const void *h,
+                            const void *a, const void *dy, void *da, void *dh, void *dx, int64_t dx_rows, void *dw1,
+                            void *const *dw1_ptrs, void *db1, void *const *db1_ptrs, void *dw2,
+                            void *const *dw2_ptrs, void *db2, void *const *db2_ptrs, int accumulate,
+                            const void *workspace, hipStream_t stream);
+
 const char *gl_last_error(void);
 
 /* Library identification string. */

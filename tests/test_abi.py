@@ -116,6 +116,24 @@ def test_other_entry_points_reject():
                               FAKE2, FAKE2, FAKE, None) == -1
     assert lib.gl_wgrad_bgrad(4, 64, 30, 32, gl.GL_F32, gl.GL_F32, gl.GL_F32, FAKE, FAKE, FAKE2, None, 0,
                               FAKE2, None, FAKE, None) == -3
+    # SwiGLU and the grouped MLP
+    assert lib.gl_swiglu_forward(32, 12, gl.GL_BF16, FAKE, FAKE2, None) == -3
+    assert lib.gl_swiglu_forward(32, 16, 7, FAKE, FAKE2, None) == -2
+    assert lib.gl_swiglu_backward(32, 16, gl.GL_BF16, FAKE, None, FAKE2, None) == -1
+    assert lib.gl_swiglu_backward(32, 16, gl.GL_BF16, FAKE, FAKE + 8, FAKE2, None) == -1
+    mlp_f = lambda **k: lib.gl_grouped_mlp_forward(
+        4, 64, k.get("F", 32), 48, 32, gl.GL_BF16, FAKE, FAKE, k.get("w1p"), None, None, FAKE, None, None, None,
+        FAKE2, FAKE2, FAKE2, k.get("y_rows", 32), FAKE, None)
+    assert mlp_f(F=36) == -3                         # F % 8
+    assert mlp_f(w1p=FAKE) == -1                     # both weight forms for FC1
+    assert mlp_f(y_rows=31) == -3                    # output buffer too small
+    mlp_b = lambda **k: lib.gl_grouped_mlp_backward(
+        4, 64, 32, 48, 32, gl.GL_BF16, k.get("wd", gl.GL_F32), FAKE, FAKE, None, FAKE, None, FAKE, FAKE, FAKE,
+        FAKE2, FAKE2, FAKE2, k.get("dx_rows", 32), FAKE2, None, None, None, FAKE2, None, k.get("db2"), k.get("db2p"),
+        0, FAKE, None)
+    assert mlp_b(wd=gl.GL_F16) == -2                  # wgrad dtype neither fp32 nor the input's
+    assert mlp_b(dx_rows=16) == -3
+    assert mlp_b(db2=FAKE2, db2p=FAKE2) == -1         # both bias-grad forms
     # fused offsets + activation quantize
     assert lib.gl_offsets_quantize_mxfp8(FAKE, 0, 32, FAKE, FAKE, 64, FAKE2, FAKE2, None) == -1
     assert lib.gl_offsets_quantize_mxfp8(FAKE, 4, 32, FAKE, FAKE, 48, FAKE2, FAKE2, None) == -3
