@@ -38,8 +38,11 @@ struct ScaleStream {
 // MODE_KCONTR: wgrad on transposed columnwise codes of dy and x.
 template <int MODE>
 __global__ __launch_bounds__(kThreads) void gemm_mxfp8_kernel(Params p) {
-  __shared__ __attribute__((aligned(1024))) char lds[kS * kStageBytes];
-  __shared__ __attribute__((aligned(1024))) uint32_t lds_sc[kS][2][256];  // scale dwords per tile row
+  // One LDS object: the stage ring, then the scale dwords of every tile row
+  // [kS][A, B][256].  (A second __shared__ array makes the compiler wait for every
+  // outstanding direct-to-LDS load before each LDS read.)
+  __shared__ __attribute__((aligned(1024))) char lds[kS * kStageBytes + kS * 2 * 256 * 4];
+  uint32_t(*lds_sc)[2][256] = (uint32_t(*)[2][256])(lds + kS * kStageBytes);
 
   const WsView ws = ws_view(p.ws, p.G);
   if (!ws_usable(ws.hdr, p.G, p.T)) return;
