@@ -202,7 +202,13 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
       if (!split_finish(ws, u, part, S, acc, (int *)lds)) return;
     }
     if (BGRAD && bgrad) store_bgrad<F16>(p, t, dbl);
-    store_tile<MODE, F16>(p, t, acc, wm, wn, lane);
+    // wgrad tiles contract over one group's rows only, so their output stores weigh
+    // more: there the tile goes out through LDS as whole lines (measured neutral to
+    // slightly worse for forward and dgrad, which keep the direct stores)
+    if (MODE != MODE_ROWS && !p.out_f32 && !p.accumulate)
+      store_tile_lds<MODE, F16>(p, t, acc, wm, wn, lane, lds);
+    else
+      store_tile<MODE, F16>(p, t, acc, wm, wn, lane);
   };
 
   // whole tiles, round after round; in row mode the last round may be split

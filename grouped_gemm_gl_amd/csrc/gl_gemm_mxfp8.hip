@@ -138,7 +138,12 @@ __global__ __launch_bounds__(kThreads) void gemm_mxfp8_kernel(Params p) {
       wait_lgkm0();
       __builtin_amdgcn_s_barrier();
     }
-    store_tile<MODE>(p, t, acc, wm, wn, lane);
+    // the wgrad's short contractions make its 1 GiB output the larger cost: there
+    // the tile goes out through LDS as whole lines
+    if (MODE != MODE_ROWS && !p.out_f32 && !p.accumulate)
+      store_tile_lds<MODE, false>(p, t, acc, wm, wn, lane, lds);
+    else
+      store_tile<MODE>(p, t, acc, wm, wn, lane);
   }
 }
 

@@ -41,6 +41,15 @@ constexpr int kKcontrUnits = 64;  // one padded 128-code contraction tile, in 2-
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
 #define GL_LDS __attribute__((address_space(3)))
+// Global memory, spelled out: a pointer the compiler cannot trace to a kernel
+// argument (one taken from a per-group pointer array) would otherwise be accessed
+// with flat instructions, which also count in lgkmcnt -- and the next tile's first
+// wait for its LDS reads would then wait for the previous tile's output stores.
+#if defined(__HIP_DEVICE_COMPILE__)
+#define GL_GLOBAL __attribute__((address_space(1)))
+#else
+#define GL_GLOBAL  // the host pass only checks these device bodies
+#endif
 
 struct Params {
   const uint16_t *A;
@@ -191,28 +200,31 @@ __device__ __forceinline__ bf16x8_t frag_mnmaj(const char *st, int col0, int ks,
 // Stores 4 consecutive output columns of one row: optional bias (per output
 // column, of the output's type), optional accumulate into the existing values.
 // 16-bit outputs are bf16, or fp16 when F16.
+// Addresses arrive as integers: a cast of a generic pointer to the global address
+// space can be folded back to a flat access when the pointer is a select of a
+// kernel argument and a loaded one; an integer cannot.
 template <bool F16>
-__device__ __forceinline__ void store4(char *cbase, int64_t row, int64_t ldc, int64_t col, const char *bias_g,
+__device__ __forceinline__ void store4(uintptr_t cbase, int64_t row, int64_t ldc, int64_t col, uintptr_t bias_g,
                                       int out_f32, int accumulate, float v0, float v1, float v2, float v3) {
   if (bias_g) {
     if (out_f32) {
-      const float4 bv = *(const float4 *)(bias_g + col * 4);
+      const float4 bv = *(const GL_GLOBAL float4 *)(bias_g + col * 4);
       v0 += bv.x; v1 += bv.y; v2 += bv.z; v3 += bv.w;
     } else {
-      const uint2 bv = *(const uint2 *)(bias_g + col * 2);
+      const uint2 bv = *(const GL_GLOBAL uint2 *)(bias_g + col * 2);
       v0 += h16_to_f32<F16>(bv.x & 0xffff); v1 += h16_to_f32<F16>(bv.x >> 16);
       v2 += h16_to_f32<F16>(bv.y & 0xffff); v3 += h16_to_f32<F16>(bv.y >> 16);
     }
   }
   if (out_f32) {
-    float4 *dst = (float4 *)(cbase + (row * ldc + col) * 4);
+    GL_GLOBAL float4 *dst = (GL_GLOBAL float4 *)(cbase + (row * ldc + col) * 4);
     if (accumulate) {
       const float4 o = *dst;
       v0 += o.x; v1 += o.y; v2 += o.z; v3 += o.w;
     }
     *dst = make_float4(v0, v1, v2, v3);
   } else {
-    uint2 *dst = (uint2 *)(cbase + (row * ldc + col) * 2);
+    GL_GLOBAL uint2 *dst = (GL_GLOBAL uint2 *)(cbase + (row * ldc + col) * 2);
     if (accumulate) {
       const uint2 o = *dst;
       v0 += h16_to_f32<F16>(o.x & 0xffff); v1 += h16_to_f32<F16>(o.x >> 16);
@@ -334,8 +346,8 @@ __device__ __forceinline__ void db_stage(const char *st, float *dbl) {
   *slot = a;
 }
 
-__device__ __forceinline__ char *db_row(const Params &p, int g) {
-  return p.db ? (char *)p.db + (int64_t)g * p.rows_i * (p.db_f32 ? 4 : 2) : (char *)p.db_ptrs[g];
+__device__ __forceinline__ uintptr_t db_row(const Params &p, int g) {
+  return p.db ? (uintptr_t)p.db + (uintptr_t)((int64_t)g * p.rows_i * (p.db_f32 ? 4 : 2)) : (uintptr_t)p.db_ptrs[g];
 }
 
 // Adds the kDbGroups partials of each column and stores db[g][n tile]; whole workgroup.
@@ -347,12 +359,12 @@ __device__ __forceinline__ void store_bgrad(const Params &p, const Tile &t, cons
     float v = 0.f;
 #pragma unroll
     for (int rg = 0; rg < kDbGroups; ++rg) v += dbl[rg * 256 + col];
-    char *row = db_row(p, t.g);
+    const uintptr_t row = db_row(p, t.g);
     const int64_t n = (int64_t)t.it * kBM + col;
     if (p.db_f32)
-      ((float *)row)[n] = v;
+      ((GL_GLOBAL float *)row)[n] = v;
     else
-      ((uint16_t *)row)[n] = f32_to_h16<F16>(v);
+      ((GL_GLOBAL uint16_t *)row)[n] = f32_to_h16<F16>(v);
   }
   __syncthreads();  // the partials area is free for the next tile
 }
@@ -361,12 +373,12 @@ __device__ __forceinline__ void store_bgrad(const Params &p, const Tile &t, cons
 __device__ __forceinline__ void store_bgrad_zero(const Params &p, const Tile &t) {
   const int col = threadIdx.x;
   if (col < t.a_rv) {
-    char *row = db_row(p, t.g);
+    const uintptr_t row = db_row(p, t.g);
     const int64_t n = (int64_t)t.it * kBM + col;
     if (p.db_f32)
-      ((float *)row)[n] = 0.f;
+      ((GL_GLOBAL float *)row)[n] = 0.f;
     else
-      ((uint16_t *)row)[n] = 0;
+      ((GL_GLOBAL uint16_t *)row)[n] = 0;
   }
 }
 
@@ -414,8 +426,8 @@ __device__ __forceinline__ bool split_finish(const WsView &ws, int u, int part, 
                                              int *flag) {
   const int tid = threadIdx.x;
   constexpr size_t kSlotF4 = kPartialBytes / 16;
-  float4 *slots = (float4 *)ws.split_part + (size_t)u * S * kSlotF4;
-  float4 *mine = slots + (size_t)part * kSlotF4;
+  GL_GLOBAL float4 *slots = (GL_GLOBAL float4 *)ws.split_part + (size_t)u * S * kSlotF4;
+  GL_GLOBAL float4 *mine = slots + (size_t)part * kSlotF4;
 #pragma unroll
   for (int ii = 0; ii < kNI; ++ii)
 #pragma unroll
@@ -437,7 +449,7 @@ __device__ __forceinline__ bool split_finish(const WsView &ws, int u, int part, 
   if (!__builtin_amdgcn_readfirstlane(*flag)) return false;
   __threadfence();  // acquire: every part's partial
   for (int s = 0; s < S; ++s) {
-    const float4 *src = slots + (size_t)s * kSlotF4;
+    const GL_GLOBAL float4 *src = slots + (size_t)s * kSlotF4;
 #pragma unroll
     for (int ii = 0; ii < kNI; ++ii)
 #pragma unroll
@@ -486,12 +498,74 @@ __device__ __forceinline__ void store_tile(const Params &p, const Tile &t, const
       for (int q4 = 0; q4 < 4; ++q4) {
         const int jl = wn * kWTN + jj * 32 + q4 * 8 + (lane >> 5) * 4;
         if (jl >= t.b_rv) continue;
-        store4<F16>(cbase, row, p.ldc, (int64_t)t.jt * kBN + jl, bias_g, p.out_f32, p.accumulate, acc[ii][jj][q4 * 4 + 0],
+        store4<F16>((uintptr_t)cbase, row, p.ldc, (int64_t)t.jt * kBN + jl, (uintptr_t)bias_g, p.out_f32, p.accumulate,
+                    acc[ii][jj][q4 * 4 + 0],
                acc[ii][jj][q4 * 4 + 1], acc[ii][jj][q4 * 4 + 2], acc[ii][jj][q4 * 4 + 3]);
       }
     }
   }
 }
+
+// 16-bit output without accumulate, staged through the idle stage ring so that
+// every store instruction writes whole cache lines.  Written directly, each store
+// instruction would touch 32 rows with 16 bytes each, and every 128-byte line of the
+// output would be assembled in L2 from 8 partial writes; on the MXFP8 wgrad (short
+// contractions, a 1 GiB output) that epilogue took half the kernel's time.
+// The tile goes to LDS as [256 rows][512 B] (16-byte slot s of row r at slot
+// s ^ (r % 32), so the 32 rows one write instruction touches spread over the
+// banks), then each wave stores 2 rows x 512 B per instruction.  Whole workgroup;
+// needs 128 KiB of `lds`, which no wave may still be reading on entry.
+template <int MODE, bool F16>
+__device__ __forceinline__ void store_tile_lds(const Params &p, const Tile &t, const f32x16_t (&acc)[kNI][kNJ],
+                                               int wm, int wn, int lane, char *lds) {
+  uintptr_t cbase;
+  int64_t row0;
+  if (MODE == MODE_ROWS) {
+    cbase = (uintptr_t)p.C;
+    row0 = t.g_off + (int64_t)t.it * kBM;
+  } else {
+    cbase = p.C ? (uintptr_t)p.C + (uintptr_t)((int64_t)t.g * p.c_gstride * 2) : (uintptr_t)p.C_ptrs[t.g];
+    row0 = (int64_t)t.it * kBM;
+  }
+  uintptr_t bias_g = 0;
+  if (p.bias) bias_g = (uintptr_t)p.bias + (uintptr_t)((int64_t)t.g * p.cols_j * 2);
+  else if (p.bias_ptrs) bias_g = (uintptr_t)p.bias_ptrs[t.g];
+  __syncthreads();  // a split tile's arrival flag sits in the ring's first word
+#pragma unroll
+  for (int ii = 0; ii < kNI; ++ii) {
+    const int il = wm * kWTM + ii * 32 + (lane & 31);
+#pragma unroll
+    for (int jj = 0; jj < kNJ; ++jj) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int jl = wn * kWTN + jj * 32 + q4 * 8 + (lane >> 5) * 4;
+        float v0 = acc[ii][jj][q4 * 4 + 0], v1 = acc[ii][jj][q4 * 4 + 1];
+        float v2 = acc[ii][jj][q4 * 4 + 2], v3 = acc[ii][jj][q4 * 4 + 3];
+        if (bias_g && jl < t.b_rv) {
+          const uint2 bv = *(const GL_GLOBAL uint2 *)(bias_g + ((int64_t)t.jt * kBN + jl) * 2);
+          v0 += h16_to_f32<F16>(bv.x & 0xffff); v1 += h16_to_f32<F16>(bv.x >> 16);
+          v2 += h16_to_f32<F16>(bv.y & 0xffff); v3 += h16_to_f32<F16>(bv.y >> 16);
+        }
+        const int slot = jl >> 3, half = (jl >> 2) & 1;
+        *(uint2 *)(lds + il * 512 + ((slot ^ (il & 31)) << 4) + half * 8) =
+            make_uint2((uint32_t)f32_to_h16<F16>(v0) | ((uint32_t)f32_to_h16<F16>(v1) << 16),
+                       (uint32_t)f32_to_h16<F16>(v2) | ((uint32_t)f32_to_h16<F16>(v3) << 16));
+      }
+    }
+  }
+  __syncthreads();
+  const int wave = threadIdx.x >> 6, s = lane & 31;
+#pragma unroll 4
+  for (int it = 0; it < kBM / kWaves / 2; ++it) {
+    const int r = wave * (kBM / kWaves) + it * 2 + (lane >> 5);
+    if (r < t.a_rv && s * 8 < t.b_rv) {
+      const uint4 v = *(const uint4 *)(lds + r * 512 + ((s ^ (r & 31)) << 4));
+      *(GL_GLOBAL uint4 *)(cbase + ((row0 + r) * p.ldc + (int64_t)t.jt * kBN + s * 8) * 2) = v;
+    }
+  }
+  __syncthreads();  // the ring is refilled by the next tile
+}
+static_assert(kS * kStageBytes >= kBM * kBN * 2, "the staged epilogue needs the whole tile in the ring");
 
 // Compute units of the current device (one persistent workgroup per CU).
 inline int num_cus() {
