@@ -148,6 +148,15 @@ class EventTimer:
     def mean_ms(self):
         return {k: sum(s.elapsed_time(e) for s, e in v) / len(v) for k, v in self.pairs.items()}
 
+    def spread_ms(self):
+        """median, p10 and p90 of each pass's samples (nearest-rank)."""
+        out = {}
+        for k, v in self.pairs.items():
+            xs = sorted(s.elapsed_time(e) for s, e in v)
+            pick = lambda q: xs[min(len(xs) - 1, max(0, int(round(q * (len(xs) - 1)))))]
+            out[k] = {"median": round(pick(0.5), 4), "p10": round(pick(0.1), 4), "p90": round(pick(0.9), 4)}
+        return out
+
 
 def cpu_baseline(wl, m, x, w, b, dy, min_s=10.0):
     """The oracle, as it stands, on whole groups of the same workload, cycling
@@ -227,19 +236,21 @@ def bench_bf16(torch, gl, synth, steps, warmup):
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     # per-kernel durations on the launch stream
-    for _ in range(max(3, min(steps, 10))):
+    for _ in range(max(3, min(steps, 30))):
         step(timer)
         # for reference, outside the step: wgrad and the bias grad as separate launches
         timer.run("wgrad_alone", lambda: gl.gl_wgrad(xd, dyd, dw, ws))
         timer.run("bgrad_alone", lambda: gl.gl_bgrad(dyd, db, ws))
     torch.cuda.synchronize()
     per = timer.mean_ms()
+    spread = timer.spread_ms()
     flops_pass = 2.0 * T * N * K
     ms_step = elapsed * 1e3 / steps
     value = 3 * flops_pass / (ms_step * 1e-3) / 1e12
     passes = {}
     for k, ms in per.items():
-        d = {"ms": round(ms, 4)}
+        d = {"ms": round(ms, 4), "ms_median": spread[k]["median"], "ms_p10": spread[k]["p10"],
+             "ms_p90": spread[k]["p90"]}
         if k in GEMM_PASSES or k == "wgrad_alone":
             d["tflops"] = round(flops_pass / (ms * 1e-3) / 1e12, 2)
             d["pct_bf16_peak"] = round(100 * d["tflops"] / PEAK_BF16_TFLOPS, 2)
@@ -384,7 +395,7 @@ def bench_mlp(torch, gl, steps, warmup):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-mxfp8", action="store_true")
     ap.add_argument("--no-mlp", action="store_true")
