@@ -236,12 +236,21 @@ def bench_bf16(torch, gl, synth, steps, warmup):
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     # per-kernel durations on the launch stream
+    queue = gl.WgradQueue()
     for _ in range(max(3, min(steps, 30))):
         step(timer)
-        # for reference, outside the step: wgrad and the bias grad as separate launches
+        # for reference, outside the step: wgrad and the bias grad as separate launches,
+        # and the step's wgrad put in the deferred-wgrad queue, then run from it
         timer.run("wgrad_alone", lambda: gl.gl_wgrad(xd, dyd, dw, ws))
         timer.run("bgrad_alone", lambda: gl.gl_bgrad(dyd, db, ws))
+        queue.put(xd, dyd, dw, ws, db=db)
+        timer.run("wgrad_bgrad_deferred", queue.flush)
     torch.cuda.synchronize()
+    t_put = time.perf_counter()
+    for _ in range(200):
+        queue.put(xd, dyd, dw, ws, db=db)
+    put_us = (time.perf_counter() - t_put) / 200 * 1e6
+    queue.clear()
     per = timer.mean_ms()
     spread = timer.spread_ms()
     flops_pass = 2.0 * T * N * K
@@ -251,7 +260,7 @@ def bench_bf16(torch, gl, synth, steps, warmup):
     for k, ms in per.items():
         d = {"ms": round(ms, 4), "ms_median": spread[k]["median"], "ms_p10": spread[k]["p10"],
              "ms_p90": spread[k]["p90"]}
-        if k in GEMM_PASSES or k == "wgrad_alone":
+        if k in GEMM_PASSES or k in ("wgrad_alone", "wgrad_bgrad_deferred"):
             d["tflops"] = round(flops_pass / (ms * 1e-3) / 1e12, 2)
             d["pct_bf16_peak"] = round(100 * d["tflops"] / PEAK_BF16_TFLOPS, 2)
         if k == "bgrad_alone":
@@ -260,6 +269,8 @@ def bench_bf16(torch, gl, synth, steps, warmup):
             d["pct_hbm"] = round(100 * gbs / PEAK_HBM_GBS, 2)
         if k == "offsets":
             d["us"] = round(ms * 1e3, 2)
+        if k == "wgrad_bgrad_deferred":
+            d["host_put_us"] = round(put_us, 2)
         passes[k] = d
     dom = max(GEMM_PASSES, key=lambda k: per[k])
     achieved = flops_pass / (per[dom] * 1e-3) / 1e12

@@ -13,6 +13,7 @@ array of their addresses is built and handed over.
 """
 from __future__ import annotations
 
+import collections
 import ctypes
 import os
 from typing import Optional, Sequence, Union
@@ -22,7 +23,7 @@ import torch
 __all__ = [
     "GL_F32", "GL_BF16", "GL_F16", "GL_E4M3", "GLError", "library_path", "load",
     "gl_workspace_size", "new_workspace", "gl_offsets", "gl_read_status", "gl_forward",
-    "gl_dgrad", "gl_wgrad", "gl_bgrad", "gl_group_quantize_mxfp8", "gl_version",
+    "gl_dgrad", "gl_wgrad", "gl_bgrad", "gl_group_quantize_mxfp8", "gl_version", "WgradQueue",
 ]
 
 GL_F32, GL_BF16, GL_F16, GL_E4M3 = 0, 1, 2, 3
@@ -75,6 +76,14 @@ def load():
         "gl_quantize_mxfp8_weights": (I, [P, I, I64, I64, P, P, P, P, P, P]),
         "gl_dgrad_mxfp8": (I, [I, I64, I64, I64, I, P, P, P, P, P, I64, P, P]),
         "gl_wgrad_mxfp8": (I, [I, I64, I64, I64, I, P, P, P, P, I64, P, P, I, P, P]),
+        "gl_wgrad_queue_create": (I, [ctypes.POINTER(P)]),
+        "gl_wgrad_queue_destroy": (I, [P]),
+        "gl_wgrad_queue_put": (I, [P, I, I64, I64, I64, I, I, I, P, P, P, P, I, P, P, P]),
+        "gl_wgrad_queue_put_mxfp8": (I, [P, I, I64, I64, I64, I, P, P, P, P, I64, P, P, I, P]),
+        "gl_wgrad_queue_size": (I, [P]),
+        "gl_wgrad_queue_run_next": (I, [P, P]),
+        "gl_wgrad_queue_flush": (I, [P, P]),
+        "gl_wgrad_queue_clear": (I, [P]),
         "gl_last_error": (ctypes.c_char_p, []),
         "gl_version": (ctypes.c_char_p, []),
     }
@@ -113,13 +122,28 @@ def _dtype(t: Tensor) -> int:
     return _DT[t.dtype]
 
 
-def _grouped(g: Optional[Grouped], device):
-    """(stacked pointer, pointer-array pointer, keep-alive) for a stacked tensor or a list."""
+def _record(tensors, stream):
+    """Ties tensors' memory to a caller-given stream: torch's caching allocator
+    then waits for the work queued on that stream before it reuses the memory
+    (without it, a pointer array freed right after an enqueue on another stream
+    could be handed out again before the kernel has read it)."""
+    if stream is None:
+        return
+    s = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(_stream(stream))
+    for t in tensors:
+        if isinstance(t, Tensor) and t.is_cuda:
+            t.record_stream(s)
+
+
+def _grouped(g: Optional[Grouped], device, stream=None):
+    """(stacked pointer, pointer-array pointer, keep-alive) for a stacked tensor or a
+    list; the device pointer array of a list is tied to ``stream`` (see _record)."""
     if g is None:
         return None, None, None
     if isinstance(g, Tensor):
         return _ptr(g), None, None
     ptrs = torch.tensor([_ptr(t) or 0 for t in g], dtype=torch.int64, device=device)
+    _record([ptrs], stream)
     return None, ptrs.data_ptr(), (ptrs, list(g))
 
 
@@ -180,9 +204,9 @@ def gl_forward(x: Tensor, w: Grouped, y: Tensor, workspace: Tensor, *, bias: Opt
     if bias is not None and _first(bias).dtype != y.dtype:
         raise ValueError("bias dtype must equal the output dtype")
     dev = x.device
-    wp, wpp, keep_w = _grouped(w, dev)
-    bp, bpp, keep_b = _grouped(bias, dev)
-    sp, spp, keep_s = _grouped(w_scale, dev)
+    wp, wpp, keep_w = _grouped(w, dev, stream)
+    bp, bpp, keep_b = _grouped(bias, dev, stream)
+    sp, spp, keep_s = _grouped(w_scale, dev, stream)
     _check(load().gl_forward(G, K, N, T, _dtype(x), _dtype(y), _ptr(x), _ptr(x_scale), wp, wpp, sp, spp, bp, bpp,
                              _ptr(y), y.shape[0], _ptr(workspace), _stream(stream)))
     del keep_w, keep_b, keep_s
@@ -199,7 +223,7 @@ def gl_dgrad(dy: Tensor, w: Grouped, dx: Tensor, workspace: Tensor, stream=None)
         raise ValueError(f"dy must be [T, {N}], got {tuple(dy.shape)}")
     if dx.dim() != 2 or dx.shape[1] != K or dx.dtype != dy.dtype or w0.dtype != dy.dtype:
         raise ValueError("dx must be [rows >= T, K] and dy, w, dx must share one dtype")
-    wp, wpp, keep = _grouped(w, dy.device)
+    wp, wpp, keep = _grouped(w, dy.device, stream)
     _check(load().gl_dgrad(G, K, N, T, _dtype(dy), _ptr(dy), wp, wpp, _ptr(dx), dx.shape[0], _ptr(workspace),
                            _stream(stream)))
     del keep
@@ -215,7 +239,7 @@ def gl_wgrad(x: Tensor, dy: Tensor, dw: Grouped, workspace: Tensor, *, accumulat
     T = x.shape[0]
     if x.shape != (T, K) or dy.shape != (T, N) or x.dtype != dy.dtype:
         raise ValueError("x must be [T, K] and dy [T, N] with one dtype")
-    dp, dpp, keep = _grouped(dw, x.device)
+    dp, dpp, keep = _grouped(dw, x.device, stream)
     _check(load().gl_wgrad(G, K, N, T, _dtype(x), _dtype(d0), _ptr(x), _ptr(dy), dp, dpp, int(bool(accumulate)),
                            _ptr(workspace), _stream(stream)))
     del keep
@@ -235,8 +259,8 @@ def gl_wgrad_bgrad(x: Tensor, dy: Tensor, dw: Grouped, db: Grouped, workspace: T
         raise ValueError("x must be [T, K] and dy [T, N] with one dtype")
     if b0.shape[-1] != N or (isinstance(db, Tensor) and db.shape != (G, N)):
         raise ValueError("db must be [G, N] or G tensors [N]")
-    dp, dpp, keep = _grouped(dw, x.device)
-    bp, bpp, keep_b = _grouped(db, x.device)
+    dp, dpp, keep = _grouped(dw, x.device, stream)
+    bp, bpp, keep_b = _grouped(db, x.device, stream)
     _check(load().gl_wgrad_bgrad(G, K, N, T, _dtype(x), _dtype(d0), _dtype(b0), _ptr(x), _ptr(dy), dp, dpp,
                                  int(bool(accumulate)), bp, bpp, _ptr(workspace), _stream(stream)))
     del keep, keep_b
@@ -250,7 +274,7 @@ def gl_bgrad(dy: Tensor, db: Grouped, workspace: Tensor, stream=None) -> Grouped
     d0 = db[0] if not isinstance(db, Tensor) else db
     if d0.shape[-1] != N or d0.dtype != dy.dtype:
         raise ValueError("db must have dy's column count and dtype")
-    dp, dpp, keep = _grouped(db, dy.device)
+    dp, dpp, keep = _grouped(db, dy.device, stream)
     _check(load().gl_bgrad(G, N, dy.shape[0], _dtype(dy), _ptr(dy), dp, dpp, _ptr(workspace), _stream(stream)))
     del keep
     return db
@@ -363,10 +387,10 @@ def gl_grouped_mlp_forward(x: Tensor, w1: Grouped, w2: Grouped, h: Tensor, a: Te
     T = x.shape[0]
     if x.shape != (T, K) or h.shape != (T, F2) or a.shape != (T, F2 // 2) or y.dim() != 2 or y.shape[1] != N:
         raise ValueError("shapes: x [T, K], w1 [G, 2F, K], w2 [G, N, F], h [T, 2F], a [T, F], y [rows >= T, N]")
-    p1, pp1, k1 = _grouped(w1, x.device)
-    p2, pp2, k2 = _grouped(w2, x.device)
-    q1, qq1, k3 = _grouped(b1, x.device)
-    q2, qq2, k4 = _grouped(b2, x.device)
+    p1, pp1, k1 = _grouped(w1, x.device, stream)
+    p2, pp2, k2 = _grouped(w2, x.device, stream)
+    q1, qq1, k3 = _grouped(b1, x.device, stream)
+    q2, qq2, k4 = _grouped(b2, x.device, stream)
     _check(load().gl_grouped_mlp_forward(G, K, F2 // 2, N, T, _dtype(x), _ptr(x), p1, pp1, q1, qq1, p2, pp2, q2, qq2,
                                          _ptr(h), _ptr(a), _ptr(y), y.shape[0], _ptr(workspace), _stream(stream)))
     del k1, k2, k3, k4
@@ -388,7 +412,7 @@ def gl_grouped_mlp_backward(x: Tensor, w1: Grouped, w2: Grouped, h: Tensor, a: T
     keep = []
     ptr = {}
     for name, g in (("w1", w1), ("w2", w2), ("dw1", dw1), ("dw2", dw2), ("db1", db1), ("db2", db2)):
-        p, pp, k = _grouped(g, x.device)
+        p, pp, k = _grouped(g, x.device, stream)
         ptr[name] = (p, pp)
         keep.append(k)
     _check(load().gl_grouped_mlp_backward(G, K, F2 // 2, N, T, _dtype(x), _dtype(_first(dw1)), _ptr(x), *ptr["w1"],
@@ -420,9 +444,109 @@ def gl_wgrad_mxfp8(dy_t: Tensor, dy_t_scale: Tensor, x_t: Tensor, x_t_scale: Ten
     K = x_t.shape[0]
     if x_t.shape != (K, ld) or tuple(d0.shape[-2:]) != (N, K):
         raise ValueError("x_t must be [K, ld] and dw [G, N, K] or G tensors [N, K]")
-    dp, dpp, keep = _grouped(dw, dy_t.device)
+    dp, dpp, keep = _grouped(dw, dy_t.device, stream)
     _check(load().gl_wgrad_mxfp8(G, K, N, int(total_rows), _dtype(d0), _ptr(dy_t), _ptr(dy_t_scale), _ptr(x_t),
                                  _ptr(x_t_scale), ld, dp, dpp, int(bool(accumulate)), _ptr(workspace),
                                  _stream(stream)))
     del keep
     return dw
+
+
+def _tensors(obj):
+    """Every tensor inside nested tuples / lists."""
+    if isinstance(obj, Tensor):
+        yield obj
+    elif isinstance(obj, (tuple, list)):
+        for o in obj:
+            yield from _tensors(o)
+
+
+class WgradQueue:
+    """Deferred grouped weight gradients (the ``gl_wgrad_queue_*`` entry points).
+
+    ``put`` / ``put_mxfp8`` take the arguments of ``gl_wgrad_bgrad`` (``db=None``:
+    plain ``gl_wgrad``) / ``gl_wgrad_mxfp8``, check them in full and record the
+    call without running it; ``run_next`` launches the oldest recorded call and
+    ``flush`` all of them, in put order.  The queue holds a reference to every
+    tensor of a recorded call until it has been launched, and ties their memory
+    to the stream it runs on; the workspace must still hold the same splits' offsets.
+    """
+
+    def __init__(self):
+        self._q = ctypes.c_void_p()
+        _check(load().gl_wgrad_queue_create(ctypes.byref(self._q)))
+        self._held = collections.deque()
+
+    def __len__(self) -> int:
+        n = load().gl_wgrad_queue_size(self._q)
+        if n < 0:
+            _check(n)
+        return n
+
+    def put(self, x: Tensor, dy: Tensor, dw: Grouped, workspace: Tensor, *, db: Optional[Grouped] = None,
+            accumulate: bool = False) -> None:
+        G = dw.shape[0] if isinstance(dw, Tensor) else len(dw)
+        d0 = _first(dw)
+        N, K = d0.shape[-2], d0.shape[-1]
+        T = x.shape[0]
+        if x.shape != (T, K) or dy.shape != (T, N) or x.dtype != dy.dtype:
+            raise ValueError("x must be [T, K] and dy [T, N] with one dtype")
+        db_dtype = GL_F32
+        if db is not None:
+            b0 = _first(db)
+            if b0.shape[-1] != N or (isinstance(db, Tensor) and db.shape != (G, N)):
+                raise ValueError("db must be [G, N] or G tensors [N]")
+            db_dtype = _dtype(b0)
+        dp, dpp, keep = _grouped(dw, x.device)
+        bp, bpp, keep_b = _grouped(db, x.device)
+        _check(load().gl_wgrad_queue_put(self._q, G, K, N, T, _dtype(x), _dtype(d0), db_dtype, _ptr(x), _ptr(dy), dp,
+                                         dpp, int(bool(accumulate)), bp, bpp, _ptr(workspace)))
+        self._held.append((x, dy, dw, db, workspace, keep, keep_b))
+
+    def put_mxfp8(self, dy_t: Tensor, dy_t_scale: Tensor, x_t: Tensor, x_t_scale: Tensor, dw: Grouped,
+                  workspace: Tensor, total_rows: int, *, accumulate: bool = False) -> None:
+        G = dw.shape[0] if isinstance(dw, Tensor) else len(dw)
+        d0 = _first(dw)
+        N, ld = dy_t.shape
+        K = x_t.shape[0]
+        if x_t.shape != (K, ld) or tuple(d0.shape[-2:]) != (N, K):
+            raise ValueError("x_t must be [K, ld] and dw [G, N, K] or G tensors [N, K]")
+        dp, dpp, keep = _grouped(dw, dy_t.device)
+        _check(load().gl_wgrad_queue_put_mxfp8(self._q, G, K, N, int(total_rows), _dtype(d0), _ptr(dy_t),
+                                               _ptr(dy_t_scale), _ptr(x_t), _ptr(x_t_scale), ld, dp, dpp,
+                                               int(bool(accumulate)), _ptr(workspace)))
+        self._held.append((dy_t, dy_t_scale, x_t, x_t_scale, dw, workspace, keep))
+
+    def _launching(self, held, stream):
+        _record(list(_tensors(held)), torch.cuda.current_stream() if stream is None else stream)
+
+    def run_next(self, stream=None) -> None:
+        """Launch the oldest recorded call on ``stream`` (torch's current one by default)."""
+        if not self._held:
+            return
+        self._launching(self._held.popleft(), stream)
+        _check(load().gl_wgrad_queue_run_next(self._q, _stream(stream)))
+
+    def flush(self, stream=None) -> None:
+        """Launch every recorded call, in put order."""
+        held, self._held = list(self._held), collections.deque()
+        for h in held:
+            self._launching(h, stream)
+        _check(load().gl_wgrad_queue_flush(self._q, _stream(stream)))
+
+    def clear(self) -> None:
+        """Drop the recorded calls without running them."""
+        _check(load().gl_wgrad_queue_clear(self._q))
+        self._held.clear()
+
+    def close(self) -> None:
+        if self._q:
+            load().gl_wgrad_queue_destroy(self._q)
+            self._q = ctypes.c_void_p()
+        self._held.clear()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -9,6 +9,8 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <deque>
+#include <new>
 
 #include "../../include/grouped_linear.h"
 #include "gl_common.hpp"
@@ -465,10 +467,11 @@ int gl_dgrad_mxfp8(int num_groups, int64_t in_features, int64_t out_features, in
                     "gl_dgrad_mxfp8");
 }
 
-int gl_wgrad_mxfp8(int num_groups, int64_t in_features, int64_t out_features, int64_t total_rows, gl_dtype out_dtype,
-                   const uint8_t *dy_t, const uint8_t *dy_t_scale, const uint8_t *x_t, const uint8_t *x_t_scale,
-                   int64_t ld, void *dw, void *const *dw_ptrs, int accumulate, const void *workspace,
-                   hipStream_t stream) {
+namespace {
+int wgrad_mxfp8_impl(int num_groups, int64_t in_features, int64_t out_features, int64_t total_rows,
+                     gl_dtype out_dtype, const uint8_t *dy_t, const uint8_t *dy_t_scale, const uint8_t *x_t,
+                     const uint8_t *x_t_scale, int64_t ld, void *dw, void *const *dw_ptrs, int accumulate,
+                     const void *workspace, hipStream_t stream, bool launch = true) {
   const int G = num_groups;
   const int64_t K = in_features, N = out_features, T = total_rows;
   GL_TRY(check_sizes(G, K, N, T));
@@ -484,10 +487,24 @@ int gl_wgrad_mxfp8(int num_groups, int64_t in_features, int64_t out_features, in
   if (!dy_t || !x_t || !dy_t_scale || !x_t_scale) return fail(GL_ERR_ARG, "codes or scales are NULL");
   if (!aligned16(dy_t) || !aligned16(x_t) || ((uintptr_t)dy_t_scale & 3u) || ((uintptr_t)x_t_scale & 3u))
     return fail(GL_ERR_ARG, "codes must be 16-byte and scales 4-byte aligned");
+  if (!launch) return ok();
   return hip_result(gl::launch_wgrad_mxfp8(G, K, N, T, dy_t, dy_t_scale, x_t, x_t_scale, ld, dw, dw_ptrs,
                                            out_dtype == GL_F32, accumulate, workspace, stream),
                     "gl_wgrad_mxfp8");
 }
+}  // namespace
+
+extern "C" {
+
+int gl_wgrad_mxfp8(int num_groups, int64_t in_features, int64_t out_features, int64_t total_rows, gl_dtype out_dtype,
+                   const uint8_t *dy_t, const uint8_t *dy_t_scale, const uint8_t *x_t, const uint8_t *x_t_scale,
+                   int64_t ld, void *dw, void *const *dw_ptrs, int accumulate, const void *workspace,
+                   hipStream_t stream) {
+  return wgrad_mxfp8_impl(num_groups, in_features, out_features, total_rows, out_dtype, dy_t, dy_t_scale, x_t,
+                          x_t_scale, ld, dw, dw_ptrs, accumulate, workspace, stream);
+}
+
+}  // extern "C"
 
 // ------------------------------------------------------------------ grouped MLP --
 
@@ -581,6 +598,157 @@ int gl_grouped_mlp_backward(int num_groups, int64_t in_features, int64_t ffn_fea
   if (T > 0) GL_TRY(hip_result(gl::launch_swiglu_bwd(sw_el(dtype), T, F, h, da, dh, stream), "gl_grouped_mlp_backward"));
   GL_TRY(fc1_wgrad(true));
   return fc1_dgrad(true);
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------ deferred wgrad --
+//
+// The layer of page "transformer_engine/pytorch/ops/basic/grouped_linear.py" can
+// delay its weight-gradient GEMMs (delay_wgrad_compute): the backward stores the
+// wgrad call with its operands, and backward_dw later takes the oldest stored call
+// and runs it.  Here the stored call is a host record of the C arguments, checked
+// in full when it is put, so running it can only fail in the HIP launch.
+
+struct gl_wgrad_queue {
+  struct Entry {
+    bool mx;  // gl_wgrad_mxfp8 form, else gl_wgrad / gl_wgrad_bgrad form
+    int G;
+    int64_t K, N, T;
+    gl_dtype in_dtype, out_dtype, db_dtype;
+    const void *x, *dy;
+    void *dw;
+    void *const *dw_ptrs;
+    int accumulate;
+    bool with_db;
+    void *db;
+    void *const *db_ptrs;
+    const uint8_t *dy_t, *dy_t_scale, *x_t, *x_t_scale;
+    int64_t ld;
+    const void *workspace;
+  };
+  std::deque<Entry> pending;
+};
+
+namespace {
+int run_entry(const gl_wgrad_queue::Entry &e, hipStream_t stream) {
+  if (e.mx)
+    return wgrad_mxfp8_impl(e.G, e.K, e.N, e.T, e.out_dtype, e.dy_t, e.dy_t_scale, e.x_t, e.x_t_scale, e.ld, e.dw,
+                            e.dw_ptrs, e.accumulate, e.workspace, stream);
+  return wgrad_impl(e.with_db ? "gl_wgrad_bgrad" : "gl_wgrad", e.G, e.K, e.N, e.T, e.in_dtype, e.out_dtype, e.x,
+                    e.dy, e.dw, e.dw_ptrs, e.accumulate, e.with_db, e.db_dtype, e.db, e.db_ptrs, e.workspace,
+                    stream);
+}
+}  // namespace
+
+extern "C" {
+
+int gl_wgrad_queue_create(gl_wgrad_queue **queue) {
+  if (!queue) return fail(GL_ERR_ARG, "queue is NULL");
+  *queue = new (std::nothrow) gl_wgrad_queue();
+  if (!*queue) return fail(GL_ERR_ARG, "out of host memory");
+  return ok();
+}
+
+int gl_wgrad_queue_destroy(gl_wgrad_queue *queue) {
+  delete queue;
+  return ok();
+}
+
+int gl_wgrad_queue_put(gl_wgrad_queue *queue, int num_groups, int64_t in_features, int64_t out_features,
+                       int64_t total_rows, gl_dtype in_dtype, gl_dtype out_dtype, gl_dtype db_dtype, const void *x,
+                       const void *dy, void *dw, void *const *dw_ptrs, int accumulate, void *db,
+                       void *const *db_ptrs, const void *workspace) {
+  if (!queue) return fail(GL_ERR_ARG, "queue is NULL");
+  gl_wgrad_queue::Entry e{};
+  e.mx = false;
+  e.G = num_groups;
+  e.K = in_features;
+  e.N = out_features;
+  e.T = total_rows;
+  e.in_dtype = in_dtype;
+  e.out_dtype = out_dtype;
+  e.db_dtype = db_dtype;
+  e.x = x;
+  e.dy = dy;
+  e.dw = dw;
+  e.dw_ptrs = dw_ptrs;
+  e.accumulate = accumulate;
+  e.with_db = db || db_ptrs;
+  e.db = db;
+  e.db_ptrs = db_ptrs;
+  e.workspace = workspace;
+  GL_TRY(wgrad_impl(e.with_db ? "gl_wgrad_bgrad" : "gl_wgrad", e.G, e.K, e.N, e.T, e.in_dtype, e.out_dtype, e.x,
+                    e.dy, e.dw, e.dw_ptrs, e.accumulate, e.with_db, e.db_dtype, e.db, e.db_ptrs, e.workspace,
+                    nullptr, false));
+  queue->pending.push_back(e);
+  return ok();
+}
+
+int gl_wgrad_queue_put_mxfp8(gl_wgrad_queue *queue, int num_groups, int64_t in_features, int64_t out_features,
+                             int64_t total_rows, gl_dtype out_dtype, const uint8_t *dy_t, const uint8_t *dy_t_scale,
+                             const uint8_t *x_t, const uint8_t *x_t_scale, int64_t ld, void *dw,
+                             void *const *dw_ptrs, int accumulate, const void *workspace) {
+  if (!queue) return fail(GL_ERR_ARG, "queue is NULL");
+  GL_TRY(wgrad_mxfp8_impl(num_groups, in_features, out_features, total_rows, out_dtype, dy_t, dy_t_scale, x_t,
+                          x_t_scale, ld, dw, dw_ptrs, accumulate, workspace, nullptr, false));
+  gl_wgrad_queue::Entry e{};
+  e.mx = true;
+  e.G = num_groups;
+  e.K = in_features;
+  e.N = out_features;
+  e.T = total_rows;
+  e.out_dtype = out_dtype;
+  e.dy_t = dy_t;
+  e.dy_t_scale = dy_t_scale;
+  e.x_t = x_t;
+  e.x_t_scale = x_t_scale;
+  e.ld = ld;
+  e.dw = dw;
+  e.dw_ptrs = dw_ptrs;
+  e.accumulate = accumulate;
+  e.workspace = workspace;
+  queue->pending.push_back(e);
+  return ok();
+}
+
+int gl_wgrad_queue_size(const gl_wgrad_queue *queue) {
+  if (!queue) return fail(GL_ERR_ARG, "queue is NULL");
+  return (int)queue->pending.size();
+}
+
+int gl_wgrad_queue_run_next(gl_wgrad_queue *queue, hipStream_t stream) {
+  if (!queue) return fail(GL_ERR_ARG, "queue is NULL");
+  if (queue->pending.empty()) return ok();
+  const gl_wgrad_queue::Entry e = queue->pending.front();
+  queue->pending.pop_front();
+  return run_entry(e, stream);
+}
+
+int gl_wgrad_queue_flush(gl_wgrad_queue *queue, hipStream_t stream) {
+  if (!queue) return fail(GL_ERR_ARG, "queue is NULL");
+  while (!queue->pending.empty()) {
+    const gl_wgrad_queue::Entry e = queue->pending.front();
+    queue->pending.pop_front();
+    const int rc = run_entry(e, stream);
+    if (rc != GL_OK) {
+      const size_t dropped = queue->pending.size();
+      queue->pending.clear();
+      if (dropped) {
+        char msg[sizeof(g_err)];
+        snprintf(msg, sizeof(msg), "%s (%zu later calls dropped)", g_err, dropped);
+        return fail(rc, "%s", msg);
+      }
+      return rc;
+    }
+  }
+  return ok();
+}
+
+int gl_wgrad_queue_clear(gl_wgrad_queue *queue) {
+  if (!queue) return fail(GL_ERR_ARG, "queue is NULL");
+  queue->pending.clear();
+  return ok();
 }
 
 }  // extern "C"

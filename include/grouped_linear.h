@@ -17,9 +17,10 @@
  *
  * Conventions shared by every entry point:
  *  - Every pointer argument is a DEVICE pointer owned by the caller, except the
- *    stream.  The library allocates nothing, keeps no pointer after return and
- *    never synchronises the host (gl_read_status is the one exception).  Work is
- *    enqueued on `stream` in call order.
+ *    stream and the deferred-wgrad queue handle.  The library allocates no device
+ *    memory, keeps no pointer after return (except the records of a deferred-wgrad
+ *    queue, until they run) and never synchronises the host (gl_read_status is the
+ *    one exception).  Work is enqueued on `stream` in call order.
  *  - Weights (and biases, wgrad outputs) come in one of two forms: a stacked
  *    buffer (`w`) or a DEVICE array of G per-group pointers (`w_ptrs`); exactly one
  *    of the two must be non-NULL (page "Improve device-init grouped linear module
@@ -358,6 +359,47 @@ int gl_grouped_mlp_backward(int num_groups, int64_t in_features, int64_t ffn_fea
                             void *const *dw1_ptrs, void *db1, void *const *db1_ptrs, void *dw2,
                             void *const *dw2_ptrs, void *db2, void *const *db2_ptrs, int accumulate,
                             const void *workspace, hipStream_t stream);
+
+/*
+ * Deferred weight gradients (page "transformer_engine/pytorch/ops/basic/
+ * grouped_linear.py", delay_wgrad_compute and backward_dw): the backward pass puts
+ * its wgrad call in a queue instead of running it, and a later call runs the
+ * oldest put call, so the weight-gradient GEMMs can be scheduled after the rest of
+ * the backward (for instance behind another layer's dgrad or a communication).
+ *
+ * A queue is a host object (host memory only, not thread-safe: one thread at a
+ * time).  gl_wgrad_queue_put takes the arguments of gl_wgrad_bgrad without the
+ * stream (db and db_ptrs both NULL: plain gl_wgrad, db_dtype ignored), and
+ * gl_wgrad_queue_put_mxfp8 those of gl_wgrad_mxfp8.  Every check of that entry
+ * point runs at put time, with the same errors; on an error nothing is queued.
+ * Nothing is launched and no device memory is read by a put.  The queue keeps the
+ * pointers: the caller keeps every buffer, pointer array and the workspace alive
+ * and unchanged until the call has run, and the workspace must still hold the
+ * offsets of the same splits (gl_offsets on it in between changes what runs).
+ *
+ * gl_wgrad_queue_run_next launches the oldest queued call on `stream` (nothing if
+ * the queue is empty); gl_wgrad_queue_flush launches all of them in put order.  A
+ * launched call leaves the queue whatever its result; if a launch fails, flush
+ * drops the calls after it and returns the error.  gl_wgrad_queue_size returns the
+ * number of queued calls (>= 0), gl_wgrad_queue_clear drops them without running,
+ * gl_wgrad_queue_destroy frees the queue (queued calls are dropped; NULL is a
+ * no-op).
+ */
+typedef struct gl_wgrad_queue gl_wgrad_queue;
+int gl_wgrad_queue_create(gl_wgrad_queue **queue);
+int gl_wgrad_queue_destroy(gl_wgrad_queue *queue);
+int gl_wgrad_queue_put(gl_wgrad_queue *queue, int num_groups, int64_t in_features, int64_t out_features,
+                       int64_t total_rows, gl_dtype in_dtype, gl_dtype out_dtype, gl_dtype db_dtype, const void *x,
+                       const void *dy, void *dw, void *const *dw_ptrs, int accumulate, void *db,
+                       void *const *db_ptrs, const void *workspace);
+int gl_wgrad_queue_put_mxfp8(gl_wgrad_queue *queue, int num_groups, int64_t in_features, int64_t out_features,
+                             int64_t total_rows, gl_dtype out_dtype, const uint8_t *dy_t, const uint8_t *dy_t_scale,
+                             const uint8_t *x_t, const uint8_t *x_t_scale, int64_t ld, void *dw,
+                             void *const *dw_ptrs, int accumulate, const void *workspace);
+int gl_wgrad_queue_size(const gl_wgrad_queue *queue);
+int gl_wgrad_queue_run_next(gl_wgrad_queue *queue, hipStream_t stream);
+int gl_wgrad_queue_flush(gl_wgrad_queue *queue, hipStream_t stream);
+int gl_wgrad_queue_clear(gl_wgrad_queue *queue);
 
 const char *gl_last_error(void);
 
