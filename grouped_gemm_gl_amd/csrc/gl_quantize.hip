@@ -190,6 +190,121 @@ __global__ __launch_bounds__(kQThreads) void quantize_mxfp8_colwise_kernel(
                           data, scale, ld);
 }
 
+// Group-mode columnwise MXFP8 by tiles of 128 rows x 64 columns, one workgroup
+// each: the tile is read with 16-byte row loads into LDS, each thread quantizes one
+// column's 32-row block from there, and the codes go back through LDS so that every
+// store instruction writes whole 128-byte lines of the transposed output (8 rows of
+// 128 codes per wave) and each output row gets its 4 scale bytes as one word.  A
+// 128-row tile is one of a group's padded 128-row tiles (the workspace's 128-row
+// prefix table), so it lies in one group; rows past the group's end read as zero.
+// Needs cols % 8 == 0 and a 4-byte aligned scale matrix; the per-thread kernel
+// above serves the other cases.  Tiles past the last group's padding are left
+// untouched.
+// 128-column tiles (256-byte row reads, two columns per thread) measured slower:
+// the larger LDS and register footprint costs more occupancy than they save.
+constexpr int kCtRows = 128, kCtCols = 64;
+constexpr int kCtCpt = kCtCols / 64;  // adjacent columns per thread in the quantize step
+
+__global__ __launch_bounds__(kQThreads) void quantize_mxfp8_colwise_tile_kernel(
+    const uint16_t *__restrict__ src, int64_t cols, const void *ws, int G, int64_t total_rows,
+    uint8_t *__restrict__ data, uint8_t *__restrict__ scale, int64_t ld) {
+  // [128 rows][kCtCols bf16] input, then [kCtCols rows][128 codes] output (16-byte
+  // slots XOR-swizzled by row), then [kCtCols][4] scale bytes: one array (see the GEMMs)
+  __shared__ __attribute__((aligned(16))) char lds[kCtRows * kCtCols * 2 + kCtCols * kCtRows + kCtCols * 4];
+  char *in = lds, *outc = lds + kCtRows * kCtCols * 2, *sc = outc + kCtCols * kCtRows;
+  const int ncol_tiles = (int)((cols + kCtCols - 1) / kCtCols);
+  const int64_t b128 = blockIdx.x / ncol_tiles;
+  const int64_t c0 = (int64_t)(blockIdx.x % ncol_tiles) * kCtCols;
+  const WsView v = ws_view(ws, G);
+  const int32_t *__restrict__ pre = v.pre[tile_rows_index(kCtRows)];
+  const int tid = threadIdx.x;
+  // The tile's group and rows.  Up to 63 groups the header, pre[] and off[] are read
+  // in one round (lane i holds entry i; a ballot finds the group and shuffles hand
+  // out its entries), so a workgroup waits for one load latency before its input
+  // loads instead of three.
+  int64_t r0, rend;
+  if (G < 64) {
+    const int lane = tid & 63;
+    const WsHeader *h = v.hdr;
+    const int32_t st = h->status, mg = h->magic, ng = h->num_groups;
+    const int64_t tr = h->total_rows;
+    const int32_t pv = lane <= G ? pre[lane] : 0x7fffffff;
+    const int64_t ov = lane <= G ? v.off[lane] : 0;
+    if (mg != kWsMagic || ng != G || tr != total_rows) {
+      if (tid == 0) atomicOr((int *)&h->status, 4);
+      return;
+    }
+    if (st != 0) return;
+    if (b128 >= __shfl(pv, G, 64)) return;  // past the last group's padding: untouched
+    const int g = __popcll(__ballot(pv <= (int)b128)) - 1;
+    r0 = __shfl(ov, g, 64) + (b128 - __shfl(pv, g, 64)) * kCtRows;
+    rend = __shfl(ov, g + 1, 64);
+  } else {
+    if (!ws_usable(v.hdr, G, total_rows)) return;
+    if (b128 >= pre[G]) return;
+    const int g = find_group(pre, G, (int)b128);
+    r0 = v.off[g] + (b128 - pre[g]) * kCtRows;
+    rend = v.off[g + 1];
+  }
+  constexpr int kRowBytes = kCtCols * 2, kLanesPerRow = kRowBytes / 16, kRowsPerPass = kQThreads / kLanesPerRow;
+
+  // load: 16 bytes (8 columns) per thread, kRowsPerPass rows per pass
+  {
+    const int cc = (tid % kLanesPerRow) * 8;
+#pragma unroll
+    for (int i = 0; i < kCtRows / kRowsPerPass; ++i) {
+      const int r = tid / kLanesPerRow + kRowsPerPass * i;
+      uint4 val = make_uint4(0, 0, 0, 0);
+      if (r0 + r < rend && c0 + cc < cols) val = *(const uint4 *)(src + (r0 + r) * cols + c0 + cc);
+      *(uint4 *)(in + r * kRowBytes + cc * 2) = val;
+    }
+  }
+  __syncthreads();
+  // quantize: thread (columns kCtCpt (t % 64) .., block k = t / 64) -- one wave per block
+  {
+    const int cp = tid & 63, k = tid >> 6;
+    uint32_t w[kCtCpt][16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = 32 * k + 2 * i;
+      if (kCtCpt == 1) {
+        const uint32_t lo = *(const uint16_t *)(in + r * kRowBytes + cp * 2);
+        const uint32_t hi = *(const uint16_t *)(in + (r + 1) * kRowBytes + cp * 2);
+        w[0][i] = lo | (hi << 16);
+      } else {
+        const uint32_t lo = *(const uint32_t *)(in + r * kRowBytes + cp * 4);
+        const uint32_t hi = *(const uint32_t *)(in + (r + 1) * kRowBytes + cp * 4);
+        w[0][i] = (lo & 0xffffu) | (hi << 16);
+        w[kCtCpt - 1][i] = (lo >> 16) | (hi & 0xffff0000u);
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < kCtCpt; ++h) {
+      const int c = cp * kCtCpt + h;
+      uint32_t out[8];
+      uint8_t sbyte;
+      quantize_block(w[h], out, sbyte);
+      char *row = outc + c * kCtRows;
+      *(uint4 *)(row + (((2 * k) ^ (c & 7)) << 4)) = make_uint4(out[0], out[1], out[2], out[3]);
+      *(uint4 *)(row + (((2 * k + 1) ^ (c & 7)) << 4)) = make_uint4(out[4], out[5], out[6], out[7]);
+      sc[c * 4 + k] = sbyte;
+    }
+  }
+  __syncthreads();
+  // store: thread t writes 16 codes of output row t / 8 (+ 32 i), whole lines per wave
+#pragma unroll
+  for (int i = 0; i < kCtCols / 32; ++i) {
+    const int c = (tid >> 3) + 32 * i, j = tid & 7;
+    if (c0 + c < cols) {
+      const uint4 val = *(const uint4 *)(outc + c * kCtRows + ((j ^ (c & 7)) << 4));
+      *(uint4 *)(data + (c0 + c) * ld + b128 * kCtRows + j * 16) = val;
+    }
+  }
+  for (int c = tid; c < kCtCols; c += kQThreads)
+    if (c0 + c < cols)
+      *(uint32_t *)(scale + (c0 + c) * (ld / 32) + b128 * (kCtRows / 32)) = *(const uint32_t *)(sc + c * 4);
+}
+
 // The weights' MXFP8 workspace in one launch: rowwise codes of w [G*N, K] (forward
 // operand, row_threads threads of one block each) and, when data_t is set, the
 // columnwise codes [G, K, N] (dgrad operand, col_threads threads), walked
@@ -252,8 +367,14 @@ hipError_t launch_quantize_mxfp8_colwise(const uint16_t *src, int64_t cols, int 
   const int64_t nblk = ld / 32;
   const int64_t threads = nblk * (cols / 4);
   if (threads == 0) return hipSuccess;
-  hipLaunchKernelGGL(quantize_mxfp8_colwise_kernel, dim3((unsigned)((threads + kQThreads - 1) / kQThreads)),
-                     dim3(kQThreads), 0, s, src, cols, nblk, ws, G, total_rows, (int64_t)0, data, scale, ld);
+  if (cols % 8 == 0 && ((uintptr_t)scale & 3u) == 0) {
+    const int64_t tiles = (ld / kCtRows) * ((cols + kCtCols - 1) / kCtCols);
+    hipLaunchKernelGGL(quantize_mxfp8_colwise_tile_kernel, dim3((unsigned)tiles), dim3(kQThreads), 0, s, src, cols,
+                       ws, G, total_rows, data, scale, ld);
+  } else {
+    hipLaunchKernelGGL(quantize_mxfp8_colwise_kernel, dim3((unsigned)((threads + kQThreads - 1) / kQThreads)),
+                       dim3(kQThreads), 0, s, src, cols, nblk, ws, G, total_rows, (int64_t)0, data, scale, ld);
+  }
   return hipGetLastError();
 }
 
