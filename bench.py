@@ -246,10 +246,14 @@ def bench_bf16(torch, gl, synth, steps, warmup):
         queue.put(xd, dyd, dw, ws, db=db)
         timer.run("wgrad_bgrad_deferred", queue.flush)
     torch.cuda.synchronize()
-    t_put = time.perf_counter()
+    # host cost of recording a call: median of single puts (a mean over a loop also
+    # catches the interpreter's occasional garbage-collection pass)
+    put_times = []
     for _ in range(200):
+        t_put = time.perf_counter()
         queue.put(xd, dyd, dw, ws, db=db)
-    put_us = (time.perf_counter() - t_put) / 200 * 1e6
+        put_times.append(time.perf_counter() - t_put)
+    put_us = sorted(put_times)[len(put_times) // 2] * 1e6
     queue.clear()
     per = timer.mean_ms()
     spread = timer.spread_ms()
