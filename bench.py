@@ -12,7 +12,12 @@ launch stream, the roofline entry of the dominant kernel, the MXFP8 forward on
 its own workload (G=32, K=N=4096, 32768 rows), and the CPU oracle timed on a
 bounded sample of the same workload.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-mxfp8] [--no-cpu-baseline]
+Also: the grouped MLP on the 8-group split, and two more workloads at full size
+(64 Zipf-skewed groups with wgrad into an fp32 main_grad; 256 groups forward into a
+caller buffer with per-group weights), each against its roofline.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-mxfp8] [--no-mlp] [--no-workloads]
+                    [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -407,6 +412,81 @@ def bench_mlp(torch, gl, steps, warmup):
                            "backward": round(T * 5 * F * 2 / (per["swiglu_backward"] * 1e-3) / 1e9, 1)}}
 
 
+def bench_workloads(torch, gl, synth, steps, warmup):
+    """The skewed 64-group workload (forward, dgrad, wgrad added into an fp32
+    main_grad) and the 256-group forward into a caller buffer with per-group weight
+    pointers, at full size.  Split sizes come from the seeded recipe; the values are
+    drawn on the device (torch.randn, bf16), since throughput does not depend on them
+    and the host recipe would spend most of the run making 7.5 GB of weights."""
+    dev = torch.device("cuda")
+    bf = torch.bfloat16
+    g = torch.Generator(device=dev).manual_seed(7)
+    out = {}
+    gbs = lambda nbytes, ms: round(nbytes / (ms * 1e-3) / 1e9, 1)
+    tf = lambda fl, ms: round(fl / (ms * 1e-3) / 1e12, 2)
+
+    wl = synth.WORKLOADS["bf16_zipf_g64_k2048_n1536"]
+    G, K, N, T = wl.G, wl.K, wl.N, wl.T
+    m = synth.split_sizes(wl)
+    x = torch.randn(T, K, generator=g, device=dev, dtype=bf)
+    dy = torch.randn(T, N, generator=g, device=dev, dtype=bf)
+    w = torch.randn(G, N, K, generator=g, device=dev, dtype=bf) * 0.02
+    mg = torch.randn(G, N, K, generator=g, device=dev)
+    y = torch.empty(T, N, dtype=bf, device=dev)
+    dx = torch.empty(T, K, dtype=bf, device=dev)
+    ws = gl.new_workspace(G, dev)
+    gl.gl_offsets(torch.from_numpy(m).to(dev), T, ws)
+    timer = EventTimer(torch)
+    for i in range(warmup + steps):
+        run = (lambda n, f: timer.run(n, f)) if i >= warmup else (lambda n, f: f())
+        run("forward", lambda: gl.gl_forward(x, w, y, ws))
+        run("dgrad", lambda: gl.gl_dgrad(dy, w, dx, ws))
+        run("wgrad_main_grad", lambda: gl.gl_wgrad(x, dy, mg, ws, accumulate=True))
+    torch.cuda.synchronize()
+    per = timer.mean_ms()
+    fl = 2.0 * T * N * K
+    gemm_bytes = (T * K + G * N * K + T * N) * 2
+    wgrad_bytes = (T * K + T * N) * 2 + 2 * G * N * K * 4
+    d = {"num_groups": G, "in_features": K, "out_features": N, "total_rows": T, "largest_group": int(m.max()),
+         "empty_groups": int((m == 0).sum())}
+    for k in ("forward", "dgrad", "wgrad_main_grad"):
+        nb = wgrad_bytes if k == "wgrad_main_grad" else gemm_bytes
+        d[k] = {"ms": round(per[k], 4), "tflops": tf(fl, per[k]), "pct_bf16_peak": round(100 * fl / (per[k] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+                "gbs": gbs(nb, per[k]), "pct_hbm": round(100 * nb / (per[k] * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
+                "algorithmic_bytes": nb}
+    d["fwd_dgrad_wgrad_tflops"] = tf(3 * fl, sum(per[k] for k in ("forward", "dgrad", "wgrad_main_grad")))
+    out[wl.name] = d
+    del x, dy, w, mg, y, dx
+
+    wl = synth.WORKLOADS["bf16_fwd_g256_k7168_n2048_outbuf"]
+    G, K, N, T = wl.G, wl.K, wl.N, wl.T
+    m = synth.split_sizes(wl)
+    x = torch.randn(T, K, generator=g, device=dev, dtype=bf)
+    w = torch.randn(G, N, K, generator=g, device=dev, dtype=bf) * 0.02
+    w_list = list(w)  # per-group weight pointers
+    rows = 34000
+    y = torch.full((rows, N), float("nan"), dtype=bf, device=dev)
+    ws = gl.new_workspace(G, dev)
+    gl.gl_offsets(torch.from_numpy(m).to(dev), T, ws)
+    timer = EventTimer(torch)
+    for i in range(warmup + steps):
+        run = (lambda n, f: timer.run(n, f)) if i >= warmup else (lambda n, f: f())
+        run("forward", lambda: gl.gl_forward(x, w_list, y, ws))
+    torch.cuda.synchronize()
+    if not bool(torch.isnan(y[T:]).all()):
+        raise RuntimeError("the caller buffer's tail was written")
+    ms = timer.mean_ms()["forward"]
+    nb = (T * K + G * N * K + T * N) * 2
+    fl = 2.0 * T * N * K
+    out[wl.name] = {"num_groups": G, "in_features": K, "out_features": N, "total_rows": T, "output_rows": rows,
+                    "weights": "per-group pointers",
+                    "forward": {"ms": round(ms, 4), "tflops": tf(fl, ms),
+                                "pct_bf16_peak": round(100 * fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+                                "gbs": gbs(nb, ms), "pct_hbm": round(100 * nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
+                                "algorithmic_bytes": nb}}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -414,6 +494,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-mxfp8", action="store_true")
     ap.add_argument("--no-mlp", action="store_true")
+    ap.add_argument("--no-workloads", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB copy (counter calibration)")
@@ -462,6 +543,8 @@ def main():
         out["mxfp8"] = bench_mxfp8(torch, gl, synth, max(5, args.steps // 2), 2)
     if not args.no_mlp:
         out["grouped_mlp"] = bench_mlp(torch, gl, max(5, args.steps // 2), 2)
+    if not args.no_workloads:
+        out["workloads"] = bench_workloads(torch, gl, synth, max(5, args.steps // 2), 2)
     if not args.no_cpu_baseline:
         x, w, b, dy = host_inputs
         out["cpu_baseline"] = cpu_baseline(wl, m.tolist(), x, w, b, dy)
