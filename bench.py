@@ -332,14 +332,15 @@ def bench_mxfp8(torch, gl, synth, steps, warmup):
         run("quantize_x_colwise", lambda: gl.gl_group_quantize_mxfp8_colwise(x, xtq, xts, ws, G))
         run("weights_noop", lambda: gl.gl_quantize_mxfp8_weights(w, wq, wsc, wtq, wts, noop_flag=noop_set))
         run("mx_forward", lambda: gl.gl_forward(xq, wq, y, ws, x_scale=xs, w_scale=wsc))
-        run("quantize_dy", lambda: gl.gl_group_quantize_mxfp8(dy, dq, ds))
-        run("quantize_dy_colwise", lambda: gl.gl_group_quantize_mxfp8_colwise(dy, dytq, dyts, ws, G))
+        run("quantize_dy_both", lambda: gl.gl_group_quantize_mxfp8_rowwise_colwise(dy, dq, ds, dytq, dyts, ws, G))
         run("mx_dgrad", lambda: gl.gl_dgrad_mxfp8(dq, ds, wtq, wts, dx, ws))
         run("mx_wgrad", lambda: gl.gl_wgrad_mxfp8(dytq, dyts, xtq, xts, dw, ws, T))
         # quantizers on their own, each on an input no pass just read (no cache warmth)
         run("quantize_w", lambda: gl.gl_group_quantize_mxfp8(w, wq, wsc))
-        run("quantize_x", lambda: gl.gl_group_quantize_mxfp8(x, xq, xs))
+        run("quantize_dy", lambda: gl.gl_group_quantize_mxfp8(dy, dq, ds))
         run("weights_refresh", lambda: gl.gl_quantize_mxfp8_weights(w, wq, wsc, wtq, wts, noop_flag=noop_clear))
+        run("quantize_dy_colwise", lambda: gl.gl_group_quantize_mxfp8_colwise(dy, dytq, dyts, ws, G))
+        run("quantize_x", lambda: gl.gl_group_quantize_mxfp8(x, xq, xs))
     torch.cuda.synchronize()
     per = timer.mean_ms()
     flops = 2.0 * T * N * K
@@ -356,18 +357,21 @@ def bench_mxfp8(torch, gl, synth, steps, warmup):
                            "dy": gbs("quantize_dy", row_bytes(T, N)),
                            "x_colwise": gbs("quantize_x_colwise", col_bytes(T, K)),
                            "dy_colwise": gbs("quantize_dy_colwise", col_bytes(T, N)),
+                           "dy_rowwise_and_colwise": gbs("quantize_dy_both",
+                                                         row_bytes(T, N) + col_bytes(T, N) - T * N * 2),
                            "offsets_and_x": gbs("offsets_quantize_x", row_bytes(T, K)),
                            "w_rowwise_and_colwise": gbs("weights_refresh", G * N * K * (2 + 2 * (1 + 1 / 32)))}
     out["launch_us"] = {"offsets_quantize_x": round(per["offsets_quantize_x"] * 1e3, 1),
                         "quantize_x": round(per["quantize_x"] * 1e3, 1),
                         "weights_with_noop_flag_set": round(per["weights_noop"] * 1e3, 1)}
-    step = ("offsets_quantize_x", "quantize_x_colwise", "weights_noop", "mx_forward", "quantize_dy",
-            "quantize_dy_colwise", "mx_dgrad", "mx_wgrad")
+    step = ("offsets_quantize_x", "quantize_x_colwise", "weights_noop", "mx_forward", "quantize_dy_both",
+            "mx_dgrad", "mx_wgrad")
     step_ms = sum(per[k] for k in step)
     out["mx_step_ms"] = round(step_ms, 4)
     out["mx_step_tflops"] = round(3 * flops / (step_ms * 1e-3) / 1e12, 2)
     out["mx_step"] = ("offsets + quantize x (one launch), quantize x columnwise, cached-weight refresh skipped "
-                      "by its no-op flag, MX forward, quantize dy (rowwise, columnwise), MX dgrad, MX wgrad")
+                      "by its no-op flag, MX forward, quantize dy rowwise and columnwise in one pass, MX dgrad, "
+                      "MX wgrad")
     return out
 
 

@@ -68,6 +68,7 @@ def load():
         "gl_colwise_ld": (I64, [I, I64]),
         "gl_group_quantize_mxfp8_colwise": (I, [P, I64, I, I64, P, P, P, I64, P]),
         "gl_quantize_mxfp8_colwise_weights": (I, [P, I, I64, I64, P, P, P]),
+        "gl_group_quantize_mxfp8_rowwise_colwise": (I, [P, I64, I, I64, P, P, P, P, P, I64, P]),
         "gl_offsets_quantize_mxfp8": (I, [P, I, I64, P, P, I64, P, P, P]),
         "gl_swiglu_forward": (I, [I64, I64, I, P, P, P]),
         "gl_swiglu_backward": (I, [I64, I64, I, P, P, P, P]),
@@ -313,6 +314,22 @@ def gl_group_quantize_mxfp8_colwise(src: Tensor, data_t: Tensor, scale_t: Tensor
     _check(load().gl_group_quantize_mxfp8_colwise(_ptr(src), C, int(num_groups), T, _ptr(workspace), _ptr(data_t),
                                                   _ptr(scale_t), ld, _stream(stream)))
     return data_t, scale_t
+
+
+def gl_group_quantize_mxfp8_rowwise_colwise(src: Tensor, data: Tensor, scale: Tensor, data_t: Tensor,
+                                            scale_t: Tensor, workspace: Tensor, num_groups: int, stream=None):
+    """Rowwise codes data [T, C] / scale [T, C/32] and per-group columnwise codes
+    data_t [C, ld] / scale_t [C, ld/32] of one bf16 tensor [T, C], read once."""
+    T, C = src.shape
+    ld = data_t.shape[1]
+    if src.dtype != torch.bfloat16 or data.shape != (T, C) or scale.shape != (T, C // 32):
+        raise ValueError("src must be bf16 [T, C], data [T, C] and scale [T, C/32]")
+    if data_t.shape != (C, ld) or scale_t.shape != (C, ld // 32):
+        raise ValueError("data_t must be [C, ld] and scale_t [C, ld/32]")
+    _check(load().gl_group_quantize_mxfp8_rowwise_colwise(_ptr(src), C, int(num_groups), T, _ptr(workspace),
+                                                          _ptr(data), _ptr(scale), _ptr(data_t), _ptr(scale_t), ld,
+                                                          _stream(stream)))
+    return data, scale, data_t, scale_t
 
 
 def gl_quantize_mxfp8_colwise_weights(w: Tensor, data_t: Tensor, scale_t: Tensor, stream=None):

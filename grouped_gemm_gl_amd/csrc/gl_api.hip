@@ -45,6 +45,9 @@ hipError_t launch_quantize_mxfp8_colwise(const uint16_t *src, int64_t cols, int 
                                          const void *ws, uint8_t *data, uint8_t *scale, int64_t ld, hipStream_t s);
 hipError_t launch_quantize_mxfp8_colwise_weights(const uint16_t *w, int G, int64_t N, int64_t K, uint8_t *data,
                                                  uint8_t *scale, hipStream_t s);
+hipError_t launch_quantize_mxfp8_rowwise_colwise(const uint16_t *src, int64_t cols, int G, int64_t total_rows,
+                                                 const void *ws, uint8_t *row_data, uint8_t *row_scale,
+                                                 uint8_t *data, uint8_t *scale, int64_t ld, hipStream_t s);
 hipError_t launch_offsets_quantize_mxfp8(const int64_t *m_splits, int G, int64_t total_rows, void *ws,
                                          const uint16_t *src, int64_t cols, uint8_t *data, uint8_t *scale,
                                          hipStream_t s);
@@ -383,6 +386,27 @@ int gl_group_quantize_mxfp8_colwise(const void *src, int64_t cols, int num_group
   return hip_result(gl::launch_quantize_mxfp8_colwise((const uint16_t *)src, cols, G, total_rows, workspace, data_t,
                                                       scale_t, ld, stream),
                     "gl_group_quantize_mxfp8_colwise");
+}
+
+int gl_group_quantize_mxfp8_rowwise_colwise(const void *src, int64_t cols, int num_groups, int64_t total_rows,
+                                            const void *workspace, uint8_t *data, uint8_t *scale, uint8_t *data_t,
+                                            uint8_t *scale_t, int64_t ld, hipStream_t stream) {
+  const int G = num_groups;
+  if (G <= 0 || total_rows < 0 || cols <= 0)
+    return fail(GL_ERR_ARG, "Invalid sizes (groups %d, rows %lld, cols %lld)", G, (long long)total_rows,
+                (long long)cols);
+  if (cols % 32) return fail(GL_ERR_SHAPE, "cols must be a multiple of 32 (got %lld)", (long long)cols);
+  if (total_rows * (cols / 32) / 256 >= ((int64_t)1 << 31))
+    return fail(GL_ERR_SHAPE, "src too large for one launch (%lld x %lld)", (long long)total_rows, (long long)cols);
+  GL_TRY(check_colwise_ld(G, total_rows, ld));
+  if (!workspace) return fail(GL_ERR_ARG, "workspace is NULL");
+  if (total_rows == 0) return ok();
+  if (!src || !data || !scale || !data_t || !scale_t) return fail(GL_ERR_ARG, "a buffer is NULL");
+  if (!aligned16(src) || !aligned16(data) || !aligned16(data_t))
+    return fail(GL_ERR_ARG, "src, data and data_t must be 16-byte aligned");
+  return hip_result(gl::launch_quantize_mxfp8_rowwise_colwise((const uint16_t *)src, cols, G, total_rows, workspace,
+                                                              data, scale, data_t, scale_t, ld, stream),
+                    "gl_group_quantize_mxfp8_rowwise_colwise");
 }
 
 int gl_offsets_quantize_mxfp8(const int64_t *m_splits, int num_groups, int64_t total_rows, void *workspace,

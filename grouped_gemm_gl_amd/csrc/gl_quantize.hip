@@ -8,30 +8,26 @@
 // dimension); scale rule from OCP MX v1.0: shared exponent floor(log2(amax)) - 8
 // clamped to [-127, 127], elements rounded to nearest-even E4M3 and saturated at
 // 448.  HBM-bound: each thread owns one 32-element block (64 bytes in, 32 + 1 out),
-// so a wave streams 4 KiB of contiguous input.  Everything is exact integer /
-// power-of-two arithmetic, bit-identical to the rule.
+// so a wave streams 4 KiB of contiguous input.  The scale comes from the exponent
+// bits and multiplies exactly (a power of two); the rounding to E4M3 is the
+// hardware pack conversion, bit-identical to the rule over every value it can see.
 #include "gl_offsets.hpp"
 
 namespace gl {
 
 constexpr int kQThreads = 256;
 
-// E4M3 code of a finite float s (already scaled into the block's range), RNE,
-// magnitudes >= 448 saturate to 448; the sign bit is kept (also for zero).
-__device__ __forceinline__ uint32_t e4m3_code(float s) {
-  const uint32_t sign = (__float_as_uint(s) >> 24) & 0x80u;
-  const float a = fabsf(s);
-  uint32_t mag;
-  if (a >= 448.0f) {
-    mag = 0x7e;
-  } else if (a < 0.015625f) {                    // below 2^-6: subnormal spacing 2^-9
-    mag = (uint32_t)__builtin_rintf(a * 512.0f);  // 0..8; 8 is the smallest normal's code
-  } else {
-    const int E = (int)((__float_as_uint(a) >> 23) & 0xff) - 127;  // -6 .. 8
-    const float m = __builtin_rintf(__builtin_ldexpf(a, 3 - E));   // 8 .. 16 (16 carries)
-    mag = (uint32_t)((E + 6) * 8) + (uint32_t)m;
-  }
-  return sign | mag;
+// E4M3 codes of four finite floats (already scaled into the block's range), packed
+// one per byte: round to nearest even, magnitudes above 448 saturate to 448, the sign
+// bit is kept (also for zero).  gfx950's pack conversion to OCP E4M3 rounds to
+// nearest even and keeps the sign; the clamp first makes overflow saturate.  Over
+// every value the quantizers can pass (8 significant bits, exponents -149 .. 9, both
+// signs) it gives the same bytes as the rule spelled out (checked exhaustively on
+// the device).
+__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d) {
+  const auto sat = [](float v) { return __builtin_amdgcn_fmed3f(v, -448.0f, 448.0f); };
+  uint32_t o = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat(a), sat(b), 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat(c), sat(d), (int)o, true);
 }
 
 // One block of 32 bf16 values, given as 16 words of two packed values each (element
@@ -62,14 +58,10 @@ __device__ __forceinline__ void quantize_block(const uint32_t *w, uint32_t *out,
     const float mul = __builtin_ldexpf(1.0f, 127 - byte);  // 2^-e, a normal float
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      uint32_t o = 0;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int el = i * 4 + k;
-        const uint32_t h = (w[el >> 1] >> ((el & 1) * 16)) & 0xffffu;
-        o |= e4m3_code(__uint_as_float(h << 16) * mul) << (8 * k);
-      }
-      out[i] = o;
+      // elements 4i .. 4i + 3 are the halves of words 2i and 2i + 1
+      const uint32_t w0 = w[2 * i], w1 = w[2 * i + 1];
+      out[i] = e4m3_pack4(__uint_as_float(w0 << 16) * mul, __uint_as_float(w0 & 0xffff0000u) * mul,
+                          __uint_as_float(w1 << 16) * mul, __uint_as_float(w1 & 0xffff0000u) * mul);
     }
   }
 }
@@ -199,7 +191,9 @@ __global__ __launch_bounds__(kQThreads) void quantize_mxfp8_colwise_kernel(
 // prefix table), so it lies in one group; rows past the group's end read as zero.
 // Needs cols % 8 == 0 and a 4-byte aligned scale matrix; the per-thread kernel
 // above serves the other cases.  Tiles past the last group's padding are left
-// untouched.
+// untouched.  With row_data set (cols % 32 == 0) the same tile also gives the
+// rowwise codes of its valid rows (blocks of 32 along a row, layout [T, cols]),
+// so a tensor needed both ways is read once.
 // 128-column tiles (256-byte row reads, two columns per thread) measured slower:
 // the larger LDS and register footprint costs more occupancy than they save.
 constexpr int kCtRows = 128, kCtCols = 64;
@@ -207,7 +201,8 @@ constexpr int kCtCpt = kCtCols / 64;  // adjacent columns per thread in the quan
 
 __global__ __launch_bounds__(kQThreads) void quantize_mxfp8_colwise_tile_kernel(
     const uint16_t *__restrict__ src, int64_t cols, const void *ws, int G, int64_t total_rows,
-    uint8_t *__restrict__ data, uint8_t *__restrict__ scale, int64_t ld) {
+    uint8_t *__restrict__ data, uint8_t *__restrict__ scale, int64_t ld, uint8_t *__restrict__ row_data,
+    uint8_t *__restrict__ row_scale) {
   // [128 rows][kCtCols bf16] input, then [kCtCols rows][128 codes] output (16-byte
   // slots XOR-swizzled by row), then [kCtCols][4] scale bytes: one array (see the GEMMs)
   __shared__ __attribute__((aligned(16))) char lds[kCtRows * kCtCols * 2 + kCtCols * kCtRows + kCtCols * 4];
@@ -290,6 +285,21 @@ __global__ __launch_bounds__(kQThreads) void quantize_mxfp8_colwise_tile_kernel(
       sc[c * 4 + k] = sbyte;
     }
   }
+  // rowwise: thread (row t / 2, block t % 2) of the tile's valid rows
+  if (row_data) {
+    const int r = tid >> 1, hb = tid & 1;
+    if (r0 + r < rend && c0 + hb * 32 < cols) {
+      const uint4 *q = (const uint4 *)(in + r * kRowBytes + hb * 64);
+      uint4 vv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vv[i] = q[i];
+      uint32_t out[8];
+      uint8_t sbyte;
+      quantize_block((const uint32_t *)vv, out, sbyte);
+      store_block(row_data + (r0 + r) * cols + c0 + hb * 32, out);
+      row_scale[(r0 + r) * (cols / 32) + c0 / 32 + hb] = sbyte;
+    }
+  }
   __syncthreads();
   // store: thread t writes 16 codes of output row t / 8 (+ 32 i), whole lines per wave
 #pragma unroll
@@ -370,12 +380,30 @@ hipError_t launch_quantize_mxfp8_colwise(const uint16_t *src, int64_t cols, int 
   if (cols % 8 == 0 && ((uintptr_t)scale & 3u) == 0) {
     const int64_t tiles = (ld / kCtRows) * ((cols + kCtCols - 1) / kCtCols);
     hipLaunchKernelGGL(quantize_mxfp8_colwise_tile_kernel, dim3((unsigned)tiles), dim3(kQThreads), 0, s, src, cols,
-                       ws, G, total_rows, data, scale, ld);
+                       ws, G, total_rows, data, scale, ld, (uint8_t *)nullptr, (uint8_t *)nullptr);
   } else {
     hipLaunchKernelGGL(quantize_mxfp8_colwise_kernel, dim3((unsigned)((threads + kQThreads - 1) / kQThreads)),
                        dim3(kQThreads), 0, s, src, cols, nblk, ws, G, total_rows, (int64_t)0, data, scale, ld);
   }
   return hipGetLastError();
+}
+
+// Rowwise codes [T, cols] / scales [T, cols / 32] and group-mode columnwise codes
+// of the same bf16 tensor (cols % 32 == 0), reading it once when the tile kernel
+// applies, else as the two separate launches.
+hipError_t launch_quantize_mxfp8_rowwise_colwise(const uint16_t *src, int64_t cols, int G, int64_t total_rows,
+                                                 const void *ws, uint8_t *row_data, uint8_t *row_scale,
+                                                 uint8_t *data, uint8_t *scale, int64_t ld, hipStream_t s) {
+  if (((uintptr_t)scale & 3u) == 0) {
+    const int64_t tiles = (ld / kCtRows) * ((cols + kCtCols - 1) / kCtCols);
+    if (tiles == 0) return hipSuccess;
+    hipLaunchKernelGGL(quantize_mxfp8_colwise_tile_kernel, dim3((unsigned)tiles), dim3(kQThreads), 0, s, src, cols,
+                       ws, G, total_rows, data, scale, ld, row_data, row_scale);
+    return hipGetLastError();
+  }
+  hipError_t e = launch_quantize_mxfp8(src, total_rows, cols, row_data, row_scale, s);
+  if (e != hipSuccess) return e;
+  return launch_quantize_mxfp8_colwise(src, cols, G, total_rows, ws, data, scale, ld, s);
 }
 
 // Uniform mode for stacked weights [G, N, K] (N % 32 == 0): codes [G, K, N], scales

@@ -240,6 +240,21 @@ int gl_group_quantize_mxfp8_colwise(const void *src, int64_t cols, int num_group
                                     hipStream_t stream);
 
 /*
+ * Both usages of one bf16 tensor in one pass (page "transformer_engine/pytorch/ops/
+ * basic/grouped_linear.py": a quantizer can make rowwise and columnwise data of the
+ * same tensor; the quantized backward uses dy rowwise for dgrad and columnwise for
+ * wgrad): data [total_rows, cols] / scale [total_rows, cols / 32] exactly as
+ * gl_group_quantize_mxfp8 makes them, and data_t / scale_t exactly as
+ * gl_group_quantize_mxfp8_colwise makes them.  cols % 32 == 0; src, data and data_t
+ * 16-byte aligned; ld as for gl_group_quantize_mxfp8_colwise.  The input is read
+ * once when scale_t is 4-byte aligned, else the two quantizations run as separate
+ * launches.  Split sizes found invalid by gl_offsets: nothing is written.
+ */
+int gl_group_quantize_mxfp8_rowwise_colwise(const void *src, int64_t cols, int num_groups, int64_t total_rows,
+                                            const void *workspace, uint8_t *data, uint8_t *scale, uint8_t *data_t,
+                                            uint8_t *scale_t, int64_t ld, hipStream_t stream);
+
+/*
  * Split-offset scan and rowwise MXFP8 quantization of the activations in one launch
  * (page "Single parameter for GroupedLinear module", review comments: compute the
  * tensor offsets in the same kernel rather than a separate cumsum; the grouped

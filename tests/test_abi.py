@@ -100,6 +100,11 @@ def test_other_entry_points_reject():
     assert lib.gl_group_quantize_mxfp8_colwise(FAKE, 64, 4, 1000, FAKE, FAKE2, FAKE2, ld + 64, None) == -3
     assert lib.gl_group_quantize_mxfp8_colwise(FAKE, 64, 4, 1000, None, FAKE2, FAKE2, ld, None) == -1
     assert lib.gl_quantize_mxfp8_colwise_weights(FAKE, 2, 48, 64, FAKE2, FAKE2, None) == -3
+    rc = lib.gl_group_quantize_mxfp8_rowwise_colwise
+    assert rc(FAKE, 48, 4, 1000, FAKE, FAKE2, FAKE2, FAKE2, FAKE2, ld, None) == -3       # cols % 32
+    assert rc(FAKE, 64, 4, 1000, FAKE, FAKE2, FAKE2, FAKE2, FAKE2, ld - 128, None) == -3  # ld too short
+    assert rc(FAKE, 64, 4, 1000, FAKE, None, FAKE2, FAKE2, FAKE2, ld, None) == -1         # a buffer missing
+    assert rc(FAKE + 8, 64, 4, 1000, FAKE, FAKE2, FAKE2, FAKE2, FAKE2, ld, None) == -1    # misaligned src
     assert lib.gl_dgrad_mxfp8(4, 64, 192, 32, gl.GL_BF16, FAKE, FAKE, FAKE, FAKE, FAKE2, 32, FAKE, None) == -3
     assert lib.gl_dgrad_mxfp8(4, 64, 256, 32, gl.GL_E4M3, FAKE, FAKE, FAKE, FAKE, FAKE2, 32, FAKE, None) == -2
     assert lib.gl_dgrad_mxfp8(4, 64, 256, 32, gl.GL_BF16, FAKE, FAKE, FAKE, FAKE, FAKE2, 16, FAKE, None) == -3

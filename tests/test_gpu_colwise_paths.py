@@ -69,3 +69,39 @@ def test_fallback_columns_not_multiple_of_8(cols):
 @pytest.mark.parametrize("offset", [1, 2])
 def test_fallback_misaligned_scales(offset):
     run_case([129, 0, 64, 300], 64, 66, scale_offset=offset)
+
+
+@pytest.mark.parametrize("G,cols,scale_offset", [(5, 96, 0), (70, 64, 0), (4, 160, 1)])
+def test_rowwise_and_colwise_in_one_pass(G, cols, scale_offset):
+    """Both usages of one tensor from one call: bit-equal to the two separate
+    quantizations and to the oracle (a misaligned columnwise scale matrix takes the
+    two-launch path)."""
+    rng = np.random.default_rng(67 + G)
+    m = (rng.integers(0, 300, G) * (rng.random(G) < 0.8)).tolist()
+    m[0] = 0
+    T = int(sum(m))
+    g = torch.Generator().manual_seed(68)
+    x = (torch.randn(T, cols, generator=g) * 2).to(torch.bfloat16)
+    ws = gl.new_workspace(G)
+    gl.gl_offsets(torch.tensor(m, dtype=torch.int64, device=DEV), T, ws)
+    ld = gl.gl_colwise_ld(G, T)
+    u8 = dict(dtype=torch.uint8, device=DEV)
+    dq, ds = torch.empty(T, cols, **u8), torch.empty(T, cols // 32, **u8)
+    tq = torch.full((cols, ld), 0xAB, **u8)
+    sbuf = torch.full((cols * (ld // 32) + 8,), 0xAB, **u8)
+    ts = sbuf[scale_offset:scale_offset + cols * (ld // 32)].view(cols, ld // 32)
+    xd = x.to(DEV)
+    gl.gl_group_quantize_mxfp8_rowwise_colwise(xd, dq, ds, tq, ts, ws, G)
+    rq, rs = torch.empty_like(dq), torch.empty_like(ds)
+    gl.gl_group_quantize_mxfp8(xd, rq, rs)
+    ctq, cts = torch.full((cols, ld), 0xAB, **u8), torch.full((cols, ld // 32), 0xAB, **u8)
+    gl.gl_group_quantize_mxfp8_colwise(xd, ctq, cts, ws, G)
+    torch.cuda.synchronize()
+    assert torch.equal(dq, rq) and torch.equal(ds, rs), "rowwise differs from gl_group_quantize_mxfp8"
+    assert torch.equal(tq, ctq) and torch.equal(ts, cts), "columnwise differs from gl_group_quantize_mxfp8_colwise"
+    oq, osc = oracle.quantize_mxfp8(to64(x))
+    assert np.array_equal(dq.cpu().numpy(), oq) and np.array_equal(ds.cpu().numpy(), osc)
+    cq, cs, poff = oracle.quantize_mxfp8_colwise(to64(x), m, ld=ld)
+    end = int(poff[-1])
+    assert np.array_equal(tq[:, :end].cpu().numpy(), cq[:, :end])
+    assert np.array_equal(ts[:, : end // 32].cpu().numpy(), cs[:, : end // 32])

@@ -294,6 +294,32 @@ def test_quantize_every_bf16_pattern_bit_exact():
     assert np.array_equal(data.cpu().numpy(), q)
 
 
+@pytest.mark.parametrize("e", [0, 16])
+def test_quantize_every_scaled_value_bit_exact(e):
+    """Every value the E4M3 rounding can be handed: a block whose first element is
+    1.5 * 2^(8+e) has shared exponent e, so its other 31 elements (every finite bf16
+    of magnitude at most that) reach the rounding as v * 2^-e.  e = 0 and e = 16
+    together cover every value of 8 significant bits from 2^-149 to 2^8, both signs."""
+    say(f"quantize every scaled value, e={e}")
+    v = synth.special_bf16_block_values()
+    head = 1.5 * 2.0 ** (8 + e)
+    v = v[v.float().abs() <= head]
+    n = (v.numel() + 30) // 31
+    body = torch.zeros(n * 31, dtype=torch.bfloat16)
+    body[: v.numel()] = v
+    src = torch.cat([torch.full((n, 1), head, dtype=torch.bfloat16), body.reshape(n, 31)], dim=1)
+    src = src.reshape(-1, 32 * 8) if n % 8 == 0 else torch.cat(
+        [src, torch.full((8 - n % 8, 32), head, dtype=torch.bfloat16)]).reshape(-1, 32 * 8)
+    data = torch.empty(src.shape, dtype=torch.uint8, device=DEV)
+    scale = torch.empty(src.shape[0], src.shape[1] // 32, dtype=torch.uint8, device=DEV)
+    gl.gl_group_quantize_mxfp8(src.to(DEV), data, scale)
+    torch.cuda.synchronize()
+    q, s = oracle.quantize_mxfp8(src.double().numpy())
+    assert (s == 127 + e).all(), "every block has the intended shared exponent"
+    assert np.array_equal(scale.cpu().numpy(), s)
+    assert np.array_equal(data.cpu().numpy(), q)
+
+
 @pytest.mark.parametrize("G,K,N,m", [(3, 256, 264, [0, 300, 77]), (4, 128, 512, [256, 1, 0, 257])])
 def test_mxfp8_forward(G, K, N, m):
     say(f"mxfp8 forward G={G} K={K} N={N} m={m}")
