@@ -70,6 +70,7 @@ def load():
         "gl_quantize_mxfp8_colwise_weights": (I, [P, I, I64, I64, P, P, P]),
         "gl_group_quantize_mxfp8_rowwise_colwise": (I, [P, I64, I, I64, P, P, P, P, P, I64, P]),
         "gl_offsets_quantize_mxfp8": (I, [P, I, I64, P, P, I64, P, P, P]),
+        "gl_offsets_quantize_mxfp8_rowwise_colwise": (I, [P, I, I64, P, P, I64, P, P, P, P, I64, P]),
         "gl_swiglu_forward": (I, [I64, I64, I, P, P, P]),
         "gl_swiglu_backward": (I, [I64, I64, I, P, P, P, P]),
         "gl_grouped_mlp_forward": (I, [I, I64, I64, I64, I64, I] + [P] * 12 + [I64, P, P]),
@@ -353,6 +354,25 @@ def gl_offsets_quantize_mxfp8(m_splits: Tensor, x: Tensor, workspace: Tensor, da
     _check(load().gl_offsets_quantize_mxfp8(_ptr(m_splits), m_splits.numel(), T, _ptr(workspace), _ptr(x), K,
                                             _ptr(data), _ptr(scale), _stream(stream)))
     return data, scale
+
+
+def gl_offsets_quantize_mxfp8_rowwise_colwise(m_splits: Tensor, x: Tensor, workspace: Tensor, data: Tensor,
+                                              scale: Tensor, data_t: Tensor, scale_t: Tensor, stream=None):
+    """The split-offset scan into ``workspace`` and both MXFP8 usages of the bf16
+    activations x [T, K]: rowwise data [T, K] / scale [T, K/32] and per-group
+    columnwise data_t [K, ld] / scale_t [K, ld/32], x read once."""
+    if m_splits.dtype != torch.int64:
+        raise ValueError("m_splits must be int64")
+    T, K = x.shape
+    ld = data_t.shape[1]
+    if x.dtype != torch.bfloat16 or data.shape != (T, K) or scale.shape != (T, K // 32):
+        raise ValueError("x must be bf16 [T, K], data [T, K] and scale [T, K/32]")
+    if data_t.shape != (K, ld) or scale_t.shape != (K, ld // 32):
+        raise ValueError("data_t must be [K, ld] and scale_t [K, ld/32]")
+    _check(load().gl_offsets_quantize_mxfp8_rowwise_colwise(_ptr(m_splits), m_splits.numel(), T, _ptr(workspace),
+                                                            _ptr(x), K, _ptr(data), _ptr(scale), _ptr(data_t),
+                                                            _ptr(scale_t), ld, _stream(stream)))
+    return data, scale, data_t, scale_t
 
 
 def gl_quantize_mxfp8_weights(w: Tensor, data: Tensor, scale: Tensor, data_t: Tensor = None, scale_t: Tensor = None,

@@ -48,6 +48,10 @@ hipError_t launch_quantize_mxfp8_colwise_weights(const uint16_t *w, int G, int64
 hipError_t launch_quantize_mxfp8_rowwise_colwise(const uint16_t *src, int64_t cols, int G, int64_t total_rows,
                                                  const void *ws, uint8_t *row_data, uint8_t *row_scale,
                                                  uint8_t *data, uint8_t *scale, int64_t ld, hipStream_t s);
+hipError_t launch_offsets_quantize_mxfp8_rowwise_colwise(const int64_t *m_splits, int G, int64_t total_rows,
+                                                         void *ws, const uint16_t *src, int64_t cols,
+                                                         uint8_t *row_data, uint8_t *row_scale, uint8_t *data,
+                                                         uint8_t *scale, int64_t ld, hipStream_t s);
 hipError_t launch_offsets_quantize_mxfp8(const int64_t *m_splits, int G, int64_t total_rows, void *ws,
                                          const uint16_t *src, int64_t cols, uint8_t *data, uint8_t *scale,
                                          hipStream_t s);
@@ -407,6 +411,31 @@ int gl_group_quantize_mxfp8_rowwise_colwise(const void *src, int64_t cols, int n
   return hip_result(gl::launch_quantize_mxfp8_rowwise_colwise((const uint16_t *)src, cols, G, total_rows, workspace,
                                                               data, scale, data_t, scale_t, ld, stream),
                     "gl_group_quantize_mxfp8_rowwise_colwise");
+}
+
+int gl_offsets_quantize_mxfp8_rowwise_colwise(const int64_t *m_splits, int num_groups, int64_t total_rows,
+                                              void *workspace, const void *x, int64_t in_features,
+                                              uint8_t *x_data, uint8_t *x_scale, uint8_t *x_data_t,
+                                              uint8_t *x_scale_t, int64_t ld, hipStream_t stream) {
+  const int G = num_groups;
+  const int64_t K = in_features;
+  if (G <= 0) return fail(GL_ERR_ARG, "Invalid number of groups (%d)", G);
+  if (total_rows < 0 || K <= 0) return fail(GL_ERR_ARG, "Invalid shape (%lld, %lld)", (long long)total_rows, (long long)K);
+  if (K % 32) return fail(GL_ERR_SHAPE, "in_features must be a multiple of 32 (got %lld)", (long long)K);
+  if (total_rows * (K / 32) / 256 >= ((int64_t)1 << 31))
+    return fail(GL_ERR_SHAPE, "x too large for one launch (%lld x %lld)", (long long)total_rows, (long long)K);
+  GL_TRY(check_colwise_ld(G, total_rows, ld));
+  if (!m_splits || ((uintptr_t)m_splits & 7u)) return fail(GL_ERR_ARG, "m_splits NULL or not 8-byte aligned");
+  if (!workspace || !aligned16(workspace)) return fail(GL_ERR_ARG, "workspace NULL or not 16-byte aligned");
+  if (total_rows > 0) {
+    if (!x || !x_data || !x_scale || !x_data_t || !x_scale_t) return fail(GL_ERR_ARG, "a buffer is NULL");
+    if (!aligned16(x) || !aligned16(x_data) || !aligned16(x_data_t))
+      return fail(GL_ERR_ARG, "x, x_data and x_data_t must be 16-byte aligned");
+  }
+  return hip_result(gl::launch_offsets_quantize_mxfp8_rowwise_colwise(m_splits, G, total_rows, workspace,
+                                                                      (const uint16_t *)x, K, x_data, x_scale,
+                                                                      x_data_t, x_scale_t, ld, stream),
+                    "gl_offsets_quantize_mxfp8_rowwise_colwise");
 }
 
 int gl_offsets_quantize_mxfp8(const int64_t *m_splits, int num_groups, int64_t total_rows, void *workspace,

@@ -193,16 +193,22 @@ __global__ __launch_bounds__(kQThreads) void quantize_mxfp8_colwise_kernel(
 // above serves the other cases.  Tiles past the last group's padding are left
 // untouched.  With row_data set (cols % 32 == 0) the same tile also gives the
 // rowwise codes of its valid rows (blocks of 32 along a row, layout [T, cols]),
-// so a tensor needed both ways is read once.
+// so a tensor needed both ways is read once.  FROM_SPLITS (fewer than 64 groups):
+// every workgroup derives the offsets and tile prefix from m_splits itself (one
+// wave scan), so the launch needs no workspace written before it; its first wave
+// of workgroup 0 also writes the workspace, as the offsets kernel does, for the
+// kernels after it.  Invalid splits (a negative size, or a sum other than
+// total_rows): the workspace gets its status word and no code is written.
 // 128-column tiles (256-byte row reads, two columns per thread) measured slower:
 // the larger LDS and register footprint costs more occupancy than they save.
 constexpr int kCtRows = 128, kCtCols = 64;
 constexpr int kCtCpt = kCtCols / 64;  // adjacent columns per thread in the quantize step
 
+template <bool FROM_SPLITS>
 __global__ __launch_bounds__(kQThreads) void quantize_mxfp8_colwise_tile_kernel(
     const uint16_t *__restrict__ src, int64_t cols, const void *ws, int G, int64_t total_rows,
     uint8_t *__restrict__ data, uint8_t *__restrict__ scale, int64_t ld, uint8_t *__restrict__ row_data,
-    uint8_t *__restrict__ row_scale) {
+    uint8_t *__restrict__ row_scale, const int64_t *__restrict__ m_splits) {
   // [128 rows][kCtCols bf16] input, then [kCtCols rows][128 codes] output (16-byte
   // slots XOR-swizzled by row), then [kCtCols][4] scale bytes: one array (see the GEMMs)
   __shared__ __attribute__((aligned(16))) char lds[kCtRows * kCtCols * 2 + kCtCols * kCtRows + kCtCols * 4];
@@ -218,7 +224,23 @@ __global__ __launch_bounds__(kQThreads) void quantize_mxfp8_colwise_tile_kernel(
   // out its entries), so a workgroup waits for one load latency before its input
   // loads instead of three.
   int64_t r0, rend;
-  if (G < 64) {
+  if constexpr (FROM_SPLITS) {
+    const int lane = tid & 63;
+    if (blockIdx.x == 0 && tid < 64) offsets_wave(m_splits, G, total_rows, (void *)ws);
+    const int64_t m = lane < G ? m_splits[lane] : 0;
+    const bool bad = __ballot(m < 0) != 0;
+    const int64_t mv = m > 0 ? m : 0;
+    const int64_t incl = wave_inclusive_scan(mv);
+    const int32_t t128 = (int32_t)((mv + kCtRows - 1) / kCtRows);
+    const int32_t tincl = wave_inclusive_scan(t128);
+    if (bad || __shfl(incl, 63, 64) != total_rows) return;  // the status word says why
+    // lane l <= G: exclusive prefixes (lane G: the totals)
+    const int32_t pv = lane <= G ? tincl - t128 : 0x7fffffff;
+    if (b128 >= __shfl(pv, G, 64)) return;  // past the last group's padding: untouched
+    const int g = __popcll(__ballot(pv <= (int)b128)) - 1;
+    r0 = __shfl(incl - mv, g, 64) + (b128 - __shfl(pv, g, 64)) * kCtRows;
+    rend = __shfl(incl, g, 64);
+  } else if (G < 64) {
     const int lane = tid & 63;
     const WsHeader *h = v.hdr;
     const int32_t st = h->status, mg = h->magic, ng = h->num_groups;
@@ -379,8 +401,9 @@ hipError_t launch_quantize_mxfp8_colwise(const uint16_t *src, int64_t cols, int 
   if (threads == 0) return hipSuccess;
   if (cols % 8 == 0 && ((uintptr_t)scale & 3u) == 0) {
     const int64_t tiles = (ld / kCtRows) * ((cols + kCtCols - 1) / kCtCols);
-    hipLaunchKernelGGL(quantize_mxfp8_colwise_tile_kernel, dim3((unsigned)tiles), dim3(kQThreads), 0, s, src, cols,
-                       ws, G, total_rows, data, scale, ld, (uint8_t *)nullptr, (uint8_t *)nullptr);
+    hipLaunchKernelGGL(quantize_mxfp8_colwise_tile_kernel<false>, dim3((unsigned)tiles), dim3(kQThreads), 0, s, src,
+                       cols, ws, G, total_rows, data, scale, ld, (uint8_t *)nullptr, (uint8_t *)nullptr,
+                       (const int64_t *)nullptr);
   } else {
     hipLaunchKernelGGL(quantize_mxfp8_colwise_kernel, dim3((unsigned)((threads + kQThreads - 1) / kQThreads)),
                        dim3(kQThreads), 0, s, src, cols, nblk, ws, G, total_rows, (int64_t)0, data, scale, ld);
@@ -397,11 +420,31 @@ hipError_t launch_quantize_mxfp8_rowwise_colwise(const uint16_t *src, int64_t co
   if (((uintptr_t)scale & 3u) == 0) {
     const int64_t tiles = (ld / kCtRows) * ((cols + kCtCols - 1) / kCtCols);
     if (tiles == 0) return hipSuccess;
-    hipLaunchKernelGGL(quantize_mxfp8_colwise_tile_kernel, dim3((unsigned)tiles), dim3(kQThreads), 0, s, src, cols,
-                       ws, G, total_rows, data, scale, ld, row_data, row_scale);
+    hipLaunchKernelGGL(quantize_mxfp8_colwise_tile_kernel<false>, dim3((unsigned)tiles), dim3(kQThreads), 0, s, src,
+                       cols, ws, G, total_rows, data, scale, ld, row_data, row_scale, (const int64_t *)nullptr);
     return hipGetLastError();
   }
   hipError_t e = launch_quantize_mxfp8(src, total_rows, cols, row_data, row_scale, s);
+  if (e != hipSuccess) return e;
+  return launch_quantize_mxfp8_colwise(src, cols, G, total_rows, ws, data, scale, ld, s);
+}
+
+// The split-offset scan and both usages of the activations in one launch when the
+// tile kernel can take the splits itself (fewer than 64 groups, a 4-byte aligned
+// columnwise scale matrix), else the fused scan + rowwise launch and the columnwise
+// launch after it.
+hipError_t launch_offsets_quantize_mxfp8_rowwise_colwise(const int64_t *m_splits, int G, int64_t total_rows,
+                                                         void *ws, const uint16_t *src, int64_t cols,
+                                                         uint8_t *row_data, uint8_t *row_scale, uint8_t *data,
+                                                         uint8_t *scale, int64_t ld, hipStream_t s) {
+  if (G < 64 && ((uintptr_t)scale & 3u) == 0) {
+    const int64_t tiles = (ld / kCtRows) * ((cols + kCtCols - 1) / kCtCols);
+    hipLaunchKernelGGL(quantize_mxfp8_colwise_tile_kernel<true>, dim3((unsigned)(tiles > 0 ? tiles : 1)),
+                       dim3(kQThreads), 0, s, src, cols, (const void *)ws, G, total_rows, data, scale, ld, row_data,
+                       row_scale, m_splits);
+    return hipGetLastError();
+  }
+  hipError_t e = launch_offsets_quantize_mxfp8(m_splits, G, total_rows, ws, src, cols, row_data, row_scale, s);
   if (e != hipSuccess) return e;
   return launch_quantize_mxfp8_colwise(src, cols, G, total_rows, ws, data, scale, ld, s);
 }

@@ -271,6 +271,21 @@ int gl_offsets_quantize_mxfp8(const int64_t *m_splits, int num_groups, int64_t t
                               hipStream_t stream);
 
 /*
+ * gl_offsets_quantize_mxfp8 plus the columnwise codes of x for the wgrad (as
+ * gl_group_quantize_mxfp8_colwise makes them, into x_data_t [K, ld] / x_scale_t
+ * [K, ld / 32]), reading x once: with fewer than 64 groups and a 4-byte aligned
+ * x_scale_t, one launch in which every workgroup derives the group offsets from
+ * m_splits itself while the first also writes the workspace; otherwise the two
+ * launches one after the other.  ld as for gl_group_quantize_mxfp8_colwise.
+ * Invalid splits: the workspace's status word is set (which stops every later
+ * kernel) and the codes are not to be used; the one-launch form writes none.
+ */
+int gl_offsets_quantize_mxfp8_rowwise_colwise(const int64_t *m_splits, int num_groups, int64_t total_rows,
+                                              void *workspace, const void *x, int64_t in_features,
+                                              uint8_t *x_data, uint8_t *x_scale, uint8_t *x_data_t,
+                                              uint8_t *x_scale_t, int64_t ld, hipStream_t stream);
+
+/*
  * The MXFP8 weight workspace, refreshed in one launch and skippable on the device
  * (page "Improve device-init grouped linear module with single grouped weight
  * support": group_quantize writes into a cached output in place and takes a

@@ -91,6 +91,56 @@ def test_fused_offsets_quantize_zero_rows():
     assert gl.workspace_offsets(ws, 4).cpu().tolist() == [0] * 5
 
 
+def both_buffers(T, K, G, scale_offset=0):
+    ld = gl.gl_colwise_ld(G, T)
+    u8 = dict(dtype=torch.uint8, device=DEV)
+    sbuf = torch.full((K * (ld // 32) + 8,), 0xAB, **u8)
+    return (torch.empty(T, K, **u8), torch.empty(T, K // 32, **u8), torch.full((K, ld), 0xAB, **u8),
+            sbuf[scale_offset:scale_offset + K * (ld // 32)].view(K, ld // 32))
+
+
+@pytest.mark.parametrize("m,scale_offset", [([5, 0, 300, 17, 1], 0), ([2048, 1, 0, 511, 1000, 3], 0),
+                                            (MANY.tolist(), 0), ([129, 0, 64], 1)])
+def test_offsets_and_both_usages_in_one_pass(m, scale_offset):
+    """The scan plus rowwise and columnwise codes of x: the workspace tables and both
+    codes bit-equal to gl_offsets + gl_group_quantize_mxfp8 + the columnwise call (one
+    launch below 64 groups with an aligned scale matrix, two launches otherwise)."""
+    m = np.array(m, dtype=np.int64)
+    G, T, K = len(m), int(m.sum()), 192
+    say(f"offsets + both usages: G={G} T={T} scale_offset={scale_offset}")
+    x = bf16((T, K), 2.0, 3).to(DEV)
+    md = torch.from_numpy(m).to(DEV)
+    ws_a, ws_b = gl.new_workspace(G), gl.new_workspace(G)
+    ws_a.fill_(0x5a)
+    ws_b.fill_(0x5a)
+    qa, sa, ta, tsa = both_buffers(T, K, G, scale_offset)
+    qb, sb, tb, tsb = both_buffers(T, K, G)
+    gl.gl_offsets_quantize_mxfp8_rowwise_colwise(md, x, ws_a, qa, sa, ta, tsa)
+    gl.gl_offsets(md, T, ws_b)
+    gl.gl_group_quantize_mxfp8(x, qb, sb)
+    gl.gl_group_quantize_mxfp8_colwise(x, tb, tsb, ws_b, G)
+    torch.cuda.synchronize()
+    nb = table_bytes(G)
+    assert_bits_equal(ws_a[:nb], ws_b[:nb], "workspace tables")
+    assert gl.gl_read_status(ws_a) == 0
+    assert_bits_equal(qa, qb, "rowwise codes")
+    assert_bits_equal(sa, sb, "rowwise scales")
+    assert_bits_equal(ta, tb, "columnwise codes")
+    assert_bits_equal(tsa, tsb, "columnwise scales")
+
+
+def test_offsets_and_both_usages_invalid_and_empty():
+    for m, bit in (([10, -3, 25], gl.GL_STATUS_NEGATIVE_SPLIT), ([0, 0, 0, 0], 0)):
+        md = torch.tensor(m, dtype=torch.int64, device=DEV)
+        T = 32 if bit else 0
+        x = bf16((T, 64), 1.0, 4).to(DEV)
+        ws = gl.new_workspace(len(m))
+        gl.gl_offsets_quantize_mxfp8_rowwise_colwise(md, x, ws, *both_buffers(T, 64, len(m)))
+        st = gl.gl_read_status(ws)
+        assert (st & bit) if bit else st == 0
+    assert gl.workspace_offsets(ws, 4).cpu().tolist() == [0] * 5
+
+
 def weight_buffers(G, N, K):
     u8 = dict(dtype=torch.uint8, device=DEV)
     return (torch.empty(G, N, K, **u8), torch.empty(G, N, K // 32, **u8), torch.empty(G, K, N, **u8),
