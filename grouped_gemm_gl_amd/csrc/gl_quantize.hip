@@ -204,65 +204,23 @@ __global__ __launch_bounds__(kQThreads) void quantize_mxfp8_colwise_kernel(
 constexpr int kCtRows = 128, kCtCols = 64;
 constexpr int kCtCpt = kCtCols / 64;  // adjacent columns per thread in the quantize step
 
-template <bool FROM_SPLITS>
-__global__ __launch_bounds__(kQThreads) void quantize_mxfp8_colwise_tile_kernel(
-    const uint16_t *__restrict__ src, int64_t cols, const void *ws, int G, int64_t total_rows,
-    uint8_t *__restrict__ data, uint8_t *__restrict__ scale, int64_t ld, uint8_t *__restrict__ row_data,
-    uint8_t *__restrict__ row_scale, const int64_t *__restrict__ m_splits) {
-  // [128 rows][kCtCols bf16] input, then [kCtCols rows][128 codes] output (16-byte
-  // slots XOR-swizzled by row), then [kCtCols][4] scale bytes: one array (see the GEMMs)
-  __shared__ __attribute__((aligned(16))) char lds[kCtRows * kCtCols * 2 + kCtCols * kCtRows + kCtCols * 4];
+// One 128-row x 64-column tile of the columnwise (and optionally rowwise) MXFP8
+// quantization: rows [r0, rend) of src [*, cols] (rows past rend read as zero),
+// columns c0 .. c0 + 63.  Output row c (input column c0 + c) gets its 128 codes at
+// dt + c * dt_ld and its 4 scale bytes as one word at st + c * st_ld; with row_data
+// set, the tile's valid rows also get their rowwise codes (layout [*, cols]).  The
+// tile goes in through LDS with 16-byte row loads, one wave quantizes each 32-row
+// block of every column, and the codes go back through LDS so that each store
+// instruction writes whole 128-byte lines (8 output rows per wave).  Whole
+// workgroup; lds holds kCtLdsBytes.
+constexpr int kCtLdsBytes = kCtRows * kCtCols * 2 + kCtCols * kCtRows + kCtCols * 4;
+
+__device__ __forceinline__ void ct_tile(const uint16_t *__restrict__ src, int64_t cols, int64_t r0, int64_t rend,
+                                        int64_t c0, uint8_t *__restrict__ dt, int64_t dt_ld,
+                                        uint8_t *__restrict__ st, int64_t st_ld, uint8_t *__restrict__ row_data,
+                                        uint8_t *__restrict__ row_scale, char *lds) {
   char *in = lds, *outc = lds + kCtRows * kCtCols * 2, *sc = outc + kCtCols * kCtRows;
-  const int ncol_tiles = (int)((cols + kCtCols - 1) / kCtCols);
-  const int64_t b128 = blockIdx.x / ncol_tiles;
-  const int64_t c0 = (int64_t)(blockIdx.x % ncol_tiles) * kCtCols;
-  const WsView v = ws_view(ws, G);
-  const int32_t *__restrict__ pre = v.pre[tile_rows_index(kCtRows)];
   const int tid = threadIdx.x;
-  // The tile's group and rows.  Up to 63 groups the header, pre[] and off[] are read
-  // in one round (lane i holds entry i; a ballot finds the group and shuffles hand
-  // out its entries), so a workgroup waits for one load latency before its input
-  // loads instead of three.
-  int64_t r0, rend;
-  if constexpr (FROM_SPLITS) {
-    const int lane = tid & 63;
-    if (blockIdx.x == 0 && tid < 64) offsets_wave(m_splits, G, total_rows, (void *)ws);
-    const int64_t m = lane < G ? m_splits[lane] : 0;
-    const bool bad = __ballot(m < 0) != 0;
-    const int64_t mv = m > 0 ? m : 0;
-    const int64_t incl = wave_inclusive_scan(mv);
-    const int32_t t128 = (int32_t)((mv + kCtRows - 1) / kCtRows);
-    const int32_t tincl = wave_inclusive_scan(t128);
-    if (bad || __shfl(incl, 63, 64) != total_rows) return;  // the status word says why
-    // lane l <= G: exclusive prefixes (lane G: the totals)
-    const int32_t pv = lane <= G ? tincl - t128 : 0x7fffffff;
-    if (b128 >= __shfl(pv, G, 64)) return;  // past the last group's padding: untouched
-    const int g = __popcll(__ballot(pv <= (int)b128)) - 1;
-    r0 = __shfl(incl - mv, g, 64) + (b128 - __shfl(pv, g, 64)) * kCtRows;
-    rend = __shfl(incl, g, 64);
-  } else if (G < 64) {
-    const int lane = tid & 63;
-    const WsHeader *h = v.hdr;
-    const int32_t st = h->status, mg = h->magic, ng = h->num_groups;
-    const int64_t tr = h->total_rows;
-    const int32_t pv = lane <= G ? pre[lane] : 0x7fffffff;
-    const int64_t ov = lane <= G ? v.off[lane] : 0;
-    if (mg != kWsMagic || ng != G || tr != total_rows) {
-      if (tid == 0) atomicOr((int *)&h->status, 4);
-      return;
-    }
-    if (st != 0) return;
-    if (b128 >= __shfl(pv, G, 64)) return;  // past the last group's padding: untouched
-    const int g = __popcll(__ballot(pv <= (int)b128)) - 1;
-    r0 = __shfl(ov, g, 64) + (b128 - __shfl(pv, g, 64)) * kCtRows;
-    rend = __shfl(ov, g + 1, 64);
-  } else {
-    if (!ws_usable(v.hdr, G, total_rows)) return;
-    if (b128 >= pre[G]) return;
-    const int g = find_group(pre, G, (int)b128);
-    r0 = v.off[g] + (b128 - pre[g]) * kCtRows;
-    rend = v.off[g + 1];
-  }
   constexpr int kRowBytes = kCtCols * 2, kLanesPerRow = kRowBytes / 16, kRowsPerPass = kQThreads / kLanesPerRow;
 
   // load: 16 bytes (8 columns) per thread, kRowsPerPass rows per pass
@@ -329,12 +287,96 @@ __global__ __launch_bounds__(kQThreads) void quantize_mxfp8_colwise_tile_kernel(
     const int c = (tid >> 3) + 32 * i, j = tid & 7;
     if (c0 + c < cols) {
       const uint4 val = *(const uint4 *)(outc + c * kCtRows + ((j ^ (c & 7)) << 4));
-      *(uint4 *)(data + (c0 + c) * ld + b128 * kCtRows + j * 16) = val;
+      *(uint4 *)(dt + c * dt_ld + j * 16) = val;
     }
   }
   for (int c = tid; c < kCtCols; c += kQThreads)
     if (c0 + c < cols)
-      *(uint32_t *)(scale + (c0 + c) * (ld / 32) + b128 * (kCtRows / 32)) = *(const uint32_t *)(sc + c * 4);
+      *(uint32_t *)(st + c * st_ld) = *(const uint32_t *)(sc + c * 4);
+  __syncthreads();  // the LDS is free for the next tile
+}
+
+template <bool FROM_SPLITS>
+__global__ __launch_bounds__(kQThreads) void quantize_mxfp8_colwise_tile_kernel(
+    const uint16_t *__restrict__ src, int64_t cols, const void *ws, int G, int64_t total_rows,
+    uint8_t *__restrict__ data, uint8_t *__restrict__ scale, int64_t ld, uint8_t *__restrict__ row_data,
+    uint8_t *__restrict__ row_scale, const int64_t *__restrict__ m_splits) {
+  // [128 rows][kCtCols bf16] input, then [kCtCols rows][128 codes] output (16-byte
+  // slots XOR-swizzled by row), then [kCtCols][4] scale bytes: one array (see the GEMMs)
+  __shared__ __attribute__((aligned(16))) char lds[kCtLdsBytes];
+  const int ncol_tiles = (int)((cols + kCtCols - 1) / kCtCols);
+  const int64_t b128 = blockIdx.x / ncol_tiles;
+  const int64_t c0 = (int64_t)(blockIdx.x % ncol_tiles) * kCtCols;
+  const WsView v = ws_view(ws, G);
+  const int32_t *__restrict__ pre = v.pre[tile_rows_index(kCtRows)];
+  const int tid = threadIdx.x;
+  // The tile's group and rows.  Up to 63 groups the header, pre[] and off[] are read
+  // in one round (lane i holds entry i; a ballot finds the group and shuffles hand
+  // out its entries), so a workgroup waits for one load latency before its input
+  // loads instead of three.
+  int64_t r0, rend;
+  if constexpr (FROM_SPLITS) {
+    const int lane = tid & 63;
+    if (blockIdx.x == 0 && tid < 64) offsets_wave(m_splits, G, total_rows, (void *)ws);
+    const int64_t m = lane < G ? m_splits[lane] : 0;
+    const bool bad = __ballot(m < 0) != 0;
+    const int64_t mv = m > 0 ? m : 0;
+    const int64_t incl = wave_inclusive_scan(mv);
+    const int32_t t128 = (int32_t)((mv + kCtRows - 1) / kCtRows);
+    const int32_t tincl = wave_inclusive_scan(t128);
+    if (bad || __shfl(incl, 63, 64) != total_rows) return;  // the status word says why
+    // lane l <= G: exclusive prefixes (lane G: the totals)
+    const int32_t pv = lane <= G ? tincl - t128 : 0x7fffffff;
+    if (b128 >= __shfl(pv, G, 64)) return;  // past the last group's padding: untouched
+    const int g = __popcll(__ballot(pv <= (int)b128)) - 1;
+    r0 = __shfl(incl - mv, g, 64) + (b128 - __shfl(pv, g, 64)) * kCtRows;
+    rend = __shfl(incl, g, 64);
+  } else if (G < 64) {
+    const int lane = tid & 63;
+    const WsHeader *h = v.hdr;
+    const int32_t st = h->status, mg = h->magic, ng = h->num_groups;
+    const int64_t tr = h->total_rows;
+    const int32_t pv = lane <= G ? pre[lane] : 0x7fffffff;
+    const int64_t ov = lane <= G ? v.off[lane] : 0;
+    if (mg != kWsMagic || ng != G || tr != total_rows) {
+      if (tid == 0) atomicOr((int *)&h->status, 4);
+      return;
+    }
+    if (st != 0) return;
+    if (b128 >= __shfl(pv, G, 64)) return;  // past the last group's padding: untouched
+    const int g = __popcll(__ballot(pv <= (int)b128)) - 1;
+    r0 = __shfl(ov, g, 64) + (b128 - __shfl(pv, g, 64)) * kCtRows;
+    rend = __shfl(ov, g + 1, 64);
+  } else {
+    if (!ws_usable(v.hdr, G, total_rows)) return;
+    if (b128 >= pre[G]) return;
+    const int g = find_group(pre, G, (int)b128);
+    r0 = v.off[g] + (b128 - pre[g]) * kCtRows;
+    rend = v.off[g + 1];
+  }
+  ct_tile(src, cols, r0, rend, c0, data + c0 * ld + b128 * kCtRows, ld, scale + c0 * (ld / 32) + b128 * (kCtRows / 32),
+          ld / 32, row_data, row_scale, lds);
+}
+
+// The weights' MXFP8 workspace by tiles (N % 128 == 0, columnwise codes wanted,
+// 4-byte aligned columnwise scales): group g of w [G, N, K] is a uniform matrix of
+// N rows, so 128-row tile bl of group g gives rowwise codes of rows g N + 128 bl ..
+// and columnwise codes [K, N] of group g at columns 128 bl ..  Persistent over a
+// bounded grid, so that a refresh skipped by its no-op flag stays one small launch.
+__global__ __launch_bounds__(kQThreads) void quantize_mxfp8_weights_tile_kernel(
+    const uint16_t *__restrict__ w, int G, int64_t N, int64_t K, uint8_t *__restrict__ data,
+    uint8_t *__restrict__ scale, uint8_t *__restrict__ data_t, uint8_t *__restrict__ scale_t,
+    const int32_t *__restrict__ noop) {
+  __shared__ __attribute__((aligned(16))) char lds[kCtLdsBytes];
+  if (noop && *noop) return;
+  const int64_t tpg = N / kCtRows, nct = (K + kCtCols - 1) / kCtCols;
+  const int64_t tiles = (int64_t)G * tpg * nct;
+  for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
+    const int64_t ct = t % nct, rt = t / nct, g = rt / tpg, bl = rt % tpg;
+    const int64_t c0 = ct * kCtCols, r0 = g * N + bl * kCtRows;
+    ct_tile(w, K, r0, r0 + kCtRows, c0, data_t + g * K * N + c0 * N + bl * kCtRows, N,
+            scale_t + g * K * (N / 32) + c0 * (N / 32) + bl * (kCtRows / 32), N / 32, data, scale, lds);
+  }
 }
 
 // The weights' MXFP8 workspace in one launch: rowwise codes of w [G*N, K] (forward
@@ -383,6 +425,13 @@ hipError_t launch_offsets_quantize_mxfp8(const int64_t *m_splits, int G, int64_t
 hipError_t launch_quantize_mxfp8_weights(const uint16_t *w, int G, int64_t N, int64_t K, uint8_t *data,
                                          uint8_t *scale, uint8_t *data_t, uint8_t *scale_t, const int32_t *noop,
                                          hipStream_t s) {
+  if (data_t && N % kCtRows == 0 && ((uintptr_t)scale_t & 3u) == 0) {
+    const int64_t tiles = (int64_t)G * (N / kCtRows) * ((K + kCtCols - 1) / kCtCols);
+    const int64_t grid = tiles < kQuantizeWgs ? tiles : kQuantizeWgs;
+    hipLaunchKernelGGL(quantize_mxfp8_weights_tile_kernel, dim3((unsigned)(grid > 0 ? grid : 1)), dim3(kQThreads), 0,
+                       s, w, G, N, K, data, scale, data_t, scale_t, noop);
+    return hipGetLastError();
+  }
   const int64_t row_threads = (int64_t)G * N * (K / 32);
   const int64_t col_threads = data_t ? (int64_t)G * (N / 32) * (K / 4) : 0;
   const int64_t wgs = (row_threads + col_threads + kQThreads - 1) / kQThreads;
