@@ -202,7 +202,6 @@ __global__ __launch_bounds__(kQThreads) void quantize_mxfp8_colwise_kernel(
 // 128-column tiles (256-byte row reads, two columns per thread) measured slower:
 // the larger LDS and register footprint costs more occupancy than they save.
 constexpr int kCtRows = 128, kCtCols = 64;
-constexpr int kCtCpt = kCtCols / 64;  // adjacent columns per thread in the quantize step
 
 // One 128-row x 64-column tile of the columnwise (and optionally rowwise) MXFP8
 // quantization: rows [r0, rend) of src [*, cols] (rows past rend read as zero),
@@ -235,35 +234,24 @@ __device__ __forceinline__ void ct_tile(const uint16_t *__restrict__ src, int64_
     }
   }
   __syncthreads();
-  // quantize: thread (columns kCtCpt (t % 64) .., block k = t / 64) -- one wave per block
+  // quantize: thread (column c = t % 64, block k = t / 64) -- one wave per block
   {
-    const int cp = tid & 63, k = tid >> 6;
-    uint32_t w[kCtCpt][16];
+    const int c = tid & 63, k = tid >> 6;
+    uint32_t w[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int r = 32 * k + 2 * i;
-      if (kCtCpt == 1) {
-        const uint32_t lo = *(const uint16_t *)(in + r * kRowBytes + cp * 2);
-        const uint32_t hi = *(const uint16_t *)(in + (r + 1) * kRowBytes + cp * 2);
-        w[0][i] = lo | (hi << 16);
-      } else {
-        const uint32_t lo = *(const uint32_t *)(in + r * kRowBytes + cp * 4);
-        const uint32_t hi = *(const uint32_t *)(in + (r + 1) * kRowBytes + cp * 4);
-        w[0][i] = (lo & 0xffffu) | (hi << 16);
-        w[kCtCpt - 1][i] = (lo >> 16) | (hi & 0xffff0000u);
-      }
+      const uint32_t lo = *(const uint16_t *)(in + r * kRowBytes + c * 2);
+      const uint32_t hi = *(const uint16_t *)(in + (r + 1) * kRowBytes + c * 2);
+      w[i] = lo | (hi << 16);
     }
-#pragma unroll
-    for (int h = 0; h < kCtCpt; ++h) {
-      const int c = cp * kCtCpt + h;
-      uint32_t out[8];
-      uint8_t sbyte;
-      quantize_block(w[h], out, sbyte);
-      char *row = outc + c * kCtRows;
-      *(uint4 *)(row + (((2 * k) ^ (c & 7)) << 4)) = make_uint4(out[0], out[1], out[2], out[3]);
-      *(uint4 *)(row + (((2 * k + 1) ^ (c & 7)) << 4)) = make_uint4(out[4], out[5], out[6], out[7]);
-      sc[c * 4 + k] = sbyte;
-    }
+    uint32_t out[8];
+    uint8_t sbyte;
+    quantize_block(w, out, sbyte);
+    char *row = outc + c * kCtRows;
+    *(uint4 *)(row + (((2 * k) ^ (c & 7)) << 4)) = make_uint4(out[0], out[1], out[2], out[3]);
+    *(uint4 *)(row + (((2 * k + 1) ^ (c & 7)) << 4)) = make_uint4(out[4], out[5], out[6], out[7]);
+    sc[c * 4 + k] = sbyte;
   }
   // rowwise: thread (row t / 2, block t % 2) of the tile's valid rows
   if (row_data) {
