@@ -123,8 +123,9 @@ int check_buf(const void *p, int64_t T, const char *what) {
   return GL_OK;
 }
 
-// The bf16 GEMM addresses a 256-row stage of an operand with 32-bit byte offsets
-// from the stage's base, so a row may hold at most 2^22 elements.
+// The GEMMs address a 256-row stage of an operand with 32-bit byte offsets from
+// the stage's base, so a row may hold at most 2^22 elements (bf16, fp16; MXFP8
+// codes are bounded the same way).
 constexpr int64_t kMaxBf16Dim = (int64_t)1 << 22;
 
 int check_bf16_dims(gl_dtype d, int64_t K, int64_t N) {
@@ -202,6 +203,9 @@ int forward_impl(int num_groups, int64_t in_features, int64_t out_features, int6
       return fail(GL_ERR_DTYPE, "MXFP8 forward: out_dtype must be GL_BF16 or GL_F32");
     if (K % 128) return fail(GL_ERR_SHAPE, "MXFP8 forward needs in_features %% 128 == 0 (got %lld)", (long long)K);
     if (N % 8) return fail(GL_ERR_SHAPE, "MXFP8 forward needs out_features %% 8 == 0 (got %lld)", (long long)N);
+    if (K > kMaxBf16Dim || N > kMaxBf16Dim)
+      return fail(GL_ERR_SHAPE, "MXFP8 in_features and out_features must be at most %lld (got %lld, %lld)",
+                  (long long)kMaxBf16Dim, (long long)K, (long long)N);
     if (T > 0 && (!x_scale || ((uintptr_t)x_scale & 3u))) return fail(GL_ERR_ARG, "x_scale NULL or not 4-byte aligned");
     if ((w != nullptr) != (w_scale != nullptr) || (w_ptrs != nullptr) != (w_scale_ptrs != nullptr))
       return fail(GL_ERR_ARG, "weight scales must come in the same form as the weights");
@@ -505,6 +509,9 @@ int gl_dgrad_mxfp8(int num_groups, int64_t in_features, int64_t out_features, in
     return fail(GL_ERR_DTYPE, "gl_dgrad_mxfp8: out_dtype must be GL_BF16 or GL_F32");
   if (N % 128) return fail(GL_ERR_SHAPE, "MXFP8 dgrad needs out_features %% 128 == 0 (got %lld)", (long long)N);
   if (K % 8) return fail(GL_ERR_SHAPE, "MXFP8 dgrad needs in_features %% 8 == 0 (got %lld)", (long long)K);
+  if (K > kMaxBf16Dim || N > kMaxBf16Dim)
+    return fail(GL_ERR_SHAPE, "MXFP8 in_features and out_features must be at most %lld (got %lld, %lld)",
+                (long long)kMaxBf16Dim, (long long)K, (long long)N);
   if (!workspace) return fail(GL_ERR_ARG, "workspace is NULL");
   if (dx_rows < T) return fail(GL_ERR_SHAPE, "dgrad buffer has %lld rows, needs at least %lld", (long long)dx_rows,
                                (long long)T);

@@ -28,7 +28,7 @@
  *    per-group weights).  For biases both NULL means "no bias".
  *  - Buffers must be 16-byte aligned, and for bf16 K and N must be multiples of 8
  *    so every row starts on a 16-byte boundary, and at most 2^22 (GL_ERR_SHAPE
- *    otherwise).
+ *    otherwise; the MXFP8 forward and dgrad take the same 2^22 bound).
  *  - Output buffers may have more rows than T (`y_rows`, `dx_rows` >= T): only the
  *    packed valid rows [0, T) are written and any padded tail is left untouched
  *    (page "[PyTorch] Add optional caller-provided output/grad-input buffers to

@@ -68,6 +68,7 @@ def fwd(G=4, K=64, N=32, T=32, ind=gl.GL_BF16, outd=gl.GL_BF16, x=FAKE, xs=None,
     (dict(ind=gl.GL_E4M3, outd=gl.GL_BF16, K=96), -3),
     (dict(ind=gl.GL_E4M3, outd=gl.GL_BF16, K=128, xs=None), -1),
     (dict(ind=gl.GL_E4M3, outd=gl.GL_E4M3, K=128, xs=FAKE), -2),
+    (dict(ind=gl.GL_E4M3, outd=gl.GL_BF16, K=(1 << 22) + 128, xs=FAKE), -3),  # MXFP8 rows above 2^22 codes
     (dict(ws=None), -1),
 ])
 def test_forward_rejects(kw, code):
@@ -108,6 +109,8 @@ def test_other_entry_points_reject():
     assert lib.gl_dgrad_mxfp8(4, 64, 192, 32, gl.GL_BF16, FAKE, FAKE, FAKE, FAKE, FAKE2, 32, FAKE, None) == -3
     assert lib.gl_dgrad_mxfp8(4, 64, 256, 32, gl.GL_E4M3, FAKE, FAKE, FAKE, FAKE, FAKE2, 32, FAKE, None) == -2
     assert lib.gl_dgrad_mxfp8(4, 64, 256, 32, gl.GL_BF16, FAKE, FAKE, FAKE, FAKE, FAKE2, 16, FAKE, None) == -3
+    assert lib.gl_dgrad_mxfp8(4, 64, (1 << 22) + 128, 32, gl.GL_BF16, FAKE, FAKE, FAKE, FAKE, FAKE2, 32, FAKE,
+                              None) == -3
     assert lib.gl_wgrad_mxfp8(4, 64, 32, 1000, gl.GL_F32, FAKE, FAKE, FAKE, FAKE, ld - 128, FAKE2, None, 1, FAKE,
                               None) == -3
     assert lib.gl_wgrad_mxfp8(4, 64, 32, 1000, gl.GL_F32, FAKE, FAKE, FAKE, FAKE, ld, FAKE2, FAKE2, 1, FAKE,
