@@ -699,6 +699,16 @@ int run_entry(const gl_wgrad_queue::Entry &e, hipStream_t stream) {
                     e.dy, e.dw, e.dw_ptrs, e.accumulate, e.with_db, e.db_dtype, e.db, e.db_ptrs, e.workspace,
                     stream);
 }
+
+// No C++ exception may cross the C ABI: a record that cannot be stored is an error.
+int enqueue(gl_wgrad_queue *queue, const gl_wgrad_queue::Entry &e) {
+  try {
+    queue->pending.push_back(e);
+  } catch (const std::bad_alloc &) {
+    return fail(GL_ERR_HOST_MEMORY, "out of host memory");
+  }
+  return ok();
+}
 }  // namespace
 
 extern "C" {
@@ -706,7 +716,7 @@ extern "C" {
 int gl_wgrad_queue_create(gl_wgrad_queue **queue) {
   if (!queue) return fail(GL_ERR_ARG, "queue is NULL");
   *queue = new (std::nothrow) gl_wgrad_queue();
-  if (!*queue) return fail(GL_ERR_ARG, "out of host memory");
+  if (!*queue) return fail(GL_ERR_HOST_MEMORY, "out of host memory");
   return ok();
 }
 
@@ -741,8 +751,7 @@ int gl_wgrad_queue_put(gl_wgrad_queue *queue, int num_groups, int64_t in_feature
   GL_TRY(wgrad_impl(e.with_db ? "gl_wgrad_bgrad" : "gl_wgrad", e.G, e.K, e.N, e.T, e.in_dtype, e.out_dtype, e.x,
                     e.dy, e.dw, e.dw_ptrs, e.accumulate, e.with_db, e.db_dtype, e.db, e.db_ptrs, e.workspace,
                     nullptr, false));
-  queue->pending.push_back(e);
-  return ok();
+  return enqueue(queue, e);
 }
 
 int gl_wgrad_queue_put_mxfp8(gl_wgrad_queue *queue, int num_groups, int64_t in_features, int64_t out_features,
@@ -768,8 +777,7 @@ int gl_wgrad_queue_put_mxfp8(gl_wgrad_queue *queue, int num_groups, int64_t in_f
   e.dw_ptrs = dw_ptrs;
   e.accumulate = accumulate;
   e.workspace = workspace;
-  queue->pending.push_back(e);
-  return ok();
+  return enqueue(queue, e);
 }
 
 int gl_wgrad_queue_size(const gl_wgrad_queue *queue) {

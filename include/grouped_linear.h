@@ -64,7 +64,8 @@ enum {
   GL_ERR_DTYPE = -2,       /* element type not valid for this call */
   GL_ERR_SHAPE = -3,       /* output capacity < total_rows, K/N alignment, K % 32 for MXFP8 */
   GL_ERR_UNSUPPORTED = -4, /* reserved: recognised but not provided by this build */
-  GL_ERR_HIP = -5          /* a HIP runtime call failed */
+  GL_ERR_HIP = -5,         /* a HIP runtime call failed */
+  GL_ERR_HOST_MEMORY = -6  /* a deferred-wgrad queue could not allocate its host record */
 };
 
 /* Status word bits written by gl_offsets (read back with gl_read_status). */
@@ -402,6 +403,7 @@ int gl_grouped_mlp_backward(int num_groups, int64_t in_features, int64_t ffn_fea
  * stream (db and db_ptrs both NULL: plain gl_wgrad, db_dtype ignored), and
  * gl_wgrad_queue_put_mxfp8 those of gl_wgrad_mxfp8.  Every check of that entry
  * point runs at put time, with the same errors; on an error nothing is queued.
+ * A put or create that cannot allocate its host record returns GL_ERR_HOST_MEMORY.
  * Nothing is launched and no device memory is read by a put.  The queue keeps the
  * pointers: the caller keeps every buffer, pointer array and the workspace alive
  * and unchanged until the call has run, and the workspace must still hold the
