@@ -21,9 +21,14 @@ from typing import Optional, Sequence, Union
 import torch
 
 __all__ = [
-    "GL_F32", "GL_BF16", "GL_F16", "GL_E4M3", "GLError", "library_path", "load",
-    "gl_workspace_size", "new_workspace", "gl_offsets", "gl_read_status", "gl_forward",
-    "gl_dgrad", "gl_wgrad", "gl_bgrad", "gl_group_quantize_mxfp8", "gl_version", "WgradQueue",
+    "GL_F32", "GL_BF16", "GL_F16", "GL_E4M3", "GLError", "library_path", "load", "gl_version",
+    "gl_workspace_size", "new_workspace", "workspace_offsets", "gl_offsets", "gl_read_status",
+    "gl_forward", "gl_dgrad", "gl_wgrad", "gl_wgrad_bgrad", "gl_bgrad",
+    "gl_group_quantize_mxfp8", "gl_colwise_ld", "gl_group_quantize_mxfp8_colwise",
+    "gl_group_quantize_mxfp8_rowwise_colwise", "gl_quantize_mxfp8_colwise_weights",
+    "gl_offsets_quantize_mxfp8", "gl_offsets_quantize_mxfp8_rowwise_colwise", "gl_quantize_mxfp8_weights",
+    "gl_dgrad_mxfp8", "gl_wgrad_mxfp8", "gl_swiglu_forward", "gl_swiglu_backward",
+    "gl_grouped_mlp_forward", "gl_grouped_mlp_backward", "WgradQueue",
 ]
 
 GL_F32, GL_BF16, GL_F16, GL_E4M3 = 0, 1, 2, 3

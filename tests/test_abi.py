@@ -37,6 +37,19 @@ def test_library_exports_every_declared_symbol():
     assert not missing
 
 
+def test_binding_covers_every_declared_entry_point():
+    """Every C entry point has a Python function of the same name (the deferred-wgrad
+    queue's calls are the methods of WgradQueue; the error and workspace-pointer
+    helpers are used inside the binding)."""
+    internal = {"gl_last_error", "gl_workspace_offsets"}
+    names = [n for n in declared_symbols() if not n.startswith("gl_wgrad_queue_") and n not in internal]
+    assert not [n for n in names if n not in gl.__all__ or not callable(getattr(gl, n, None))]
+    for m in ["put", "put_mxfp8", "run_next", "flush", "clear", "close", "__len__"]:
+        assert callable(getattr(gl.WgradQueue, m))
+    lib = gl.load()
+    assert not [n for n in declared_symbols() if getattr(lib, n).argtypes is None], "entry point without a signature"
+
+
 def test_version_and_workspace_size():
     lib = gl.load()
     assert b"gfx950" in lib.gl_version()
