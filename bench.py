@@ -543,7 +543,10 @@ def main():
         "config": {"workload": wl.name, "num_groups": wl.G, "in_features": wl.K, "out_features": wl.N,
                    "total_rows": wl.T, "m_splits": m.tolist(), "bias": True,
                    "step": "offsets+forward(+bias)+dgrad+wgrad(+bias grad, one pass over dy)",
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU",
+                   "inputs_sha256_16": {"m_splits": synth.checksum(m), "x": synth.checksum(host_inputs[0]),
+                                        "W": synth.checksum(host_inputs[1]), "b": synth.checksum(host_inputs[2]),
+                                        "dy": synth.checksum(host_inputs[3])}},
         "pct_bf16_peak": round(100 * r["value"] / PEAK_BF16_TFLOPS, 2),
         "passes": r["passes"],
         "roofline": r["roofline"],

@@ -205,6 +205,19 @@ def main_grad(wl: Workload) -> torch.Tensor:
     return out
 
 
+def checksum(t) -> str:
+    """First 16 hex digits of the SHA-256 of a tensor's or array's raw bytes (row-major),
+    recorded beside results so that a run's inputs can be matched to this recipe."""
+    import hashlib
+    if isinstance(t, torch.Tensor):
+        t = t.detach().cpu().contiguous()
+        t = t.view(torch.int16) if t.dtype in (torch.bfloat16, torch.float16) else t
+        a = t.numpy()
+    else:
+        a = np.ascontiguousarray(t)
+    return hashlib.sha256(a.tobytes()).hexdigest()[:16]
+
+
 def special_bf16_block_values() -> torch.Tensor:
     """Every finite bfloat16 bit pattern, as a bf16 tensor (for exhaustive quantizer cases)."""
     bits = torch.arange(0, 1 << 16, dtype=torch.int32).to(torch.int16)
