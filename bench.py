@@ -110,9 +110,9 @@ def summarize_pmc(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
 
     ff = copy_factor(copy_fetch_csv, "FETCH_SIZE")
     fw = copy_factor(copy_write_csv, "WRITE_SIZE")
-    # entries of other workloads survive; this workload's passes are rewritten
+    # this workload's passes get new traffic fields; fields of a clock run on the same
+    # source survive, anything taken on another source is dropped
     table = json.load(open(TRAFFIC_JSON)) if os.path.exists(TRAFFIC_JSON) else {}
-    table = {k: v for k, v in table.items() if k.split(":")[0] not in set(PASS_WORKLOAD.values())}
     sha = source_hash(GEMM_SRCS)
     lines = [f"copy calibration ({COPY_BYTES} B): FETCH_SIZE x{ff:.3f}, WRITE_SIZE x{fw:.3f}"]
     for name, args in PASS_KERNELS.items():
@@ -123,15 +123,75 @@ def summarize_pmc(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
         fb = sum(fv) / len(fv) * 1024.0 * ff
         wb = sum(wv) / len(wv) * 1024.0 * fw
         workload = PASS_WORKLOAD[name]
-        table[f"{workload}:{name}"] = {"bytes_per_launch": round(fb + wb), "fetch_bytes": round(fb),
-                                        "write_bytes": round(wb), "launches": len(fv), "source_sha": sha,
-                                        "fetch_factor": round(ff, 4), "write_factor": round(fw, 4)}
+        entry = table.get(f"{workload}:{name}", {})
+        if entry.get("source_sha") != sha:
+            entry = {}
+        entry.update({"bytes_per_launch": round(fb + wb), "fetch_bytes": round(fb), "write_bytes": round(wb),
+                      "launches": len(fv), "source_sha": sha, "fetch_factor": round(ff, 4),
+                      "write_factor": round(fw, 4)})
+        table[f"{workload}:{name}"] = entry
         lines.append(f"{workload}:{name}: fetch {fb / 1e9:.3f} GB + write {wb / 1e9:.3f} GB per launch "
                      f"({len(fv)} launches)")
     os.makedirs(os.path.dirname(TRAFFIC_JSON), exist_ok=True)
     with open(TRAFFIC_JSON, "w") as f:
         json.dump(table, f, indent=1, sort_keys=True)
     print("\n".join(lines))
+
+
+CLOCK_COUNTERS = "GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE"
+N_XCD, N_CU, BF16_FLOP_PER_CLK_CU = 8, 256, 4096
+
+
+def summarize_clock(pmc_csv):
+    """Fold one rocprofv3 --pmc run of the benchmark with CLOCK_COUNTERS into the
+    traffic table: the engine clock each pass's GEMM ran at (GRBM_GUI_ACTIVE is
+    summed over the XCDs, so cycles = value / 8, divided by the dispatch's duration),
+    the flops it reached as a fraction of the dense bf16 peak at that clock, the MFMA
+    busy share of SIMD-cycles, and LDS bank-conflict cycles per LDS-active cycle."""
+    table = json.load(open(TRAFFIC_JSON))
+    sha = source_hash(GEMM_SRCS)
+    rows = {}
+    for counter in CLOCK_COUNTERS.split():
+        rows[counter] = _pmc_rows(pmc_csv, counter)
+    import synth
+
+    lines = [f"{'workload:pass':44s} {'sclk GHz':>9s} {'frac@sclk':>10s} {'MFMA busy':>10s} {'LDS conflicts':>14s}"]
+    for name, args in PASS_KERNELS.items():
+        sel = {c: [(v, d) for k, v, d in r if args in k] for c, r in rows.items()}
+        if not all(sel.values()):
+            continue
+        mean = {c: sum(v for v, _ in x) / len(x) for c, x in sel.items()}
+        dur_ns = sum(d for _, d in sel["GRBM_GUI_ACTIVE"]) / len(sel["GRBM_GUI_ACTIVE"])
+        cycles = mean["GRBM_GUI_ACTIVE"] / N_XCD
+        sclk = cycles / dur_ns
+        wl = synth.WORKLOADS[PASS_WORKLOAD[name]]
+        flops = 2.0 * wl.T * wl.N * wl.K
+        frac = flops / (dur_ns * 1e-9) / (N_CU * BF16_FLOP_PER_CLK_CU * sclk * 1e9)
+        mfma = mean["SQ_VALU_MFMA_BUSY_CYCLES"] / (cycles * N_CU * 4)
+        lds = mean["SQ_LDS_BANK_CONFLICT"] / max(mean["SQ_LDS_IDX_ACTIVE"], 1.0)
+        key = f"{PASS_WORKLOAD[name]}:{name}"
+        entry = table.get(key, {})
+        if entry.get("source_sha") != sha:
+            entry = {"source_sha": sha}
+        entry.update({"sclk_ghz": round(sclk, 3), "frac_of_peak_at_sclk": round(frac, 4),
+                      "mfma_busy_frac": round(mfma, 4), "lds_bank_conflict_per_active": round(lds, 5)})
+        table[key] = entry
+        lines.append(f"{key:44s} {sclk:9.3f} {frac:10.3f} {mfma:10.3f} {lds:14.5f}")
+    with open(TRAFFIC_JSON, "w") as f:
+        json.dump(table, f, indent=1, sort_keys=True)
+    print("\n".join(lines))
+
+
+def clock_for(kernel: str, workload: str):
+    """Engine clock and clock-adjusted peak fraction from a committed counter run, if
+    it was taken on the current kernel source; otherwise None."""
+    try:
+        rec = json.load(open(TRAFFIC_JSON))[f"{workload}:{kernel}"]
+    except Exception:
+        return None
+    if rec.get("source_sha") != source_hash(GEMM_SRCS) or "sclk_ghz" not in rec:
+        return None
+    return rec
 
 
 class EventTimer:
@@ -196,10 +256,34 @@ def cpu_baseline(wl, m, x, w, b, dy, min_s=10.0):
             rows += hi - lo
             if t_total >= min_s:
                 break
+    # context only (not the oracle): the same three products per group in torch fp32 on the CPU
+    import torch
+
+    g = next(i for i in range(wl.G) if m[i])
+    lo, hi = int(off[g]), int(off[g + 1])
+    xs, dys, wg = x[lo:hi].float(), dy[lo:hi].float(), w[g].float()
+    bg = b[g].float() if b is not None else 0.0
+    f32_flops, f32_s = 0.0, 0.0
+    while f32_s < 2.0:
+        t0 = time.perf_counter()
+        _ = xs @ wg.T + bg
+        _ = dys @ wg
+        _ = dys.T @ xs
+        f32_s += time.perf_counter() - t0
+        f32_flops += 6.0 * (hi - lo) * wl.N * wl.K
+    model = ""
+    try:
+        model = next(l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo") if l.startswith("model name"))
+    except Exception:  # pragma: no cover
+        pass
     return {"value": round(done_flops / t_total / 1e12, 4), "unit": "TFLOP/s", "cores": int(cores),
             "kind": "oracle",
             "sample": f"oracle fp64 forward+dgrad+wgrad, group by group, over {rows} rows of the same workload "
-                      f"({rows / wl.T:.2f}x its {wl.T} rows), {t_total:.1f} s"}
+                      f"({rows / wl.T:.2f}x its {wl.T} rows), {t_total:.1f} s",
+            "cpu_model": model, "host_cpus": os.cpu_count(),
+            "context_torch_f32": {"value": round(f32_flops / f32_s / 1e12, 4), "unit": "TFLOP/s",
+                                  "threads": torch.get_num_threads(),
+                                  "sample": f"group {g} ({hi - lo} rows), {f32_s:.1f} s"}}
 
 
 def bench_bf16(torch, gl, synth, steps, warmup):
@@ -287,6 +371,13 @@ def bench_bf16(torch, gl, synth, steps, warmup):
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic_for(dom, wl.name),
                 "algorithmic_flops_per_launch": flops_pass}
+    clk = clock_for(dom, wl.name)
+    if clk:
+        # the same achieved rate against the peak at the clock the counter run measured
+        peak_sclk = N_CU * BF16_FLOP_PER_CLK_CU * clk["sclk_ghz"] * 1e9 / 1e12
+        roofline["measured_sclk_ghz"] = clk["sclk_ghz"]
+        roofline["frac_at_measured_sclk"] = round(achieved / peak_sclk, 4)
+        roofline["mfma_busy_frac"] = clk["mfma_busy_frac"]
     return wl, m, (x, w, b, dy), {
         "value": value, "ms_per_step": ms_step, "passes": passes, "roofline": roofline,
         "fwd_dgrad_wgrad_ms": sum(per[k] for k in GEMM_PASSES),
@@ -507,15 +598,20 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB copy (counter calibration)")
+    ap.add_argument("--summarize-clock", metavar="PMC_CSV",
+                    help=f"fold a rocprofv3 --pmc run with {CLOCK_COUNTERS} into the traffic table, then exit")
     ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="fold rocprofv3 FETCH_SIZE/WRITE_SIZE CSVs into the traffic table, then exit")
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
         return
+    if args.summarize_clock:
+        summarize_clock(args.summarize_clock)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(groups would shard across GPUs as expert parallelism; see the design notes).", file=sys.stderr)
+              "(groups would shard across GPUs as expert parallelism).", file=sys.stderr)
         sys.exit(2)
 
     if args.calibrate_copy:
