@@ -139,14 +139,21 @@ def summarize_pmc(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
 
 
 CLOCK_COUNTERS = "GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE"
-N_XCD, N_CU, BF16_FLOP_PER_CLK_CU = 8, 256, 4096
+N_XCD, N_CU, BF16_FLOP_PER_CLK_CU, FP8_FLOP_PER_CLK_CU = 8, 256, 4096, 8192
+# (table key, kernel-name fragment, workload, dense flop per clock per CU) of every GEMM
+# the clock run covers; the MXFP8 forward and dgrad share one kernel and one shape
+CLOCK_KERNELS = [(f"bf16_train_g8_k4096_n14336:{k}", v, "bf16_train_g8_k4096_n14336", BF16_FLOP_PER_CLK_CU)
+                 for k, v in PASS_KERNELS.items()] + [
+    ("mxfp8_fwd_g32_k4096_n4096:mx_forward_and_dgrad", "gemm_mxfp8_kernel<0>", "mxfp8_fwd_g32_k4096_n4096",
+     FP8_FLOP_PER_CLK_CU),
+    ("mxfp8_fwd_g32_k4096_n4096:mx_wgrad", "gemm_mxfp8_kernel<2>", "mxfp8_fwd_g32_k4096_n4096", FP8_FLOP_PER_CLK_CU)]
 
 
 def summarize_clock(pmc_csv):
     """Fold one rocprofv3 --pmc run of the benchmark with CLOCK_COUNTERS into the
     traffic table: the engine clock each pass's GEMM ran at (GRBM_GUI_ACTIVE is
     summed over the XCDs, so cycles = value / 8, divided by the dispatch's duration),
-    the flops it reached as a fraction of the dense bf16 peak at that clock, the MFMA
+    the flops it reached as a fraction of the dense peak of its type at that clock, the MFMA
     busy share of SIMD-cycles, and LDS bank-conflict cycles per LDS-active cycle."""
     table = json.load(open(TRAFFIC_JSON))
     sha = source_hash(GEMM_SRCS)
@@ -155,8 +162,8 @@ def summarize_clock(pmc_csv):
         rows[counter] = _pmc_rows(pmc_csv, counter)
     import synth
 
-    lines = [f"{'workload:pass':44s} {'sclk GHz':>9s} {'frac@sclk':>10s} {'MFMA busy':>10s} {'LDS conflicts':>14s}"]
-    for name, args in PASS_KERNELS.items():
+    lines = [f"{'workload:pass':48s} {'sclk GHz':>9s} {'frac@sclk':>10s} {'MFMA busy':>10s} {'LDS conflicts':>14s}"]
+    for key, args, workload, flop_clk in CLOCK_KERNELS:
         sel = {c: [(v, d) for k, v, d in r if args in k] for c, r in rows.items()}
         if not all(sel.values()):
             continue
@@ -164,19 +171,18 @@ def summarize_clock(pmc_csv):
         dur_ns = sum(d for _, d in sel["GRBM_GUI_ACTIVE"]) / len(sel["GRBM_GUI_ACTIVE"])
         cycles = mean["GRBM_GUI_ACTIVE"] / N_XCD
         sclk = cycles / dur_ns
-        wl = synth.WORKLOADS[PASS_WORKLOAD[name]]
+        wl = synth.WORKLOADS[workload]
         flops = 2.0 * wl.T * wl.N * wl.K
-        frac = flops / (dur_ns * 1e-9) / (N_CU * BF16_FLOP_PER_CLK_CU * sclk * 1e9)
+        frac = flops / (dur_ns * 1e-9) / (N_CU * flop_clk * sclk * 1e9)
         mfma = mean["SQ_VALU_MFMA_BUSY_CYCLES"] / (cycles * N_CU * 4)
         lds = mean["SQ_LDS_BANK_CONFLICT"] / max(mean["SQ_LDS_IDX_ACTIVE"], 1.0)
-        key = f"{PASS_WORKLOAD[name]}:{name}"
         entry = table.get(key, {})
         if entry.get("source_sha") != sha:
             entry = {"source_sha": sha}
         entry.update({"sclk_ghz": round(sclk, 3), "frac_of_peak_at_sclk": round(frac, 4),
                       "mfma_busy_frac": round(mfma, 4), "lds_bank_conflict_per_active": round(lds, 5)})
         table[key] = entry
-        lines.append(f"{key:44s} {sclk:9.3f} {frac:10.3f} {mfma:10.3f} {lds:14.5f}")
+        lines.append(f"{key:48s} {sclk:9.3f} {frac:10.3f} {mfma:10.3f} {lds:14.5f}")
     with open(TRAFFIC_JSON, "w") as f:
         json.dump(table, f, indent=1, sort_keys=True)
     print("\n".join(lines))
@@ -447,6 +453,11 @@ def bench_mxfp8(torch, gl, synth, steps, warmup):
         out[f"{k}_ms"] = round(per[k], 4)
         out[f"{k}_tflops"] = tf(k)
         out[f"{k}_pct_fp8_peak"] = round(100 * tf(k) / PEAK_FP8_TFLOPS, 2)
+        # against the dense fp8 peak at the clock a committed counter run measured
+        clk = clock_for("mx_wgrad" if k == "mx_wgrad" else "mx_forward_and_dgrad", wl.name)
+        if clk:
+            peak_sclk = N_CU * FP8_FLOP_PER_CLK_CU * clk["sclk_ghz"] * 1e9 / 1e12
+            out[f"{k}_pct_fp8_peak_at_measured_sclk"] = round(100 * tf(k) / peak_sclk, 2)
     out["quantize_gbs"] = {"x": gbs("quantize_x", row_bytes(T, K)), "w": gbs("quantize_w", row_bytes(G * N, K)),
                            "dy": gbs("quantize_dy", row_bytes(T, N)),
                            "x_colwise": gbs("quantize_x_colwise", col_bytes(T, K)),
