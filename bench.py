@@ -96,6 +96,24 @@ def _pmc_rows(path, counter):
     return out
 
 
+def _mx_traffic_kernels():
+    """(table key, kernel-name fragment, algorithmic bytes) of the MXFP8 block's kernels
+    that run at a single shape there (the others mix shapes in one average): codes
+    1 B and one E8M0 byte per 32 codes; the columnwise layout holds every group's rows
+    padded to 128."""
+    import synth
+
+    wl = synth.WORKLOADS["mxfp8_fwd_g32_k4096_n4096"]
+    G, K, N, T = wl.G, wl.K, wl.N, wl.T
+    ld = (T + 127 * G + 127) // 128 * 128
+    codes = lambda r, c: r * c + r * c // 32
+    return [(f"{wl.name}:offsets_quantize_x", "offsets_quantize_mxfp8_kernel", T * K * 2 + codes(T, K) + 8 * G),
+            (f"{wl.name}:offsets_quantize_x_both", "quantize_mxfp8_colwise_tile_kernel<true>",
+             T * K * 2 + codes(T, K) + codes(K, ld) + 8 * G),
+            (f"{wl.name}:mx_forward_and_dgrad", "gemm_mxfp8_kernel<0>", codes(T, K) + codes(G * N, K) + T * N * 2),
+            (f"{wl.name}:mx_wgrad", "gemm_mxfp8_kernel<2>", codes(N, ld) + codes(K, ld) + G * N * K * 2)]
+
+
 def summarize_pmc(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
     """Turn two rocprofv3 --pmc runs of the benchmark (FETCH_SIZE, WRITE_SIZE, in KiB
     per dispatch) into HBM bytes per launch of each pass's GEMM kernel, each counter
@@ -132,6 +150,26 @@ def summarize_pmc(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
         table[f"{workload}:{name}"] = entry
         lines.append(f"{workload}:{name}: fetch {fb / 1e9:.3f} GB + write {wb / 1e9:.3f} GB per launch "
                      f"({len(fv)} launches)")
+    # the MXFP8 block's single-shape kernels, when the runs included it: bytes per launch
+    # and the rate they imply over the same run's dispatch durations
+    for key, frag, alg in _mx_traffic_kernels():
+        fr = [(v, d) for k, v, d in _pmc_rows(fetch_csv, "FETCH_SIZE") if frag in k]
+        wr = [(v, d) for k, v, d in _pmc_rows(write_csv, "WRITE_SIZE") if frag in k]
+        if not fr or not wr:
+            continue
+        fb = sum(v for v, _ in fr) / len(fr) * 1024.0 * ff
+        wb = sum(v for v, _ in wr) / len(wr) * 1024.0 * fw
+        dur = (sum(d for _, d in fr) + sum(d for _, d in wr)) / (len(fr) + len(wr)) * 1e-9
+        entry = table.get(key, {})
+        if entry.get("source_sha") != sha:
+            entry = {}
+        entry.update({"bytes_per_launch": round(fb + wb), "fetch_bytes": round(fb), "write_bytes": round(wb),
+                      "algorithmic_bytes": alg, "launches": len(fr), "source_sha": sha,
+                      "counter_gbs": round((fb + wb) / dur / 1e9, 1), "fetch_factor": round(ff, 4),
+                      "write_factor": round(fw, 4)})
+        table[key] = entry
+        lines.append(f"{key}: fetch {fb / 1e9:.3f} GB + write {wb / 1e9:.3f} GB per launch, algorithmic "
+                     f"{alg / 1e9:.3f} GB, {(fb + wb) / dur / 1e9:.0f} GB/s over the counter run's durations")
     os.makedirs(os.path.dirname(TRAFFIC_JSON), exist_ok=True)
     with open(TRAFFIC_JSON, "w") as f:
         json.dump(table, f, indent=1, sort_keys=True)
