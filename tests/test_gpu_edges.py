@@ -58,6 +58,54 @@ def test_1300_groups_mostly_tiny_or_empty():
     assert_close(db, oracle.bgrad(DY, m), TOL_BF16, "db")
 
 
+class LazyGroups:
+    """Per-group float64 views of a stacked CPU tensor, converted when asked for."""
+
+    def __init__(self, t):
+        self.t = t
+
+    def __len__(self):
+        return self.t.shape[0]
+
+    def __getitem__(self, g):
+        return self.t[g].double().numpy()
+
+
+def test_100k_groups_offsets_and_passes():
+    """100 000 groups, 95% empty, a few large ones: the scan's chunk carries over 98
+    workgroup-sized chunks (offsets bit-exact against the oracle's), and the GEMMs'
+    group lookup over a tile table that long."""
+    rng = np.random.default_rng(43)
+    G, K, N = 100_000, 32, 40
+    m = rng.integers(1, 4, G) * (rng.random(G) < 0.05)
+    m[[0, 1023, 1024, 50_000, G - 1]] = [0, 257, 1, 600, 3]
+    T = int(m.sum())
+    say(f"100k groups: T={T}, empty={int((m == 0).sum())}")
+    ws = workspace_for(m)
+    torch.cuda.synchronize()
+    assert gl.gl_read_status(ws) == 0
+    assert np.array_equal(gl.workspace_offsets(ws, G).cpu().numpy(), oracle.offsets(m.tolist(), G, T))
+    g = torch.Generator().manual_seed(44)
+    x, dy = torch.randn(T, K, generator=g).to(torch.bfloat16), torch.randn(T, N, generator=g).to(torch.bfloat16)
+    w = (torch.randn(G, N, K, generator=g) * 0.05).to(torch.bfloat16)
+    xd, dyd, wd = x.to(DEV), dy.to(DEV), w.to(DEV)
+    y = nan_tail(T + 5, N, T, torch.bfloat16, DEV)
+    gl.gl_forward(xd, wd, y, ws)
+    dx = torch.empty(T, K, dtype=torch.bfloat16, device=DEV)
+    gl.gl_dgrad(dyd, wd, dx, ws)
+    dw = torch.full((G, N, K), float("nan"), dtype=torch.bfloat16, device=DEV)
+    gl.gl_wgrad(xd, dyd, dw, ws)
+    torch.cuda.synchronize()
+    X, DY = to64(x), to64(dy)
+    W = LazyGroups(w)
+    assert_close(y[:T], oracle.forward(X, W, None, m), TOL_BF16, "y")
+    assert torch.isnan(y[T:]).all()
+    assert_close(dx, oracle.dgrad(DY, W, m), TOL_BF16, "dx")
+    groups = [0, 1, 1023, 1024, 50_000, G - 1] + [int(i) for i in np.nonzero(m)[0][:5]]
+    assert_close(dw[groups], oracle.wgrad(X, DY, m, groups=groups), TOL_BF16, "dW (selected groups)")
+    assert not dw[torch.from_numpy(np.nonzero(m == 0)[0]).to(DEV)].float().abs().sum().item()
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_zero_total_rows(dtype):
     G, K, N = 3, 64, 96
