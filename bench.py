@@ -35,8 +35,10 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 / MXFP8 MFMA
 PEAK_HBM_GBS = 8000.0
 METRIC = "grouped GEMM TFLOP/s (fwd+dgrad+wgrad) and % of MFMA peak, bf16 & MXFP8"
+# every source the GEMM kernels are compiled from (the counter records are tied to them)
 GEMM_SRCS = [os.path.join(ROOT, "grouped_gemm_gl_amd", "csrc", f)
-             for f in ("gl_gemm_tile.hpp", "gl_gemm_bf16.hip", "gl_gemm_mxfp8.hip")]
+             for f in ("gl_gemm_tile.hpp", "gl_gemm_bf16.hip", "gl_gemm_mxfp8.hip", "gl_common.hpp",
+                       "gl_offsets.hpp")]
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 # kernel-name fragment of each pass's GEMM (template arguments <A K-major, B K-major, mode, fp16>)
 PASS_KERNELS = {"forward": "gemm_bf16_kernel<true, true, 0, false, false>",
