@@ -268,6 +268,15 @@ class EventTimer:
             out[k] = {"median": round(pick(0.5), 4), "p10": round(pick(0.1), 4), "p90": round(pick(0.9), 4)}
         return out
 
+    def sum_spread_ms(self, names):
+        """mean, median, p10 and p90 of the per-step sums of the named passes (their
+        i-th samples belong to the same step)."""
+        cols = [[s.elapsed_time(e) for s, e in self.pairs[k]] for k in names]
+        xs = sorted(sum(v) for v in zip(*cols))
+        pick = lambda q: xs[min(len(xs) - 1, max(0, int(round(q * (len(xs) - 1)))))]
+        return {"ms": round(sum(xs) / len(xs), 4), "ms_median": round(pick(0.5), 4), "ms_p10": round(pick(0.1), 4),
+                "ms_p90": round(pick(0.9), 4)}
+
 
 def cpu_baseline(wl, m, x, w, b, dy, min_s=10.0):
     """The oracle, as it stands, on whole groups of the same workload, cycling
@@ -424,9 +433,12 @@ def bench_bf16(torch, gl, synth, steps, warmup):
         roofline["measured_sclk_ghz"] = clk["sclk_ghz"]
         roofline["frac_at_measured_sclk"] = round(achieved / peak_sclk, 4)
         roofline["mfma_busy_frac"] = clk["mfma_busy_frac"]
+    fdw = timer.sum_spread_ms(GEMM_PASSES)
+    fdw["tflops"] = round(3 * flops_pass / (fdw["ms"] * 1e-3) / 1e12, 2)
+    fdw["pct_bf16_peak"] = round(100 * fdw["tflops"] / PEAK_BF16_TFLOPS, 2)
     return wl, m, (x, w, b, dy), {
         "value": value, "ms_per_step": ms_step, "passes": passes, "roofline": roofline,
-        "fwd_dgrad_wgrad_ms": sum(per[k] for k in GEMM_PASSES),
+        "fwd_dgrad_wgrad": fdw,
     }
 
 
@@ -696,6 +708,7 @@ def main():
                                         "dy": synth.checksum(host_inputs[3])}},
         "pct_bf16_peak": round(100 * r["value"] / PEAK_BF16_TFLOPS, 2),
         "passes": r["passes"],
+        "fwd_dgrad_wgrad_events": r["fwd_dgrad_wgrad"],
         "roofline": r["roofline"],
     }
     if not args.no_mxfp8:
