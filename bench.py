@@ -524,6 +524,11 @@ def bench_mxfp8(torch, gl, synth, steps, warmup):
                         "offsets_quantize_x_both_ways": round(per["offsets_quantize_x_both"] * 1e3, 1),
                         "quantize_x": round(per["quantize_x"] * 1e3, 1),
                         "weights_with_noop_flag_set": round(per["weights_noop"] * 1e3, 1)}
+    # forward alone, end to end: offsets with x's rowwise quantization (one launch), the
+    # cached-weight refresh skipped by its flag, the MX GEMM
+    fwd_e2e = per["offsets_quantize_x"] + per["weights_noop"] + per["mx_forward"]
+    out["forward_with_quantize_ms"] = round(fwd_e2e, 4)
+    out["forward_with_quantize_tflops"] = round(flops / (fwd_e2e * 1e-3) / 1e12, 2)
     step = ("offsets_quantize_x_both", "weights_noop", "mx_forward", "quantize_dy_both", "mx_dgrad", "mx_wgrad")
     step_ms = sum(per[k] for k in step)
     out["mx_step_ms"] = round(step_ms, 4)
