@@ -320,9 +320,13 @@ def test_quantize_every_scaled_value_bit_exact(e):
     assert np.array_equal(data.cpu().numpy(), q)
 
 
+@pytest.mark.parametrize("out", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("G,K,N,m", [(3, 256, 264, [0, 300, 77]), (4, 128, 512, [256, 1, 0, 257])])
-def test_mxfp8_forward(G, K, N, m):
-    say(f"mxfp8 forward G={G} K={K} N={N} m={m}")
+def test_mxfp8_forward(G, K, N, m, out):
+    """bf16 output at the bf16 bound; fp32 output (bias added to the fp32 accumulator,
+    stored unrounded) at the fp32 bound, since the products of decoded codes are
+    exact and only the fp32 summation order differs from the oracle."""
+    say(f"mxfp8 forward G={G} K={K} N={N} m={m} out={out}")
     x, w, b, _, _ = rand_case(8, G, K, N, m, torch.bfloat16, scale_w=0.02)
     T = sum(m)
     ws = workspace_for(m, T)
@@ -332,17 +336,17 @@ def test_mxfp8_forward(G, K, N, m):
     wq = torch.empty(G, N, K, dtype=torch.uint8, device=DEV)
     wsc = torch.empty(G, N, K // 32, dtype=torch.uint8, device=DEV)
     gl.gl_group_quantize_mxfp8(w.to(DEV), wq, wsc)
-    y = nan_tail(T + 11, N, T, torch.bfloat16, DEV)
-    gl.gl_forward(xq, wq, y, ws, x_scale=xs, w_scale=wsc, bias=b.to(DEV))
-    y2 = torch.empty(T, N, dtype=torch.bfloat16, device=DEV)
-    gl.gl_forward(xq, [wq[g] for g in range(G)], y2, ws, x_scale=xs, w_scale=[wsc[g] for g in range(G)],
-                  bias=b.to(DEV))
+    y = nan_tail(T + 11, N, T, out, DEV)
+    bo = b.to(out).to(DEV)  # the bias comes in the output type (bf16 -> fp32 is exact)
+    gl.gl_forward(xq, wq, y, ws, x_scale=xs, w_scale=wsc, bias=bo)
+    y2 = torch.empty(T, N, dtype=out, device=DEV)
+    gl.gl_forward(xq, [wq[g] for g in range(G)], y2, ws, x_scale=xs, w_scale=[wsc[g] for g in range(G)], bias=bo)
     torch.cuda.synchronize()
     oq, os_ = oracle.quantize_mxfp8(to64(x))
     assert np.array_equal(xq.cpu().numpy(), oq) and np.array_equal(xs.cpu().numpy(), os_)
     wqs = [oracle.quantize_mxfp8(to64(w[g])) for g in range(G)]
     assert np.array_equal(wq.cpu().numpy(), np.stack([a for a, _ in wqs]))
     ref = oracle.forward_mxfp8(oq, os_, [a for a, _ in wqs], [c for _, c in wqs], to64(b), m)
-    assert_close(y[:T], ref, TOL_BF16, "MXFP8 forward")
+    assert_close(y[:T], ref, TOL_BF16 if out == torch.bfloat16 else TOL_F32, "MXFP8 forward")
     assert torch.isnan(y[T:]).all()
     assert_bits_equal(y[:T], y2, "MXFP8 stacked vs per-group weights")
