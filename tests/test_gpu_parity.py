@@ -350,3 +350,49 @@ def test_mxfp8_forward(G, K, N, m, out):
     assert_close(y[:T], ref, TOL_BF16 if out == torch.bfloat16 else TOL_F32, "MXFP8 forward")
     assert torch.isnan(y[T:]).all()
     assert_bits_equal(y[:T], y2, "MXFP8 stacked vs per-group weights")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("per_group", [False, True])
+def test_wgrad_accumulate_into_16bit(dtype, per_group):
+    """accumulate=1 into a weight gradient of the input type (not an fp32 main_grad):
+    the stored value is read, the fp32 sum added and the result rounded once; an
+    empty group's gradient stays bit-identical."""
+    G, K, N, m = 3, 136, 200, [0, 300, 77]
+    say(f"wgrad accumulate into {dtype} per_group={per_group}")
+    x, _, _, dy, mg = rand_case(31, G, K, N, m, dtype)
+    mg16 = mg.to(dtype)
+    ws = workspace_for(m, sum(m))
+    dw = [t.to(DEV) for t in mg16] if per_group else mg16.to(DEV)
+    gl.gl_wgrad(x.to(DEV), dy.to(DEV), dw, ws, accumulate=True)
+    torch.cuda.synchronize()
+    got = torch.stack(dw) if per_group else dw
+    assert_close(got, oracle.wgrad(to64(x), to64(dy), m, main_grad=to64(mg16), accumulate=True),
+                 TOL_BF16 if dtype == torch.bfloat16 else 2e-3, "16-bit accumulate")
+    assert_bits_equal(got[0], mg16[0].to(DEV), "empty group untouched")
+
+
+def test_mxfp8_wgrad_accumulate_into_bf16():
+    """The MXFP8 wgrad's accumulate mode into a bf16 weight gradient."""
+    G, K, N, m = 3, 128, 256, [100, 0, 333]
+    T = sum(m)
+    say("MXFP8 wgrad accumulate into bf16")
+    x, _, _, dy, mg = rand_case(32, G, K, N, m, torch.bfloat16)
+    mg16 = mg.to(torch.bfloat16)
+    ws = workspace_for(m, T)
+    ld = gl.gl_colwise_ld(G, T)
+    u8 = dict(dtype=torch.uint8, device=DEV)
+    xq, xs = torch.zeros(K, ld, **u8), torch.zeros(K, ld // 32, **u8)
+    dq, ds = torch.zeros(N, ld, **u8), torch.zeros(N, ld // 32, **u8)
+    gl.gl_group_quantize_mxfp8_colwise(x.to(DEV), xq, xs, ws, G)
+    gl.gl_group_quantize_mxfp8_colwise(dy.to(DEV), dq, ds, ws, G)
+    dw = mg16.to(DEV)
+    gl.gl_wgrad_mxfp8(dq, ds, xq, xs, dw, ws, T, accumulate=True)
+    torch.cuda.synchronize()
+    cxq, cxs, poff = oracle.quantize_mxfp8_colwise(to64(x), m, ld=ld)
+    cdq, cds, _ = oracle.quantize_mxfp8_colwise(to64(dy), m, ld=ld)
+    end = int(poff[-1])
+    ref = oracle.wgrad_mxfp8(cdq[:, :end], cds[:, : end // 32], cxq[:, :end], cxs[:, : end // 32], m,
+                             main_grad=to64(mg16), accumulate=True)
+    assert_close(dw, ref, TOL_BF16, "MXFP8 accumulate into bf16")
+    assert_bits_equal(dw[1], mg16[1].to(DEV), "empty group untouched")
