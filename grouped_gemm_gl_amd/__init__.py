@@ -179,8 +179,10 @@ def gl_offsets(m_splits: Tensor, total_rows: int, workspace: Tensor, stream=None
 
 
 def workspace_offsets(workspace: Tensor, num_groups: int) -> Tensor:
-    """The int64[G+1] offsets inside a workspace, as a view (no device work)."""
-    return workspace[32: 32 + 8 * (num_groups + 1)].view(torch.int64)
+    """The int64[G+1] offsets inside a workspace, as a view (no device work); the
+    library names where they sit (gl_workspace_offsets)."""
+    start = int(load().gl_workspace_offsets(_ptr(workspace))) - workspace.data_ptr()
+    return workspace[start: start + 8 * (num_groups + 1)].view(torch.int64)
 
 
 def gl_read_status(workspace: Tensor, stream=None) -> int:

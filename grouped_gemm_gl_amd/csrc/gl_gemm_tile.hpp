@@ -4,6 +4,7 @@
 // the pieces fit together.
 #pragma once
 
+#include <atomic>
 #include <type_traits>
 
 #include "gl_common.hpp"
@@ -567,12 +568,16 @@ __device__ __forceinline__ void store_tile_lds(const Params &p, const Tile &t, c
 }
 static_assert(kS * kStageBytes >= kBM * kBN * 2, "the staged epilogue needs the whole tile in the ring");
 
-// Compute units of the current device (one persistent workgroup per CU).
+// Compute units of the current device (one persistent workgroup per CU), queried
+// once per device and cached.
+constexpr int kMaxDevices = 64;
 inline int num_cus() {
+  static std::atomic<int> cached[kMaxDevices];  // 0: not queried yet
   int dev = 0, n = 0;
-  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) !=
-                                              hipSuccess || n <= 0)
-    n = 256;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev >= 0 && dev < kMaxDevices && (n = cached[dev].load(std::memory_order_relaxed)) > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  if (dev >= 0 && dev < kMaxDevices) cached[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 

@@ -29,11 +29,10 @@
  *  - Buffers must be 16-byte aligned, and for bf16 K and N must be multiples of 8
  *    so every row starts on a 16-byte boundary, and at most 2^22 (GL_ERR_SHAPE
  *    otherwise; the MXFP8 forward and dgrad take the same 2^22 bound).
- *  - Output buffers may have more rows than T (`y_rows`, `dx_rows` >= T): only the
- *    packed valid rows [0, T) are written and any padded tail is left untouched
- *    (page "[PyTorch] Add optional caller-provided output/grad-input buffers to
- *    GroupedLinear and fused grouped MLP", Changes: the GEMM writes only the packed
- *    valid rows per m_splits).
+ *  - Output buffers may have more rows than T (`y_rows`, `dx_rows` >= T).  Kernels
+ *    store into rows [0, T) alone; every row from T to the end of the buffer keeps
+ *    whatever it held before the call (page "[PyTorch] Add optional caller-provided
+ *    output/grad-input buffers to GroupedLinear and fused grouped MLP", Changes).
  *  - Return value: GL_OK (0) or a negative GL_ERR_* code.  On any host-detected
  *    error nothing is launched and nothing is written; gl_last_error() gives a
  *    message (thread-local).
@@ -205,7 +204,6 @@ int gl_wgrad_bgrad(int num_groups, int64_t in_features, int64_t out_features, in
 int gl_group_quantize_mxfp8(const void *src, int64_t rows, int64_t cols, uint8_t *data,
                             uint8_t *scale, hipStream_t stream);
 
-/* Message of the last error on this thread ("" if none). */
 /*
  * ---------------------------------------------------------------- MXFP8 backward
  * The quantized backward pass (page "transformer_engine/pytorch/ops/basic/
@@ -433,6 +431,7 @@ int gl_wgrad_queue_run_next(gl_wgrad_queue *queue, hipStream_t stream);
 int gl_wgrad_queue_flush(gl_wgrad_queue *queue, hipStream_t stream);
 int gl_wgrad_queue_clear(gl_wgrad_queue *queue);
 
+/* Message of the last error on this thread ("" if none). */
 const char *gl_last_error(void);
 
 /* Library identification string. */

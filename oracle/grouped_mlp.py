@@ -4,7 +4,7 @@ test infrastructure only.
 What is computed (page "[PyTorch] Add optional caller-provided output/grad-input
 buffers to GroupedLinear and fused grouped MLP": a fused op of FC1, an
 activation and FC2 over the same split sizes, whose FC2 output and FC1 grad-input
-may be caller buffers of which only the packed valid rows are written).  The pages
+may be caller-provided buffers, written on the valid rows alone).  The pages
 do not name the activation; it is taken here as SwiGLU over the two halves of
 FC1's output: act(h) = silu(h[:, :F]) * h[:, F:], silu(v) = v / (1 + exp(-v)).
 

@@ -10,7 +10,7 @@ import torch
 
 import grouped_gemm_gl_amd as gl
 import oracle
-from gl_testutil import TOL_BF16, assert_bits_equal, assert_close, nan_tail, to64
+from gl_testutil import TOL_BF16, TOL_F32, assert_bits_equal, assert_close, nan_tail, to64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -55,6 +55,21 @@ def test_1300_groups_mostly_tiny_or_empty():
     groups = [1, 2, 1023, 1024, 1029, 1298] + [int(i) for i in np.nonzero(m)[0][:5]]
     assert_close(dw[groups], oracle.wgrad(X, DY, m, groups=groups), TOL_BF16, "dW (selected groups)")
     assert not dw[torch.from_numpy(np.nonzero(m == 0)[0]).to(DEV)].float().abs().sum().item()
+    # bias grad over 100 000 groups: the standalone kernel (bf16) and the fp32
+    # wgrad + bias grad call, whose bias grad is a launch of its own
+    say("100k groups: bias grad, fp32 wgrad + bias grad")
+    db = torch.full((G, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+    gl.gl_bgrad(dyd, db, ws)
+    x32, dy32 = xd.float(), dyd.float()
+    dw32 = torch.full((G, N, K), float("nan"), device=DEV)
+    db32 = torch.full((G, N), float("nan"), device=DEV)
+    gl.gl_wgrad_bgrad(x32, dy32, dw32, db32, ws)
+    torch.cuda.synchronize()
+    ref_db = oracle.bgrad(DY, m)
+    assert_close(db, ref_db, TOL_BF16, "db (bf16, every group)")
+    assert_close(db32, ref_db, TOL_F32, "db (fp32, every group)")
+    assert_close(dw32[groups], oracle.wgrad(X, DY, m, groups=groups), TOL_F32, "dW fp32 (selected groups)")
+    assert not dw32[torch.from_numpy(np.nonzero(m == 0)[0]).to(DEV)].abs().sum().item()
     assert_close(db, oracle.bgrad(DY, m), TOL_BF16, "db")
 
 
@@ -104,6 +119,21 @@ def test_100k_groups_offsets_and_passes():
     groups = [0, 1, 1023, 1024, 50_000, G - 1] + [int(i) for i in np.nonzero(m)[0][:5]]
     assert_close(dw[groups], oracle.wgrad(X, DY, m, groups=groups), TOL_BF16, "dW (selected groups)")
     assert not dw[torch.from_numpy(np.nonzero(m == 0)[0]).to(DEV)].float().abs().sum().item()
+    # bias grad over 100 000 groups: the standalone kernel (bf16) and the fp32
+    # wgrad + bias grad call, whose bias grad is a launch of its own
+    say("100k groups: bias grad, fp32 wgrad + bias grad")
+    db = torch.full((G, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+    gl.gl_bgrad(dyd, db, ws)
+    x32, dy32 = xd.float(), dyd.float()
+    dw32 = torch.full((G, N, K), float("nan"), device=DEV)
+    db32 = torch.full((G, N), float("nan"), device=DEV)
+    gl.gl_wgrad_bgrad(x32, dy32, dw32, db32, ws)
+    torch.cuda.synchronize()
+    ref_db = oracle.bgrad(DY, m)
+    assert_close(db, ref_db, TOL_BF16, "db (bf16, every group)")
+    assert_close(db32, ref_db, TOL_F32, "db (fp32, every group)")
+    assert_close(dw32[groups], oracle.wgrad(X, DY, m, groups=groups), TOL_F32, "dW fp32 (selected groups)")
+    assert not dw32[torch.from_numpy(np.nonzero(m == 0)[0]).to(DEV)].abs().sum().item()
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])

@@ -153,8 +153,8 @@ def test_grouped_mlp_per_group_weights_and_main_grad_accumulate():
     assert_bits_equal(y, y_stacked, "per-group vs stacked weights")
     Ag, DHg = to64(a), to64(dh)
     assert_close(torch.stack(mg2d), oracle.wgrad(Ag, to64(dy), m, main_grad=mg2.numpy(), accumulate=True),
-                 TOL_BF16, "main_grad 2")
+                 TOL_F32, "main_grad 2")
     assert_close(torch.stack(mg1d), oracle.wgrad(to64(x), DHg, m, main_grad=mg1.numpy(), accumulate=True),
-                 TOL_BF16, "main_grad 1")
+                 TOL_F32, "main_grad 1")
     assert_bits_equal(mg1d[1], mg1[1].to(DEV), "empty group main_grad 1 untouched")
     assert_bits_equal(mg2d[1], mg2[1].to(DEV), "empty group main_grad 2 untouched")

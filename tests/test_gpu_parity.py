@@ -202,8 +202,8 @@ def test_wgrad_bf16(G, K, N, m):
     X, DY, MG = to64(x), to64(dy), to64(mg)
     ref = oracle.wgrad(X, DY, m)
     assert_close(dw, ref, TOL_BF16, "dW bf16 store")
-    assert_close(torch.stack(dwf), ref, TOL_BF16, "dW fp32 per-group store")
-    assert_close(mgd, oracle.wgrad(X, DY, m, main_grad=MG, accumulate=True), TOL_BF16, "main_grad accumulate")
+    assert_close(torch.stack(dwf), ref, TOL_F32, "dW fp32 per-group store")
+    assert_close(mgd, oracle.wgrad(X, DY, m, main_grad=MG, accumulate=True), TOL_F32, "main_grad accumulate")
     for g in range(G):
         if m[g] == 0:
             assert_bits_equal(mgd[g], mg[g].to(DEV), f"empty group {g} main_grad untouched")

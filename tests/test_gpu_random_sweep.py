@@ -88,7 +88,8 @@ def test_random_grouped_linear(case):
     assert_close(dx[:T], oracle.dgrad(DY, W, m), tol, "dx")
     dws = torch.stack(dw) if per_group else dw
     ref = oracle.wgrad(X, DY, m, main_grad=mg.numpy(), accumulate=accumulate)
-    assert_close(dws, ref, TOL_BF16 if accumulate and dtype != torch.float32 else tol, "dW")
+    # an fp32 main_grad (accumulate) is held to the fp32 bound whatever the input type
+    assert_close(dws, ref, TOL_F32 if accumulate else tol, "dW")
     assert_close(db, oracle.bgrad(DY, m), tol, "db")
 
 

@@ -74,7 +74,7 @@ def test_wgrad_bgrad_matches_oracle_and_wgrad(G, K, N, m, dtype):
     assert_close(db, ref_db, tol, "db")
     assert_close(torch.stack(db32), ref_db, TOL_F32 if dtype == torch.float32 else 1e-4, "db fp32")
     X, MG = to64(x), to64(mg)
-    assert_close(mgd, oracle.wgrad(X, DY, m, main_grad=MG, accumulate=True), TOL_BF16, "main_grad")
+    assert_close(mgd, oracle.wgrad(X, DY, m, main_grad=MG, accumulate=True), TOL_F32, "main_grad")
     for g in range(G):
         if m[g] == 0:
             assert not db[g].float().abs().sum().item() and not db32[g].abs().sum().item()

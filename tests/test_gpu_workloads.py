@@ -1,13 +1,11 @@
 """GPU parity at the workloads' full sizes, through the C ABI, in the same launch
 configuration the benchmark times.
 
-Outputs are checked on samples the oracle computes one by one (rows, wgrad rows of
-selected groups) and, where cheap, in full (bias grad, the untouched tail of a
-caller buffer, untouched main_grad of empty groups).  Inputs come from the seeded
-generators; the oracle quantizes and computes on its own.
+Every element of every output is compared with the float64 oracle, which runs one
+group at a time (tests/full_check.py).  Quantized codes and scales are compared
+bit for bit with the oracle's own quantization of the same inputs before the
+oracle's GEMMs consume them.  Inputs come from the seeded generators in synth.py.
 """
-import sys
-
 import numpy as np
 import pytest
 import torch
@@ -15,51 +13,11 @@ import torch
 import grouped_gemm_gl_amd as gl
 import oracle
 import synth
-from gl_testutil import TOL_BF16, assert_bits_equal, assert_close, to64
+from full_check import assert_codes_equal, check_chunks, group_bounds, pool_map, say
+from gl_testutil import TOL_BF16, TOL_F32, assert_bits_equal, to64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
-
-
-def say(*a):
-    print(*a, file=sys.stderr, flush=True)
-
-
-class LazyGroups:
-    """Per-group float64 views of a stacked CPU tensor, converted when asked for."""
-
-    def __init__(self, t):
-        self.t = t
-
-    def __len__(self):
-        return self.t.shape[0]
-
-    def __getitem__(self, g):
-        return self.t[g].double().numpy()
-
-
-def sample_rows(m, n_random=48, seed=0, groups=None):
-    """First two and last two rows of every (listed) non-empty group, plus random
-    rows of those groups."""
-    off = np.concatenate([[0], np.cumsum(m)])
-    groups = range(len(m)) if groups is None else groups
-    rows = set()
-    rng = np.random.default_rng(seed)
-    nonempty = [g for g in groups if m[g]]
-    for g in nonempty:
-        for r in (off[g], off[g] + 1, off[g + 1] - 2, off[g + 1] - 1):
-            if off[g] <= r < off[g + 1]:
-                rows.add(int(r))
-    for _ in range(n_random):
-        g = nonempty[rng.integers(0, len(nonempty))]
-        rows.add(int(rng.integers(off[g], off[g + 1])))
-    return np.array(sorted(rows), dtype=np.int64)
-
-
-def some_groups(G, k, seed=1):
-    """Group 0, the last group and k - 2 others."""
-    rng = np.random.default_rng(seed)
-    return sorted({0, G - 1, *rng.choice(np.arange(1, G - 1), size=k - 2, replace=False).tolist()})
 
 
 def workspace(m, T):
@@ -80,24 +38,41 @@ def test_bf16_train_g8_all_passes():
     dx = torch.empty(wl.T, wl.K, dtype=torch.bfloat16, device=DEV)
     dw = torch.empty(wl.G, wl.N, wl.K, dtype=torch.bfloat16, device=DEV)
     db = torch.empty(wl.G, wl.N, dtype=torch.bfloat16, device=DEV)
-    say("  launching offsets/forward/dgrad/wgrad/bgrad")
+    dw_sep = torch.empty_like(dw)
+    db_sep = torch.empty_like(db)
+    say("  launching offsets/forward/dgrad/wgrad+bgrad (fused, as timed) and wgrad, bgrad alone")
     gl.gl_forward(xd, wd, y, ws, bias=bd)
     gl.gl_dgrad(dyd, wd, dx, ws)
-    gl.gl_wgrad(xd, dyd, dw, ws)
-    gl.gl_bgrad(dyd, db, ws)
+    gl.gl_wgrad_bgrad(xd, dyd, dw, db, ws)
+    gl.gl_wgrad(xd, dyd, dw_sep, ws)
+    gl.gl_bgrad(dyd, db_sep, ws)
     torch.cuda.synchronize()
-    say("  checking against the oracle")
-    rows = sample_rows(m)
-    X, DY = x.float().numpy(), dy.float().numpy()
-    W = LazyGroups(w)
-    assert_close(y[torch.from_numpy(rows).to(DEV)], oracle.forward(X, W, to64(b), m, rows=rows), TOL_BF16, "y rows")
-    assert_close(dx[torch.from_numpy(rows).to(DEV)], oracle.dgrad(DY, W, m, rows=rows), TOL_BF16, "dx rows")
-    groups = [int(np.argmax(m)), int(np.argmin(m)), 3]
-    nsel = np.array([0, 1, 255, 256, 7000, wl.N - 1])
-    ref = oracle.wgrad(X, DY, m, groups=groups, out_rows=nsel)
-    got = dw[groups][:, torch.from_numpy(nsel).to(DEV)]
-    assert_close(got, ref, TOL_BF16, "dW rows")
-    assert_close(db, oracle.bgrad(DY, m), TOL_BF16, "db")
+    assert_bits_equal(dw, dw_sep, "dW of the fused call vs gl_wgrad")
+    say("  checking every element against the oracle")
+    X, DY, B = x.float().numpy(), dy.float().numpy(), to64(b)
+    yc, dxc = y.cpu(), dx.cpu()
+    bounds = group_bounds(m)
+
+    def fwd_chunks():
+        for g, lo, hi in bounds:
+            Wg = w[g].double().numpy()
+            yield g, yc[lo:hi], oracle.forward(X[lo:hi], [Wg], [B[g]], [hi - lo])
+
+    def dgrad_chunks():
+        for g, lo, hi in bounds:
+            Wg = w[g].double().numpy()
+            yield g, dxc[lo:hi], oracle.dgrad(DY[lo:hi], [Wg], [hi - lo])
+
+    def wgrad_chunks():
+        for g, lo, hi in bounds:
+            yield g, dw[g].cpu(), oracle.wgrad(X[lo:hi], DY[lo:hi], [hi - lo])[0]
+
+    check_chunks("y", TOL_BF16, fwd_chunks())
+    check_chunks("dx", TOL_BF16, dgrad_chunks())
+    check_chunks("dW", TOL_BF16, wgrad_chunks())
+    ref_db = oracle.bgrad(DY, m)
+    check_chunks("db (fused)", TOL_BF16, [("all", db, ref_db)])
+    check_chunks("db (gl_bgrad)", TOL_BF16, [("all", db_sep, ref_db)])
 
 
 def test_bf16_zipf_g64_main_grad_accumulate():
@@ -115,20 +90,24 @@ def test_bf16_zipf_g64_main_grad_accumulate():
     gl.gl_dgrad(dyd, wd, dx, ws)
     gl.gl_wgrad(xd, dyd, mgd, ws, accumulate=True)
     torch.cuda.synchronize()
-    say("  checking against the oracle")
-    rows = sample_rows(m)
+    say("  checking every element against the oracle")
     X, DY = x.float().numpy(), dy.float().numpy()
-    W = LazyGroups(w)
-    idx = torch.from_numpy(rows).to(DEV)
-    assert_close(y[idx], oracle.forward(X, W, None, m, rows=rows), TOL_BF16, "y rows")
-    assert_close(dx[idx], oracle.dgrad(DY, W, m, rows=rows), TOL_BF16, "dx rows")
-    nz = np.nonzero(m)[0]
-    groups = [int(np.argmax(m)), int(nz[np.argmin(m[nz])]), int(nz[len(nz) // 2])]
-    nsel = np.array([0, 5, 511, 1535])
-    ref = oracle.wgrad(X, DY, m, main_grad=mg.numpy(), accumulate=True, groups=groups, out_rows=nsel)
-    assert_close(mgd[groups][:, torch.from_numpy(nsel).to(DEV)], ref, TOL_BF16, "main_grad rows")
+    yc, dxc, mgc = y.cpu(), dx.cpu(), mgd.cpu()
+    bounds = [(g, lo, hi) for g, lo, hi in group_bounds(m) if hi > lo]
+    check_chunks("y", TOL_BF16,
+                 ((g, yc[lo:hi], oracle.forward(X[lo:hi], [w[g].double().numpy()], None, [hi - lo]))
+                  for g, lo, hi in bounds))
+    check_chunks("dx", TOL_BF16,
+                 ((g, dxc[lo:hi], oracle.dgrad(DY[lo:hi], [w[g].double().numpy()], [hi - lo]))
+                  for g, lo, hi in bounds))
+    # fp32 main_grad: the fp32 bound, over every group (the longest contracts over
+    # about 19 900 rows)
+    check_chunks("main_grad (fp32, accumulate)", TOL_F32,
+                 ((g, mgc[g], oracle.wgrad(X[lo:hi], DY[lo:hi], [hi - lo], main_grad=mg[g:g + 1].numpy(),
+                                           accumulate=True)[0])
+                  for g, lo, hi in bounds))
     for g in np.nonzero(m == 0)[0]:
-        assert_bits_equal(mgd[int(g)], mg[int(g)], f"empty group {g} main_grad")
+        assert_bits_equal(mgc[int(g)], mg[int(g)], f"empty group {g} main_grad")
 
 
 def test_bf16_fwd_g256_caller_buffer_per_group_weights():
@@ -148,13 +127,30 @@ def test_bf16_fwd_g256_caller_buffer_per_group_weights():
     y_stacked = torch.empty(wl.T, wl.N, dtype=torch.bfloat16, device=DEV)
     gl.gl_forward(xd, wd, y_stacked, ws)
     torch.cuda.synchronize()
-    say("  checking against the oracle")
     assert_bits_equal(y[wl.T:], tail_before, "padded tail")
     assert_bits_equal(y[: wl.T], y_stacked, "per-group pointers vs stacked weight")
-    rows = sample_rows(m, n_random=32, groups=some_groups(wl.G, 16))
+    say("  checking every row against the oracle")
     X = x.float().numpy()
-    assert_close(y[torch.from_numpy(rows).to(DEV)], oracle.forward(X, LazyGroups(w), None, m, rows=rows), TOL_BF16,
-                 "y rows")
+    yc = y[: wl.T].cpu()
+    check_chunks("y", TOL_BF16,
+                 ((g, yc[lo:hi], oracle.forward(X[lo:hi], [w[g].double().numpy()], None, [hi - lo]))
+                  for g, lo, hi in group_bounds(m) if hi > lo))
+
+
+def _rowwise_codes_check(what, src, q, s, block_rows=1024):
+    """Rowwise codes and scales of src [rows, K] against the oracle, bit for bit,
+    in blocks of rows on host threads."""
+    qc, sc = q.cpu().numpy(), s.cpu().numpy()
+    rows = src.shape[0]
+
+    def one(lo):
+        hi = min(rows, lo + block_rows)
+        rq, rs = oracle.quantize_mxfp8(src[lo:hi].double().numpy())
+        assert_codes_equal(f"{what} codes rows {lo}..{hi}", qc[lo:hi], rq)
+        assert_codes_equal(f"{what} scales rows {lo}..{hi}", sc[lo:hi], rs)
+
+    pool_map(one, range(0, rows, block_rows))
+    say(f"  {what}: codes and scales of {rows} rows bit-exact")
 
 
 def test_mxfp8_fwd_g32_quantize_and_forward():
@@ -174,20 +170,14 @@ def test_mxfp8_fwd_g32_quantize_and_forward():
     y = torch.empty(wl.T, wl.N, dtype=torch.bfloat16, device=DEV)
     gl.gl_forward(xq, wq, y, ws, x_scale=xs, w_scale=wsc)
     torch.cuda.synchronize()
-    say("  checking against the oracle")
-    rows = sample_rows(m, n_random=24, groups=some_groups(wl.G, 4))
-    off = np.concatenate([[0], np.cumsum(m)])
-    gs = oracle.group_of_rows(off, rows)
-    xq_c, xs_c = xq.cpu().numpy(), xs.cpu().numpy()
-    ref_rows = np.zeros((rows.size, wl.N))
-    for g in np.unique(gs):
-        g = int(g)
-        sel = np.nonzero(gs == g)[0]
-        qx, sx = oracle.quantize_mxfp8(x[torch.from_numpy(rows[sel])].double().numpy())
-        assert np.array_equal(xq_c[rows[sel]], qx) and np.array_equal(xs_c[rows[sel]], sx), f"x codes, group {g}"
-        qw, sw = oracle.quantize_mxfp8(w[g].double().numpy())
-        if g in (int(gs[0]), int(gs[-1])):  # whole-group weight codes, bit for bit
-            assert np.array_equal(wq[g].cpu().numpy(), qw) and np.array_equal(wsc[g].cpu().numpy(), sw)
-        # rows are independent: each sampled row is a one-group problem of its own
-        ref_rows[sel] = oracle.forward_mxfp8(qx, sx, [qw], [sw], None, [len(sel)])
-    assert_close(y[torch.from_numpy(rows).to(DEV)], ref_rows, TOL_BF16, "MXFP8 y rows")
+    say("  checking every code against the oracle's quantization")
+    _rowwise_codes_check("x", x, xq, xs)
+    _rowwise_codes_check("W", w.view(wl.G * wl.N, wl.K), wq.view(wl.G * wl.N, wl.K),
+                         wsc.view(wl.G * wl.N, wl.K // 32))
+    say("  checking every element of y against the oracle on the dequantized operands")
+    xq_c, xs_c, wq_c, ws_c = xq.cpu().numpy(), xs.cpu().numpy(), wq.cpu().numpy(), wsc.cpu().numpy()
+    yc = y.cpu()
+    check_chunks("MXFP8 y", TOL_BF16,
+                 ((g, yc[lo:hi], oracle.forward_mxfp8(xq_c[lo:hi], xs_c[lo:hi], [wq_c[g]], [ws_c[g]], None,
+                                                      [hi - lo]))
+                  for g, lo, hi in group_bounds(m) if hi > lo))
