@@ -65,7 +65,10 @@ class Tally:
             self.within_f32 += int((r32 <= 1.0).sum())
             self.worst_f32 = max(self.worst_f32, float(r32.max()))
 
-    def finish(self):
+    def finish(self, f32_floor=None):
+        """Asserts the bound on every element; with ``f32_floor`` also that at least
+        that share of the elements is within the fp32 bound (a regression guard for
+        outputs whose fp32 summation order alone misses it on a few elements)."""
         frac32 = self.within_f32 / self.n if self.n else 1.0
         say(f"  {self.what}: {self.n} elements, {self.bad} outside {self.rel}*(|ref|+1), "
             f"worst err/limit {self.worst:.3g} at {self.worst_at}; "
@@ -73,15 +76,18 @@ class Tally:
         assert self.n > 0, f"{self.what}: nothing compared"
         assert self.bad == 0, (f"{self.what}: {self.bad} of {self.n} elements outside {self.rel}*(|ref|+1); "
                                f"worst {self.worst:.3g} at {self.worst_at}")
+        if f32_floor is not None:
+            assert frac32 >= f32_floor, (f"{self.what}: only {frac32:.6%} of the elements within "
+                                         f"{TOL_F32}*(|ref|+1), below {f32_floor:.4%}")
         return frac32
 
 
-def check_chunks(what, rel, chunks):
+def check_chunks(what, rel, chunks, f32_floor=None):
     """chunks: iterable of (label, got, ref); every element of every chunk is compared."""
     t = Tally(what, rel)
     for label, got, ref in chunks:
         t.add(label, got, ref)
-    return t.finish()
+    return t.finish(f32_floor)
 
 
 def group_bounds(m):
