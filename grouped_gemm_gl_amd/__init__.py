@@ -28,10 +28,12 @@ __all__ = [
     "gl_group_quantize_mxfp8_rowwise_colwise", "gl_quantize_mxfp8_colwise_weights",
     "gl_offsets_quantize_mxfp8", "gl_offsets_quantize_mxfp8_rowwise_colwise", "gl_quantize_mxfp8_weights",
     "gl_dgrad_mxfp8", "gl_wgrad_mxfp8", "gl_swiglu_forward", "gl_swiglu_backward",
-    "gl_grouped_mlp_forward", "gl_grouped_mlp_backward", "WgradQueue",
+    "gl_grouped_mlp_forward", "gl_grouped_mlp_backward", "WgradQueue", "gl_forward_noalloc",
+    "NOALLOC_MAX_GROUPS",
 ]
 
 GL_F32, GL_BF16, GL_F16, GL_E4M3 = 0, 1, 2, 3
+NOALLOC_MAX_GROUPS = 16384  # GL_NOALLOC_MAX_GROUPS
 GL_STATUS_NEGATIVE_SPLIT, GL_STATUS_SUM_MISMATCH, GL_STATUS_WORKSPACE = 1, 2, 4
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -91,6 +93,7 @@ def load():
         "gl_wgrad_queue_run_next": (I, [P, P]),
         "gl_wgrad_queue_flush": (I, [P, P]),
         "gl_wgrad_queue_clear": (I, [P]),
+        "gl_forward_noalloc": (I, [I, I64, I64, I64, I, I] + [P] * 10 + [I64, P]),
         "gl_last_error": (ctypes.c_char_p, []),
         "gl_version": (ctypes.c_char_p, []),
     }
@@ -218,6 +221,36 @@ def gl_forward(x: Tensor, w: Grouped, y: Tensor, workspace: Tensor, *, bias: Opt
     sp, spp, keep_s = _grouped(w_scale, dev, stream)
     _check(load().gl_forward(G, K, N, T, _dtype(x), _dtype(y), _ptr(x), _ptr(x_scale), wp, wpp, sp, spp, bp, bpp,
                              _ptr(y), y.shape[0], _ptr(workspace), _stream(stream)))
+    del keep_w, keep_b, keep_s
+    return y
+
+
+def gl_forward_noalloc(m_splits: Tensor, x: Tensor, w: Grouped, y: Tensor, *, bias: Optional[Grouped] = None,
+                       x_scale: Optional[Tensor] = None, w_scale: Optional[Grouped] = None, stream=None) -> Tensor:
+    """gl_offsets + gl_forward with the library's own fixed device scratch in place of a
+    workspace (the C call allocates nothing; the per-group pointer form of ``w`` builds
+    its pointer array here, so callers that must not allocate pass stacked tensors).
+    At most NOALLOC_MAX_GROUPS groups; calls that overlap on one device race."""
+    G = w.shape[0] if isinstance(w, Tensor) else len(w)
+    w0 = _first(w)
+    N, K = w0.shape[-2], w0.shape[-1]
+    T = x.shape[0]
+    if m_splits.dtype != torch.int64 or m_splits.numel() != G:
+        raise ValueError(f"m_splits must be int64 with {G} entries")
+    if x.dim() != 2 or x.shape[1] != K:
+        raise ValueError(f"x must be [T, {K}], got {tuple(x.shape)}")
+    if y.dim() != 2 or y.shape[1] != N:
+        raise ValueError(f"y must be [rows >= {T}, {N}], got {tuple(y.shape)}")
+    if w0.dtype != x.dtype:
+        raise ValueError("x and w must have the same dtype")
+    if bias is not None and _first(bias).dtype != y.dtype:
+        raise ValueError("bias dtype must equal the output dtype")
+    dev = x.device
+    wp, wpp, keep_w = _grouped(w, dev, stream)
+    bp, bpp, keep_b = _grouped(bias, dev, stream)
+    sp, spp, keep_s = _grouped(w_scale, dev, stream)
+    _check(load().gl_forward_noalloc(G, K, N, T, _dtype(x), _dtype(y), _ptr(m_splits), _ptr(x), _ptr(x_scale), wp,
+                                     wpp, sp, spp, bp, bpp, _ptr(y), y.shape[0], _stream(stream)))
     del keep_w, keep_b, keep_s
     return y
 

@@ -10,13 +10,15 @@
 #include <cstdio>
 #include <cstring>
 #include <deque>
+#include <mutex>
 #include <new>
 
 #include "../../include/grouped_linear.h"
 #include "gl_common.hpp"
 
 namespace gl {
-hipError_t launch_offsets(const int64_t *m_splits, int G, int64_t total_rows, void *ws, hipStream_t stream);
+hipError_t launch_offsets(const int64_t *m_splits, int G, int64_t total_rows, void *ws, int split_slots,
+                          hipStream_t stream);
 hipError_t launch_forward_bf16(int G, int64_t K, int64_t N, int64_t T, const uint16_t *x, const uint16_t *w,
                                const uint16_t *const *w_ptrs, const void *bias, const void *const *bias_ptrs,
                                uint16_t *y, int f16, const void *ws, hipStream_t s);
@@ -164,7 +166,8 @@ int gl_offsets(const int64_t *m_splits, int num_groups, int64_t total_rows, void
   if (!m_splits) return fail(GL_ERR_ARG, "m_splits is NULL");
   if ((uintptr_t)m_splits & 7u) return fail(GL_ERR_ARG, "m_splits not 8-byte aligned");
   if (!workspace || !aligned16(workspace)) return fail(GL_ERR_ARG, "workspace NULL or not 16-byte aligned");
-  return hip_result(gl::launch_offsets(m_splits, num_groups, total_rows, workspace, stream), "gl_offsets");
+  return hip_result(gl::launch_offsets(m_splits, num_groups, total_rows, workspace, gl::kSplitSlots, stream),
+                    "gl_offsets");
 }
 
 int gl_read_status(const void *workspace, int *status, hipStream_t stream) {
@@ -817,6 +820,77 @@ int gl_wgrad_queue_clear(gl_wgrad_queue *queue) {
   if (!queue) return fail(GL_ERR_ARG, "queue is NULL");
   queue->pending.clear();
   return ok();
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------ allocation-free forward
+// gl_forward_noalloc: the offsets and the forward's split area live in `scratch`, a
+// file-scope device array of fixed size, instead of a caller workspace.  Host code
+// never passes the array's name to a kernel (on the host it is a stand-in, not a
+// device address): the device address comes from hipGetSymbolAddress, once per
+// device, and is kept per device.
+namespace {
+constexpr int kNoallocSlots = GL_NOALLOC_SPLIT_SLOTS;
+constexpr size_t kNoallocBytes = gl::ws_bytes_slots(GL_NOALLOC_MAX_GROUPS, kNoallocSlots);
+static_assert(kNoallocBytes <= ((size_t)17 << 20), "the allocation-free forward's scratch stays small");
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kNoallocBytes];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxScratchDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on the first call
+// per device, with that device current).
+int scratch_address(void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_result(e, "gl_forward_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(GL_ERR_UNSUPPORTED, "gl_forward_noalloc: device %d beyond the %d devices it serves", dev,
+                kMaxScratchDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) return hip_result(e != hipSuccess ? e : hipErrorInvalidSymbol,
+                                                   "gl_forward_noalloc: hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return GL_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int gl_forward_noalloc(int num_groups, int64_t in_features, int64_t out_features, int64_t total_rows,
+                       gl_dtype in_dtype, gl_dtype out_dtype, const int64_t *m_splits, const void *x,
+                       const uint8_t *x_scale, const void *w, const void *const *w_ptrs, const uint8_t *w_scale,
+                       const uint8_t *const *w_scale_ptrs, const void *bias, const void *const *bias_ptrs, void *y,
+                       int64_t y_rows, hipStream_t stream) {
+  if (num_groups > GL_NOALLOC_MAX_GROUPS)
+    return fail(GL_ERR_SHAPE, "gl_forward_noalloc: %d groups exceed its maximum of %d (use gl_forward with a "
+                "workspace)", num_groups, GL_NOALLOC_MAX_GROUPS);
+  if (num_groups <= 0) return fail(GL_ERR_ARG, "Invalid number of groups (%d)", num_groups);
+  if (!m_splits) return fail(GL_ERR_ARG, "m_splits is NULL");
+  if ((uintptr_t)m_splits & 7u) return fail(GL_ERR_ARG, "m_splits not 8-byte aligned");
+  // every argument check of gl_forward, before anything is enqueued (a stand-in
+  // workspace pointer: these checks only test it for NULL)
+  GL_TRY(forward_impl(num_groups, in_features, out_features, total_rows, in_dtype, out_dtype, x, x_scale, w, w_ptrs,
+                      w_scale, w_scale_ptrs, bias, bias_ptrs, y, y_rows, m_splits, stream, false));
+  if (total_rows == 0) return ok();
+  void *ws = nullptr;
+  GL_TRY(scratch_address(&ws));
+  // the scan rewrites the header and tables and zeroes the split counters, so
+  // nothing of the previous call's contents is read
+  GL_TRY(hip_result(gl::launch_offsets(m_splits, num_groups, total_rows, ws, kNoallocSlots, stream),
+                    "gl_forward_noalloc"));
+  return forward_impl(num_groups, in_features, out_features, total_rows, in_dtype, out_dtype, x, x_scale, w, w_ptrs,
+                      w_scale, w_scale_ptrs, bias, bias_ptrs, y, y_rows, ws, stream, true);
 }
 
 }  // extern "C"

@@ -16,11 +16,12 @@ namespace gl {
 //         counters[kSplitSlots] (zeroed by the offsets kernel, left zero by every
 //         GEMM launch), then kSplitSlots fp32 partial tiles of kPartialBytes each.
 struct WsHeader {
-  int32_t status;      // GL_STATUS_* bits, 0 = valid splits
+  int32_t status;       // GL_STATUS_* bits, 0 = valid splits
   int32_t num_groups;
   int64_t total_rows;
   int32_t magic;
-  int32_t pad[3];
+  int32_t split_slots;  // partial-tile slots of the split area (at most kSplitSlots)
+  int32_t pad[2];
 };
 static_assert(sizeof(WsHeader) == 32, "workspace header is 32 bytes");
 
@@ -36,16 +37,21 @@ __host__ __device__ inline size_t ws_prefix_byte(int G, int idx) {
   size_t base = 32 + 8 * (size_t)(G + 1);
   return base + (size_t)idx * 4 * (size_t)(G + 1);
 }
-// A GEMM launch splits at most kSplitSlots tile parts over the contraction; each
-// part leaves one 256 x 256 fp32 partial tile.
+// A GEMM launch splits at most split_slots (header) tile parts over the
+// contraction; each part leaves one 256 x 256 fp32 partial tile.  A workspace of
+// gl_workspace_size has kSplitSlots slots; the counter area always has room for
+// kSplitSlots counters.
 constexpr int kSplitSlots = 256;
 constexpr size_t kPartialBytes = 256 * 256 * 4;
-__host__ __device__ inline size_t ws_split_byte(int G) {
-  return (ws_prefix_byte(G, kNumTileRows) + 1023) & ~(size_t)1023;
+__host__ __device__ constexpr size_t ws_split_byte_c(int G) {
+  return (32 + 8 * (size_t)(G + 1) + (size_t)kNumTileRows * 4 * (size_t)(G + 1) + 1023) & ~(size_t)1023;
 }
-__host__ __device__ inline size_t ws_bytes(int G) {
-  return ws_split_byte(G) + 4 * kSplitSlots + (size_t)kSplitSlots * kPartialBytes;
+__host__ __device__ inline size_t ws_split_byte(int G) { return ws_split_byte_c(G); }
+// bytes of a workspace over G groups with `slots` partial-tile slots
+__host__ __device__ constexpr size_t ws_bytes_slots(int G, int slots) {
+  return ws_split_byte_c(G) + 4 * kSplitSlots + (size_t)slots * kPartialBytes;
 }
+__host__ __device__ inline size_t ws_bytes(int G) { return ws_bytes_slots(G, kSplitSlots); }
 
 struct WsView {
   WsHeader *hdr;

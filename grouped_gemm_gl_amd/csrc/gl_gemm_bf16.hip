@@ -73,6 +73,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
   const int grid = gridDim.x, b = blockIdx.x;
   const int first = (grid & 7) == 0 ? (b & 7) * (grid >> 3) + (b >> 3) : b;
   const int nk_rows = (int)((p.P + kBK - 1) / kBK);  // row mode: the same for every tile
+  const int slots = min(max(ws.hdr->split_slots, 0), kSplitSlots);
 
   // One work item: the whole contraction of a tile, or (SPLIT) part `part` of S of
   // the u-th split tile.  A wgrad tile of the first column, when a bias gradient is
@@ -212,11 +213,11 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
   };
 
   // whole tiles, round after round; in row mode the last round may be split
-  const int full = MODE == MODE_ROWS ? split_plan(total, grid, nk_rows).full : total;
+  const int full = MODE == MODE_ROWS ? split_plan(total, grid, nk_rows, slots).full : total;
   for (int w = first; w < full; w += grid) item(w, 0, 1, 0, std::false_type{});
   if constexpr (MODE == MODE_ROWS) {
     const int tiles = pre[p.G] * p.tiles_j;
-    const SplitPlan sp = split_plan(tiles, grid, nk_rows);
+    const SplitPlan sp = split_plan(tiles, grid, nk_rows, slots);
     // the parts of the last round: u = first, consecutive u are consecutive tiles
     if (first < sp.rem * sp.S)
       item(sp.full + first % sp.rem, first / sp.rem, sp.S, first % sp.rem, std::true_type{});

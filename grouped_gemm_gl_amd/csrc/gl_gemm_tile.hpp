@@ -401,13 +401,14 @@ struct SplitPlan {
   int items;  // full + rem * S
 };
 
-// nk: contraction stages of every tile (the same for all tiles of a row-mode launch)
-__device__ __forceinline__ SplitPlan split_plan(int tiles, int grid, int nk) {
+// nk: contraction stages of every tile (the same for all tiles of a row-mode launch);
+// slots: partial-tile slots of the workspace
+__device__ __forceinline__ SplitPlan split_plan(int tiles, int grid, int nk, int slots) {
   SplitPlan sp{tiles, 0, 1, tiles};
   const int rem = tiles % grid;
   if (rem == 0) return sp;
   int S = grid / rem;
-  if (S * rem > kSplitSlots) S = kSplitSlots / rem;
+  if (S * rem > slots) S = slots / rem;
   if (S > nk / kMinSplitStages) S = nk / kMinSplitStages;
   if (S < 2) return sp;
   sp.full = tiles - rem;

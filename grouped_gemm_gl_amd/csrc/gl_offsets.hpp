@@ -30,10 +30,11 @@ __device__ __forceinline__ T wave_inclusive_scan(T v) {
 
 // The whole scan, run by one workgroup of THREADS threads (groups are taken
 // THREADS at a time with a running carry); also zeroes the workspace's
-// split-contraction arrival counters.
+// split-contraction arrival counters and records how many partial-tile slots its
+// split area holds.
 template <int THREADS>
-__device__ __forceinline__ void offsets_block(const int64_t *__restrict__ m_splits,
-                                                               int G, int64_t total_rows, void *ws) {
+__device__ __forceinline__ void offsets_block(const int64_t *__restrict__ m_splits, int G, int64_t total_rows,
+                                              void *ws, int split_slots) {
   WsView v = ws_view(ws, G);
   int64_t *off = const_cast<int64_t *>(v.off);
   int32_t *pre[kNumTileRows];
@@ -107,6 +108,7 @@ __device__ __forceinline__ void offsets_block(const int64_t *__restrict__ m_spli
     h->num_groups = G;
     h->total_rows = total_rows;
     h->magic = kWsMagic;
+    h->split_slots = split_slots;
     h->status = (s_bad ? 1 : 0) | (carry != total_rows ? 2 : 0);
   }
 }
@@ -157,6 +159,7 @@ __device__ __forceinline__ void offsets_wave(const int64_t *__restrict__ m_split
     h->num_groups = G;
     h->total_rows = total_rows;
     h->magic = kWsMagic;
+    h->split_slots = kSplitSlots;
     h->status = (any_bad ? 1 : 0) | (carry != total_rows ? 2 : 0);
   }
 }

@@ -431,6 +431,36 @@ int gl_wgrad_queue_run_next(gl_wgrad_queue *queue, hipStream_t stream);
 int gl_wgrad_queue_flush(gl_wgrad_queue *queue, hipStream_t stream);
 int gl_wgrad_queue_clear(gl_wgrad_queue *queue);
 
+/*
+ * Allocation-free grouped forward, for callers that cannot allocate device memory
+ * or hand the library a workspace: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  It is gl_offsets followed by gl_forward
+ * (same arguments, same results, same host checks and errors), except that the
+ * offsets, tile tables, status word and split area live in a file-scope device
+ * array of the library instead of a caller workspace:
+ *   - at most GL_NOALLOC_MAX_GROUPS groups (more: GL_ERR_SHAPE); the array is
+ *     about 16.4 MiB (the tables for that many groups plus GL_NOALLOC_SPLIT_SLOTS
+ *     fp32 partial tiles of 256 x 256), held on every device the library runs this
+ *     call on until the process ends;
+ *   - nothing is allocated: no hipMalloc, no library allocation;
+ *   - every call on one device shares that device's array and leaves its contents
+ *     behind; each call rewrites what it reads (the scan zeroes the split
+ *     counters), so calls in sequence are independent, but calls that overlap on
+ *     one device (different streams, not ordered by events) race;
+ *   - split sizes found invalid on the device make the forward write nothing;
+ *     there is no status word for the caller to read.
+ * The split area is smaller than a workspace's, so the tail-round split of a
+ * launch may use fewer parts than gl_forward does (results then differ by fp32
+ * summation order only).
+ */
+#define GL_NOALLOC_MAX_GROUPS 16384
+#define GL_NOALLOC_SPLIT_SLOTS 64
+int gl_forward_noalloc(int num_groups, int64_t in_features, int64_t out_features, int64_t total_rows,
+                       gl_dtype in_dtype, gl_dtype out_dtype, const int64_t *m_splits, const void *x,
+                       const uint8_t *x_scale, const void *w, const void *const *w_ptrs, const uint8_t *w_scale,
+                       const uint8_t *const *w_scale_ptrs, const void *bias, const void *const *bias_ptrs, void *y,
+                       int64_t y_rows, hipStream_t stream);
+
 /* Message of the last error on this thread ("" if none). */
 const char *gl_last_error(void);
 

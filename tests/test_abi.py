@@ -180,3 +180,21 @@ def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(gl, "library_path", "/nonexistent/libgrouped_linear.so")
     with pytest.raises(RuntimeError, match="not built"):
         gl.load()
+
+
+def test_forward_noalloc_rejects_before_any_device_work():
+    """The allocation-free forward checks everything gl_forward checks, plus its own
+    group bound and the split-size pointer, before it looks up its device array."""
+    lib = gl.load()
+    args = lambda G=4, K=64, N=32, T=16, m=FAKE, x=FAKE2, y=FAKE2, yr=16: (
+        G, K, N, T, gl.GL_BF16, gl.GL_BF16, m, x, None, FAKE, None, None, None, None, None, y, yr, None)
+    assert lib.gl_forward_noalloc(*args(G=gl.NOALLOC_MAX_GROUPS + 1)) == -3
+    assert b"maximum" in lib.gl_last_error()
+    assert lib.gl_forward_noalloc(*args(G=0)) == -1
+    assert lib.gl_forward_noalloc(*args(m=None)) == -1
+    assert lib.gl_forward_noalloc(*args(m=FAKE + 4)) == -1
+    assert lib.gl_forward_noalloc(*args(K=0)) == -1
+    assert lib.gl_forward_noalloc(*args(yr=15)) == -3          # output capacity below T
+    assert lib.gl_forward_noalloc(*args(K=60)) == -3           # bf16 rows of 16-byte multiples
+    assert lib.gl_forward_noalloc(*args(T=0, x=None, y=None)) == 0  # nothing to do
+    assert lib.gl_forward_noalloc(*args(G=gl.NOALLOC_MAX_GROUPS, T=0, x=None, y=None)) == 0
