@@ -10,35 +10,47 @@
 //   dgrad    i = token row of group g, j = k, p = n:  A = dy (p contiguous), B = W_g (j contiguous)
 //   wgrad    i = n, j = k, p = token row of group g:  A = dy (i contiguous), B = x   (j contiguous)
 //
-// Tiles: 256x256 outputs per workgroup, 8 waves (two per SIMD, which keeps the MFMA
-// pipe fuller than one wave can) in a 2x4 grid, each wave a 128x64 block of
-// 32x32x16 bf16 MFMAs with fp32 accumulators.
+// Tiles: 256x256 outputs per workgroup, 8 waves (two per SIMD) in a 2x4 grid, each
+// wave a 128x64 block with fp32 accumulators.
 //
-// Operand staging: the contraction advances kBK at a time through a ring of kS LDS
-// stages filled by direct buffer->LDS loads (16 bytes per lane, no register
-// staging).  An operand whose contraction index is contiguous ("K-major") is staged
-// as 256 rows of 2*kBK bytes and read with 16-byte LDS loads; one whose tile index
-// is contiguous ("MN-major") is staged as kBK rows of 512 bytes and read with the
-// gfx950 LDS transpose load (ds_read_b64_tr_b16), which hands each lane 4
-// consecutive contraction values of one column -- the MFMA operand layout -- so no
-// operand is transposed in registers.  Both layouts XOR-swizzle 16-byte slots so
-// fragment reads are free of bank conflicts on gfx950's 64-bank LDS.
+// Operand staging: the contraction advances kBK = 64 at a time through a ring of two
+// LDS stages.  An operand whose contraction index is contiguous ("K-major") is staged
+// as 256 rows of 128 bytes and read with 16-byte LDS loads; one whose tile index is
+// contiguous ("MN-major") is staged as 64 rows of 512 bytes and read with the gfx950
+// LDS transpose load (ds_read_b64_tr_b16), which hands each lane consecutive
+// contraction values of one column -- the MFMA operand layout -- so no operand is
+// transposed in registers.  Both layouts XOR-swizzle 16-byte slots so fragment reads
+// are free of bank conflicts on gfx950's 64-bank LDS.
+//
+// Ping-pong: the two waves of a SIMD (wm = 0 and 1) run the same phase sequence --
+// read a 32-deep step of fragments from LDS, barrier, that step's MFMAs, barrier --
+// but the wm = 1 waves start one barrier later.  So while one wave of each SIMD
+// issues MFMAs, the other reads LDS, and the MFMA pipe of each SIMD is fed by one
+// wave at a time.  Four phases per stage, one workgroup barrier after each.
+//
+// Two schedules of the same loop:
+//   DIRECT (forward): direct buffer->LDS loads (16 bytes per lane, no VGPRs) of stage
+//     kt + 1 issued at the start of stage kt; 16x16x32 MFMAs.  These GEMMs run at
+//     the chip's power limit, and the 16x16x32 MFMA does the same work as the
+//     32x32x16 one for less energy (at the same throughput per clock), which lets the
+//     engine clock stay higher.
+//   STAGED (dgrad, wgrad): loads go global -> VGPR and are written to the ring by the
+//     waves themselves, in the middle of a compute phase, a stage later; the loads of
+//     stage kt + 2 go out in the read phase after stage kt + 1 is written, and the
+//     direct-load return path no longer competes with the transpose reads for LDS.
+//     32x32x16 MFMAs (two 16-deep steps per phase).  The wgrad tiles of the first
+//     column also add their dy stages into the bias gradient from the staging
+//     registers, before each stage is written to the ring.
 //
 // Loads: per lane the address of a piece is a fixed 32-bit offset from a
 // wave-uniform tile base held in a buffer resource (scalar registers), so issuing a
 // stage costs no vector arithmetic; the base advances by one stage per tile.
 //
-// Pipeline, per stage kt: the loads of stage kt + kS - 1 go out first, into the
-// slot stage kt - 1 used; MFMA steps run while the fragments of the following step
-// are read; before the last step every wave waits for its own loads of stage kt + 1
-// and the workgroup meets at one barrier, after which the last step's MFMAs run
-// while the first fragments of stage kt + 1 are read.
-//
 // Masking: rows past the valid extent of a K-major tile are clamped onto a valid
 // row (their products land in output rows that are never stored); columns past an
 // MN-major tile's extent are clamped likewise; contraction indices past the end
 // (the last stage of a group in wgrad, or a contraction length not a multiple of
-// kBK) are not loaded -- those lanes write zeros into their LDS slot instead.
+// kBK) are not loaded -- those lanes put zeros into their LDS slot instead.
 //
 // Scheduling: persistent grid, one workgroup per CU; workgroup b walks items b,
 // b + grid, ...; items are remapped so each XCD (blockIdx % 8) works on a run of
@@ -51,11 +63,17 @@ namespace gl {
 
 namespace gemm {
 
-// F16: the operands are fp16 (v_mfma_f32_32x32x16_f16) instead of bf16; staging and
-// fragments are the same 16-byte moves of 2-byte elements.
-// BGRAD (wgrad only): the tiles of the first column also produce the bias gradient.
-template <bool A_KMAJ, bool B_KMAJ, int MODE, bool F16, bool BGRAD = false>
+enum { SCHED_DIRECT = 0, SCHED_STAGED = 1 };
+
+// F16: the operands are fp16 instead of bf16; staging and fragments are the same
+// 16-byte moves of 2-byte elements.
+// BGRAD (wgrad, STAGED only): the tiles of the first column also produce the bias
+// gradient.
+template <bool A_KMAJ, bool B_KMAJ, int MODE, bool F16, int SCHED, bool BGRAD = false>
 __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
+  static_assert(!BGRAD || SCHED == SCHED_STAGED, "the bias-grad fusion runs on the staged schedule");
+  using ACC = typename std::conditional<SCHED == SCHED_DIRECT, Acc16, Acc32>::type;
+  using L = AccLayout<ACC>;
   // the stage ring; wgrad adds the bias-grad partial sums after it (one LDS object:
   // a second __shared__ array makes the compiler wait for the direct loads before
   // every LDS read)
@@ -74,21 +92,22 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
   const int first = (grid & 7) == 0 ? (b & 7) * (grid >> 3) + (b >> 3) : b;
   const int nk_rows = (int)((p.P + kBK - 1) / kBK);  // row mode: the same for every tile
   const int slots = min(max(ws.hdr->split_slots, 0), kSplitSlots);
+  auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
+  auto barrier = [&] {
+    __builtin_amdgcn_s_barrier();
+    fence();
+  };
 
   // One work item: the whole contraction of a tile, or (SPLIT) part `part` of S of
-  // the u-th split tile.  A wgrad tile of the first column, when a bias gradient is
-  // asked for, also sums its dy stages into the bias gradient of its n range (a
-  // uniform run-time switch: a second copy of the loop would cost registers).
+  // the u-th split tile.
   auto item = [&](int tile, int part, int S, int u, auto split_tag) __attribute__((always_inline)) {
     constexpr bool SPLIT = decltype(split_tag)::value;
     const Tile t = decode_tile<A_KMAJ, B_KMAJ, MODE>(p, off, pre, tile);
     const bool bgrad = BGRAD && t.jt == 0;
-    float *dbl = (float *)(lds + kS * kStageBytes);  // bias grad partials [kDbGroups][256 columns]
     if (MODE == MODE_CONTR && p.accumulate && t.g_rows == 0) {  // main_grad untouched
       if (bgrad) store_bgrad_zero(p, t);
       return;
     }
-    if (bgrad) db_zero(dbl);
     const int64_t pmax = t.pmax;
     const int nk = (int)((pmax + kBK - 1) / kBK);
     const int nfull = (int)(pmax / kBK);  // stages [0, nfull) are complete; nk - nfull <= 1
@@ -102,107 +121,183 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
     sa.init(t.a_base, p.lda, t.a_rv, wave, lane);
     sb.init(t.b_base, p.ldb, t.b_rv, wave, lane);
     auto stage_ptr = [&](int s) { return lds + (s % kS) * kStageBytes; };
-    auto issue = [&](int s) {
-      char *st = stage_ptr(s);
-      if (s < nfull) {
-        sa.issue_full(s, st, wave);
-        sb.issue_full(s, st + kOpBytes, wave);
-      } else {
-        sa.issue_masked(s, pmax, st, wave, lane);
-        sb.issue_masked(s, pmax, st + kOpBytes, wave, lane);
-      }
-    };
 
-    // -------------------------------------------------------------- main loop
-    f32x16_t acc[kNI][kNJ];
-#pragma unroll
-    for (int ii = 0; ii < kNI; ++ii)
-#pragma unroll
-      for (int jj = 0; jj < kNJ; ++jj)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) acc[ii][jj][q] = 0.f;
+    ACC acc;
+    L::zero(acc);
+    const int h = wm;  // ping-pong group
+    float dbr[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};  // bias-grad column sums (STAGED)
 
-    auto load_frags = [&](int s, int ks, bf16x8_t *af, bf16x8_t *bfr) {
-      const char *ta = stage_ptr(s);
-      const char *tb = ta + kOpBytes;
+    if constexpr (SCHED == SCHED_DIRECT) {
+      auto issue = [&](int s) {
+        char *st = stage_ptr(s);
+        if (s < nfull) {
+          sa.issue_full(s, st, wave);
+          sb.issue_full(s, st + kOpBytes, wave);
+        } else {
+          sa.issue_masked(s, pmax, st, wave, lane);
+          sb.issue_masked(s, pmax, st + kOpBytes, wave, lane);
+        }
+      };
+      bf16x8_t fa[kNI16], fb[kNJ16];
+      auto read_step = [&](int s, int ks) {
+        const char *ta = stage_ptr(s);
+        const char *tb = ta + kOpBytes;
 #pragma unroll
-      for (int ii = 0; ii < kNI; ++ii)
-        af[ii] = A_KMAJ ? frag_kmaj(ta, wm * kWTM + ii * 32, ks, lane) : frag_mnmaj(ta, wm * kWTM + ii * 32, ks, lane);
+        for (int ii = 0; ii < kNI16; ++ii)
+          fa[ii] = A_KMAJ ? frag16_kmaj(ta, wm * kWTM + ii * 16, ks, lane)
+                          : frag16_mnmaj(ta, wm * kWTM + ii * 16, ks, lane);
 #pragma unroll
-      for (int jj = 0; jj < kNJ; ++jj)
-        bfr[jj] = B_KMAJ ? frag_kmaj(tb, wn * kWTN + jj * 32, ks, lane) : frag_mnmaj(tb, wn * kWTN + jj * 32, ks, lane);
-    };
-    auto mfmas = [&](const bf16x8_t *af, const bf16x8_t *bfr) {
-      // operands swapped so each lane ends up with 4 consecutive output columns
+        for (int jj = 0; jj < kNJ16; ++jj)
+          fb[jj] = B_KMAJ ? frag16_kmaj(tb, wn * kWTN + jj * 16, ks, lane)
+                          : frag16_mnmaj(tb, wn * kWTN + jj * 16, ks, lane);
+      };
+      auto compute_step = [&]() {
 #pragma unroll
-      for (int ii = 0; ii < kNI; ++ii)
+        for (int ii = 0; ii < kNI16; ++ii)
 #pragma unroll
-        for (int jj = 0; jj < kNJ; ++jj)
-          acc[ii][jj] = F16 ? __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, bfr[jj]),
-                                                                    __builtin_bit_cast(f16x8_t, af[ii]), acc[ii][jj],
-                                                                    0, 0, 0)
-                            : __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[jj], af[ii], acc[ii][jj], 0, 0, 0);
-    };
-
-    bf16x8_t fa[2][kNI], fb[2][kNJ];
-    // prologue: stages kbeg .. kbeg+kS-2 in flight, stage kbeg visible, its step 0
-    // fragments read
-    for (int s = kbeg; s < kbeg + kS - 1 && s < kend; ++s) issue(s);
-    if (kend > kbeg) {
-      wait_vm0();
-      __builtin_amdgcn_s_barrier();
-      load_frags(kbeg, 0, fa[0], fb[0]);
-    }
-    // One stage per iteration; fragment set (ks & 1) feeds MFMA step ks while set
-    // (ks + 1) & 1 is refilled.  The barrier before the last step makes stage kt + 1
-    // visible and frees the slot stage kt used, which the next iteration refills.
-    static_assert((kKS & 1) == 0, "step 0 of every stage must read fragment set 0");
-    // Scheduling fences keep the order written here: the next step's fragment reads
-    // go out before the current step's MFMAs, so each read has a whole block of
-    // MFMAs to complete in.
-    auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
-    auto body = [&](int kt, bool steady) {
-      if (steady) {
-        char *st = stage_ptr(kt + kS - 1);
-        sa.issue_full(kt + kS - 1, st, wave);
-        sb.issue_full(kt + kS - 1, st + kOpBytes, wave);
-      } else if (kt + kS - 1 < kend) {
-        issue(kt + kS - 1);
-      }
-      fence();
-#pragma unroll
-      for (int ks = 0; ks < kKS - 1; ++ks) {
-        load_frags(kt, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
-        fence();
-        mfmas(fa[ks & 1], fb[ks & 1]);
-        fence();
-      }
-      // stage kt stays in its slot until the barrier below
-      if (BGRAD && bgrad) db_stage<F16>(stage_ptr(kt), dbl);
-      // stage kt + 1 complete: at most the loads of stages kt + 2 .. kt + kS - 1
-      // may still be in flight
-      if (steady)
-        wait_vm<(kS - 2) * kLoadsPerStage>();
-      else
+          for (int jj = 0; jj < kNJ16; ++jj)
+            acc[ii][jj] = F16 ? __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, fb[jj]),
+                                                                      __builtin_bit_cast(f16x8_t, fa[ii]),
+                                                                      acc[ii][jj], 0, 0, 0)
+                              : __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[jj], fa[ii], acc[ii][jj], 0, 0, 0);
+      };
+      static_assert(kBK == 64, "two 32-deep steps per stage");
+      if (kend > kbeg) {
+        issue(kbeg);
         wait_vm0();
-      wait_lgkm0();
-      __builtin_amdgcn_s_barrier();
-      if (steady || kt + 1 < kend) load_frags(kt + 1, 0, fa[0], fb[0]);
-      fence();
-      mfmas(fa[(kKS - 1) & 1], fb[(kKS - 1) & 1]);
-      fence();
-    };
-
-    int kt = kbeg;
-    for (; kt + kS - 1 < kfull; ++kt) body(kt, true);  // every stage issued here is complete
-    for (; kt < kend; ++kt) body(kt, false);
+        barrier();
+      }
+      if (h == 1) barrier();
+      auto body = [&](int kt, bool steady) {
+        if (steady) {
+          char *st = stage_ptr(kt + 1);
+          sa.issue_full(kt + 1, st, wave);
+          sb.issue_full(kt + 1, st + kOpBytes, wave);
+        } else if (kt + 1 < kend) {
+          issue(kt + 1);
+        }
+        fence();
+        read_step(kt, 0);
+        wait_lgkm0();
+        fence();
+        barrier();
+        compute_step();
+        fence();
+        barrier();
+        read_step(kt, 1);
+        wait_lgkm0();
+        fence();
+        wait_vm0();  // stage kt + 1 complete before the barrier after which group 0 reads it
+        barrier();
+        compute_step();
+        fence();
+        barrier();
+      };
+      int kt = kbeg;
+      for (; kt + 1 < kfull; ++kt) body(kt, true);  // the stage issued here is complete
+      for (; kt < kend; ++kt) body(kt, false);
+    } else {
+      uint4 ra[kQ], rb[kQ];
+      auto load_stage = [&](int st_, bool full) {
+        if (full) {
+          sa.load_regs(st_, ra);
+          sb.load_regs(st_, rb);
+        } else {
+          sa.load_regs_masked(st_, pmax, ra, wave, lane);
+          sb.load_regs_masked(st_, pmax, rb, wave, lane);
+        }
+      };
+      auto write_stage = [&](int st_) {
+        char *st = stage_ptr(st_);
+        sa.write_regs(st, ra, wave, lane);
+        sb.write_regs(st + kOpBytes, rb, wave, lane);
+      };
+      constexpr int kH = kKS / 2;  // 16-deep steps per phase
+      bf16x8_t fa[kH][kNI], fb[kH][kNJ];
+      auto read_half = [&](int s, int half) {
+        const char *ta = stage_ptr(s);
+        const char *tb = ta + kOpBytes;
+#pragma unroll
+        for (int ks = 0; ks < kH; ++ks) {
+#pragma unroll
+          for (int ii = 0; ii < kNI; ++ii)
+            fa[ks][ii] = A_KMAJ ? frag_kmaj(ta, wm * kWTM + ii * 32, half * kH + ks, lane)
+                                : frag_mnmaj(ta, wm * kWTM + ii * 32, half * kH + ks, lane);
+#pragma unroll
+          for (int jj = 0; jj < kNJ; ++jj)
+            fb[ks][jj] = B_KMAJ ? frag_kmaj(tb, wn * kWTN + jj * 32, half * kH + ks, lane)
+                                : frag_mnmaj(tb, wn * kWTN + jj * 32, half * kH + ks, lane);
+        }
+      };
+      auto compute = [&](int ks) {
+#pragma unroll
+        for (int ii = 0; ii < kNI; ++ii)
+#pragma unroll
+          for (int jj = 0; jj < kNJ; ++jj)
+            acc[ii][jj] = F16 ? __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, fb[ks][jj]),
+                                                                      __builtin_bit_cast(f16x8_t, fa[ks][ii]),
+                                                                      acc[ii][jj], 0, 0, 0)
+                              : __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks][jj], fa[ks][ii], acc[ii][jj], 0,
+                                                                        0, 0);
+      };
+      static_assert(kH == 2, "two 16-deep steps per phase");
+      if (kend > kbeg) {
+        load_stage(kbeg, kbeg < nfull);
+        wait_vm0();
+        if (BGRAD && bgrad) db_add<F16>(dbr, ra);
+        write_stage(kbeg);
+        if (kbeg + 1 < kend) load_stage(kbeg + 1, kbeg + 1 < nfull);
+        wait_lgkm0();
+        barrier();
+      }
+      if (h == 1) barrier();
+      // Per stage kt, four phases per wave: read the first half stage (and add the
+      // stage's rows into the bias gradient); its MFMAs, with the ring writes of
+      // stage kt + 1 between the two steps; read the second half and send the loads
+      // of stage kt + 2; its MFMAs.
+      auto body = [&](int kt, bool steady) {
+        read_half(kt, 0);
+        wait_lgkm0();
+        fence();
+        barrier();
+        compute(0);
+        fence();
+        if (steady || kt + 1 < kend) {
+          wait_vm0();
+          if (BGRAD && bgrad) db_add<F16>(dbr, ra);  // dy rows of stage kt + 1
+          write_stage(kt + 1);
+        }
+        fence();
+        compute(1);
+        fence();
+        wait_lgkm0();
+        barrier();
+        read_half(kt, 1);
+        fence();
+        if (steady)
+          load_stage(kt + 2, true);
+        else if (kt + 2 < kend)
+          load_stage(kt + 2, kt + 2 < nfull);
+        fence();
+        wait_lgkm0();
+        barrier();
+        compute(0);
+        compute(1);
+        fence();
+        barrier();
+      };
+      int kt = kbeg;
+      for (; kt + 2 < kfull; ++kt) body(kt, true);  // stages kt + 1 and kt + 2 are complete
+      for (; kt < kend; ++kt) body(kt, false);
+    }
+    if (h == 0) barrier();
     __builtin_amdgcn_s_barrier();  // every wave is done with the ring before it is refilled
 
     if constexpr (SPLIT) {
       // the ring is idle after the loop's last barrier: its first word carries the flag
       if (!split_finish(ws, u, part, S, acc, (int *)lds)) return;
     }
-    if (BGRAD && bgrad) store_bgrad<F16>(p, t, dbl);
+    if (BGRAD && bgrad) store_bgrad<F16>(p, t, dbr, (float *)(lds + kS * kStageBytes), wave, lane);
     // wgrad tiles contract over one group's rows only, so their output stores weigh
     // more: there the tile goes out through LDS as whole lines (measured neutral to
     // slightly worse for forward and dgrad, which keep the direct stores)
@@ -241,10 +336,10 @@ hipError_t launch_forward_bf16(int G, int64_t K, int64_t N, int64_t T, const uin
   p.tiles_j = (int)((N + kBN - 1) / kBN);
   const int64_t max_items = ((T + kBM - 1) / kBM + G) * p.tiles_j;
   if (f16)
-    hipLaunchKernelGGL((gemm_bf16_kernel<true, true, MODE_ROWS, true>), dim3(persistent_grid(max_items)),
+    hipLaunchKernelGGL((gemm_bf16_kernel<true, true, MODE_ROWS, true, SCHED_DIRECT>), dim3(persistent_grid(max_items)),
                        dim3(kThreads), 0, s, p);
   else
-    hipLaunchKernelGGL((gemm_bf16_kernel<true, true, MODE_ROWS, false>), dim3(persistent_grid(max_items)),
+    hipLaunchKernelGGL((gemm_bf16_kernel<true, true, MODE_ROWS, false, SCHED_DIRECT>), dim3(persistent_grid(max_items)),
                        dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
@@ -262,10 +357,10 @@ hipError_t launch_dgrad_bf16(int G, int64_t K, int64_t N, int64_t T, const uint1
   p.tiles_j = (int)((K + kBN - 1) / kBN);
   const int64_t max_items = ((T + kBM - 1) / kBM + G) * p.tiles_j;
   if (f16)
-    hipLaunchKernelGGL((gemm_bf16_kernel<true, false, MODE_ROWS, true>), dim3(persistent_grid(max_items)),
+    hipLaunchKernelGGL((gemm_bf16_kernel<true, false, MODE_ROWS, true, SCHED_STAGED>), dim3(persistent_grid(max_items)),
                        dim3(kThreads), 0, s, p);
   else
-    hipLaunchKernelGGL((gemm_bf16_kernel<true, false, MODE_ROWS, false>), dim3(persistent_grid(max_items)),
+    hipLaunchKernelGGL((gemm_bf16_kernel<true, false, MODE_ROWS, false, SCHED_STAGED>), dim3(persistent_grid(max_items)),
                        dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
@@ -290,13 +385,13 @@ hipError_t launch_wgrad_bf16(int G, int64_t K, int64_t N, int64_t T, const uint1
   const dim3 grid(persistent_grid(max_items)), block(kThreads);
   const bool bg = db || db_ptrs;
   if (f16 && bg)
-    hipLaunchKernelGGL((gemm_bf16_kernel<false, false, MODE_CONTR, true, true>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((gemm_bf16_kernel<false, false, MODE_CONTR, true, SCHED_STAGED, true>), grid, block, 0, s, p);
   else if (f16)
-    hipLaunchKernelGGL((gemm_bf16_kernel<false, false, MODE_CONTR, true>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((gemm_bf16_kernel<false, false, MODE_CONTR, true, SCHED_STAGED>), grid, block, 0, s, p);
   else if (bg)
-    hipLaunchKernelGGL((gemm_bf16_kernel<false, false, MODE_CONTR, false, true>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((gemm_bf16_kernel<false, false, MODE_CONTR, false, SCHED_STAGED, true>), grid, block, 0, s, p);
   else
-    hipLaunchKernelGGL((gemm_bf16_kernel<false, false, MODE_CONTR, false>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((gemm_bf16_kernel<false, false, MODE_CONTR, false, SCHED_STAGED>), grid, block, 0, s, p);
   return hipGetLastError();
 }
 

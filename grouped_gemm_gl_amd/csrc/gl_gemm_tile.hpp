@@ -90,11 +90,13 @@ struct Params {
 // consecutive rows share a 256-byte bank window, so the slot must differ across
 // r / (16 / kChunks).
 // MN-major rows are 512 bytes (32 slots): chunk c of contraction row p sits in slot
-// c ^ swz_m(p).  A transpose read serves 4 rows x 64 bytes per 32 lanes; the rows
-// are 512 bytes apart (same banks), so the XOR moves each row's 64 bytes to its own
-// quarter of the 256-byte window.
+// c ^ swz_m(p).  The rows are 512 bytes apart (same banks).  A 32x32x16 transpose
+// read serves rows p .. p + 3 x 64 bytes per 32 lanes: bits 2-3 of the slot move
+// each row's 64 bytes to its own quarter of the 256-byte window.  A 16x16x32
+// transpose read serves rows p .. p + 3 and p + 8 .. p + 11 x 32 bytes: bit 1 of
+// the slot then separates p from p + 8.
 __device__ __forceinline__ int swz_k(int r) { return (r / (16 / kChunks)) & (kChunks - 1); }
-__device__ __forceinline__ int swz_m(int p) { return (p & 3) << 2; }
+__device__ __forceinline__ int swz_m(int p) { return ((p & 3) << 2) | (((p >> 3) & 1) << 1); }
 
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0f70); }
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xc07f); }
@@ -153,6 +155,37 @@ struct Stream {
                                                0);
   }
 
+  // Register staging: this lane's pieces of stage t into r (global -> VGPRs), written
+  // to the ring later by write_regs at the same LDS places the direct loads fill.
+  __device__ __forceinline__ void load_regs(int t, uint4 (&r)[kQ]) const {
+    const __amdgpu_buffer_rsrc_t rs = rsrc_at(base + (int64_t)t * step);
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, off[q], 0, 0);
+      r[q] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+  }
+  // The last stage of a contraction: pieces past pmax are zeros.
+  __device__ __forceinline__ void load_regs_masked(int t, int64_t pmax, uint4 (&r)[kQ], int wave, int lane) const {
+    const __amdgpu_buffer_rsrc_t rs = rsrc_at(base + (int64_t)t * step);
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) {
+      const int u = wave + kWaves * q;
+      const int pfirst =
+          KMAJ ? ((lane % kChunks) ^ swz_k(kRowsPerPiece * u + lane / kChunks)) * 8 : 2 * u + (lane >> 5);
+      if ((int64_t)t * kBK + pfirst < pmax) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, off[q], 0, 0);
+        r[q] = make_uint4(v[0], v[1], v[2], v[3]);
+      } else {
+        r[q] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  }
+  __device__ __forceinline__ void write_regs(char *st, const uint4 (&r)[kQ], int wave, int lane) const {
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) *(uint4 *)(st + (wave + kWaves * q) * 1024 + lane * 16) = r[q];
+  }
+
   // The last stage of a contraction: lanes whose piece lies past pmax write zeros
   // into their LDS slot instead of loading.
   __device__ __forceinline__ void issue_masked(int t, int64_t pmax, char *st, int wave, int lane) const {
@@ -197,6 +230,93 @@ __device__ __forceinline__ bf16x8_t frag_mnmaj(const char *st, int col0, int ks,
   const v8i16 v = {h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
   return __builtin_bit_cast(bf16x8_t, v);
 }
+
+// 16x16x32 operand fragment (16 rows/columns x 32 contraction values; lane l holds
+// row l % 16, contraction values 8 (l / 16) + 0..7) for the 32-deep step s of a stage.
+constexpr int kNI16 = kWTM / 16, kNJ16 = kWTN / 16;  // 16x16 MFMA blocks per wave
+__device__ __forceinline__ bf16x8_t frag16_kmaj(const char *st, int row0, int s, int lane) {
+  const int r = row0 + (lane & 15);
+  const int c = 4 * s + (lane >> 4);
+  return *(const bf16x8_t *)(st + r * kRowB + ((c ^ swz_k(r)) << 4));
+}
+
+__device__ __forceinline__ bf16x8_t frag16_mnmaj(const char *st, int col0, int s, int lane) {
+  // lane q of a 16-lane group names contraction row q / 4 and columns 4 (q % 4) .. + 3
+  // of the group's 4 rows; the transpose hands lane q column q of those rows.  Group
+  // g (lanes 16 g ..) takes contraction rows 8 g .. 8 g + 7 of the step.
+  const int q = lane & 15, grp = lane >> 4;
+  const int col = col0 + ((q & 3) << 2);
+  const int chunk = col >> 3, within = col & 7;
+  v4i16 h[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int prow = s * 32 + grp * 8 + t * 4 + (q >> 2);
+    const char *a = st + prow * 512 + ((chunk ^ swz_m(prow)) << 4) + within * 2;
+    h[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GL_LDS v4i16 *)a);
+  }
+  const v8i16 v = {h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// ------------------------------------------------------ accumulator layouts --
+// A wave's 128 x 64 block of fp32 accumulators in the two MFMA shapes, seen as 32
+// "quads" per lane: 4 consecutive output columns (il, jl .. jl + 3) of one row
+// (operands are swapped in the MFMAs so a lane's 4 values run along a row).
+//   32x32x16: 4 x 2 blocks of f32x16; quad q = (ii, jj, q4) holds row ii*32 + l%32,
+//             columns jj*32 + q4*8 + (l/32)*4 ..
+//   16x16x32: 8 x 4 blocks of f32x4; quad q = (ii, jj) holds row ii*16 + l%16,
+//             columns jj*16 + (l/16)*4 ..
+typedef f32x16_t Acc32[kNI][kNJ];
+typedef f32x4_t Acc16[kNI16][kNJ16];
+constexpr int kQuads = 32;
+
+template <class ACC>
+struct AccLayout;
+template <>
+struct AccLayout<Acc32> {
+  __device__ static __forceinline__ void pos(int q, int lane, int &il, int &jl) {
+    il = (q >> 3) * 32 + (lane & 31);
+    jl = ((q >> 2) & 1) * 32 + (q & 3) * 8 + (lane >> 5) * 4;
+  }
+  __device__ static __forceinline__ float4 get(const Acc32 &a, int q) {
+    const f32x16_t &v = a[q >> 3][(q >> 2) & 1];
+    const int b = (q & 3) * 4;
+    return make_float4(v[b], v[b + 1], v[b + 2], v[b + 3]);
+  }
+  __device__ static __forceinline__ void set(Acc32 &a, int q, float4 o) {
+    f32x16_t &v = a[q >> 3][(q >> 2) & 1];
+    const int b = (q & 3) * 4;
+    v[b] = o.x; v[b + 1] = o.y; v[b + 2] = o.z; v[b + 3] = o.w;
+  }
+  __device__ static __forceinline__ void zero(Acc32 &a) {
+#pragma unroll
+    for (int ii = 0; ii < kNI; ++ii)
+#pragma unroll
+      for (int jj = 0; jj < kNJ; ++jj)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) a[ii][jj][e] = 0.f;
+  }
+};
+template <>
+struct AccLayout<Acc16> {
+  __device__ static __forceinline__ void pos(int q, int lane, int &il, int &jl) {
+    il = (q >> 2) * 16 + (lane & 15);
+    jl = (q & 3) * 16 + (lane >> 4) * 4;
+  }
+  __device__ static __forceinline__ float4 get(const Acc16 &a, int q) {
+    const f32x4_t &v = a[q >> 2][q & 3];
+    return make_float4(v[0], v[1], v[2], v[3]);
+  }
+  __device__ static __forceinline__ void set(Acc16 &a, int q, float4 o) {
+    a[q >> 2][q & 3] = (f32x4_t){o.x, o.y, o.z, o.w};
+  }
+  __device__ static __forceinline__ void zero(Acc16 &a) {
+#pragma unroll
+    for (int ii = 0; ii < kNI16; ++ii)
+#pragma unroll
+      for (int jj = 0; jj < kNJ16; ++jj) a[ii][jj] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  }
+};
 
 // Stores 4 consecutive output columns of one row: optional bias (per output
 // column, of the output's type), optional accumulate into the existing values.
@@ -311,55 +431,55 @@ __device__ __forceinline__ Tile decode_tile(const Params &p, const int64_t *__re
 }
 
 // ------------------------------------------------------- bias grad in wgrad --
-// A wgrad tile (n tile it, k tile jt) streams the group's dy[:, n tile] through the
-// ring as its A operand, MN-major: stage row p (a token row) holds the tile's 256
-// n values, 16-byte chunk c in slot c ^ swz_m(p).  The tiles of the first k column
-// also sum those rows: thread (row group rg = tid / 64, 4-column group c = tid % 64)
-// adds rows rg, rg + 8, ..., rg + 56 of every stage into its own 4 fp32 slots of an
-// LDS area [8][256]; at the end the 8 partials of each column are added and stored.
-// db_g = sum over the group's rows of dy, read once for both outputs.  Rows past
-// the group's end are zero in the ring, so they add nothing.  (Four columns per
-// thread keep the extra registers few: the loop runs at the register limit.)
-constexpr int kDbGroups = kThreads / 64;
-constexpr int kDbLdsBytes = kDbGroups * 256 * 4;
-static_assert(kThreads == 512 && kBK == 64, "bias-grad thread mapping");
+// A wgrad tile (n tile it, k tile jt) streams the group's dy[:, n tile] as its A
+// operand, MN-major, through the staging registers: piece q of a lane holds the 8
+// columns c*8 .. c*8 + 7 of contraction row p = 2 (wave + 8 q) + lane / 32, with
+// c = (lane % 32) ^ swz_m(p).  The swizzle of p does not depend on q, so a lane's
+// pieces of every stage cover the same 8 columns: the tiles of the first k column
+// add each stage's pieces, as they come in, into 8 fp32 column sums per lane (rows
+// past the group's end are zero pieces and add nothing).  At the end the 16 partial
+// sums of each column (8 waves x 2 lane halves) meet in LDS in a fixed order.
+// db_g = sum over the group's rows of dy, read once for both outputs.
+constexpr int kDbParts = 2 * kWaves;
+constexpr int kDbLdsBytes = kDbParts * 256 * 4;
+static_assert(kThreads == 512 && kBK == 64 && kQ == 4, "bias-grad lane mapping");
 
-__device__ __forceinline__ void db_zero(float *dbl) {
-  *(float4 *)(dbl + (threadIdx.x >> 6) * 256 + (threadIdx.x & 63) * 4) = make_float4(0.f, 0.f, 0.f, 0.f);
+// first tile column this lane's bias-grad sums cover
+__device__ __forceinline__ int db_col(int wave, int lane) {
+  return ((lane & 31) ^ swz_m(2 * wave + (lane >> 5))) * 8;
 }
 
 template <bool F16>
-__device__ __forceinline__ void db_stage(const char *st, float *dbl) {
-  const int c = threadIdx.x & 63, rg = threadIdx.x >> 6;
-  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+__device__ __forceinline__ void db_add(float (&dbr)[8], const uint4 (&r)[kQ]) {
 #pragma unroll
-  for (int q = 0; q < kBK / kDbGroups; ++q) {
-    const int r = rg + kDbGroups * q;
-    const uint2 v = *(const uint2 *)(st + r * 512 + (((c >> 1) ^ swz_m(r)) << 4) + (c & 1) * 8);
-    s0 += h16_to_f32<F16>((uint16_t)(v.x & 0xffffu));
-    s1 += h16_to_f32<F16>((uint16_t)(v.x >> 16));
-    s2 += h16_to_f32<F16>((uint16_t)(v.y & 0xffffu));
-    s3 += h16_to_f32<F16>((uint16_t)(v.y >> 16));
+  for (int q = 0; q < kQ; ++q) {
+    const uint32_t d[4] = {r[q].x, r[q].y, r[q].z, r[q].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      dbr[2 * e] += h16_to_f32<F16>((uint16_t)(d[e] & 0xffffu));
+      dbr[2 * e + 1] += h16_to_f32<F16>((uint16_t)(d[e] >> 16));
+    }
   }
-  float4 *slot = (float4 *)(dbl + rg * 256 + c * 4);
-  float4 a = *slot;
-  a.x += s0; a.y += s1; a.z += s2; a.w += s3;
-  *slot = a;
 }
 
 __device__ __forceinline__ uintptr_t db_row(const Params &p, int g) {
   return p.db ? (uintptr_t)p.db + (uintptr_t)((int64_t)g * p.rows_i * (p.db_f32 ? 4 : 2)) : (uintptr_t)p.db_ptrs[g];
 }
 
-// Adds the kDbGroups partials of each column and stores db[g][n tile]; whole workgroup.
+// Adds the kDbParts partials of each column in a fixed order and stores db[g][n
+// tile]; whole workgroup; `dbl` is an idle LDS area of kDbLdsBytes.
 template <bool F16>
-__device__ __forceinline__ void store_bgrad(const Params &p, const Tile &t, const float *dbl) {
-  __syncthreads();  // every thread's last stage is in the partials
+__device__ __forceinline__ void store_bgrad(const Params &p, const Tile &t, const float (&dbr)[8], float *dbl,
+                                            int wave, int lane) {
+  float *part = dbl + (2 * wave + (lane >> 5)) * 256 + db_col(wave, lane);
+  *(float4 *)part = make_float4(dbr[0], dbr[1], dbr[2], dbr[3]);
+  *(float4 *)(part + 4) = make_float4(dbr[4], dbr[5], dbr[6], dbr[7]);
+  __syncthreads();
   const int col = threadIdx.x;
   if (col < t.a_rv) {
     float v = 0.f;
 #pragma unroll
-    for (int rg = 0; rg < kDbGroups; ++rg) v += dbl[rg * 256 + col];
+    for (int k = 0; k < kDbParts; ++k) v += dbl[k * 256 + col];
     const uintptr_t row = db_row(p, t.g);
     const int64_t n = (int64_t)t.it * kBM + col;
     if (p.db_f32)
@@ -424,20 +544,15 @@ __device__ __forceinline__ SplitPlan split_plan(int tiles, int grid, int nk, int
 // (The flag lives inside the kernel's one LDS array: a second __shared__ object
 // makes the compiler wait for every direct-to-LDS load before each LDS read.)  The parts of the last
 // round are items u + rem * part, so a part's CUs on one XCD run neighbouring tiles.
-__device__ __forceinline__ bool split_finish(const WsView &ws, int u, int part, int S, f32x16_t (&acc)[kNI][kNJ],
-                                             int *flag) {
+template <class ACC>
+__device__ __forceinline__ bool split_finish(const WsView &ws, int u, int part, int S, ACC &acc, int *flag) {
+  using L = AccLayout<ACC>;
   const int tid = threadIdx.x;
   constexpr size_t kSlotF4 = kPartialBytes / 16;
   GL_GLOBAL float4 *slots = (GL_GLOBAL float4 *)ws.split_part + (size_t)u * S * kSlotF4;
   GL_GLOBAL float4 *mine = slots + (size_t)part * kSlotF4;
 #pragma unroll
-  for (int ii = 0; ii < kNI; ++ii)
-#pragma unroll
-    for (int jj = 0; jj < kNJ; ++jj)
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        mine[((ii * kNJ + jj) * 4 + c) * kThreads + tid] =
-            make_float4(acc[ii][jj][4 * c], acc[ii][jj][4 * c + 1], acc[ii][jj][4 * c + 2], acc[ii][jj][4 * c + 3]);
+  for (int q = 0; q < kQuads; ++q) mine[q * kThreads + tid] = L::get(acc, q);
   __threadfence();  // release: the partial is visible device-wide before the count
   __syncthreads();
   if (tid == 0) {
@@ -453,30 +568,24 @@ __device__ __forceinline__ bool split_finish(const WsView &ws, int u, int part, 
   for (int s = 0; s < S; ++s) {
     const GL_GLOBAL float4 *src = slots + (size_t)s * kSlotF4;
 #pragma unroll
-    for (int ii = 0; ii < kNI; ++ii)
-#pragma unroll
-      for (int jj = 0; jj < kNJ; ++jj)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const float4 o = src[((ii * kNJ + jj) * 4 + c) * kThreads + tid];
-          if (s == 0) {
-            acc[ii][jj][4 * c] = o.x; acc[ii][jj][4 * c + 1] = o.y;
-            acc[ii][jj][4 * c + 2] = o.z; acc[ii][jj][4 * c + 3] = o.w;
-          } else {
-            acc[ii][jj][4 * c] += o.x; acc[ii][jj][4 * c + 1] += o.y;
-            acc[ii][jj][4 * c + 2] += o.z; acc[ii][jj][4 * c + 3] += o.w;
-          }
-        }
+    for (int q = 0; q < kQuads; ++q) {
+      const float4 o = src[q * kThreads + tid];
+      if (s == 0) {
+        L::set(acc, q, o);
+      } else {
+        const float4 c = L::get(acc, q);
+        L::set(acc, q, make_float4(c.x + o.x, c.y + o.y, c.z + o.z, c.w + o.w));
+      }
+    }
   }
   return true;
 }
 
-// Stores a wave's 128 x 64 block of a tile: lane holds C[i][j..j+3] with
-// i = ii*32 + lane%32, j = jj*32 + q4*8 + (lane/32)*4 (operands were swapped in
-// the MFMAs for that); only rows < a_rv and columns < b_rv are written.
-template <int MODE, bool F16 = false>
-__device__ __forceinline__ void store_tile(const Params &p, const Tile &t, const f32x16_t (&acc)[kNI][kNJ], int wm,
-                                           int wn, int lane) {
+// Stores a wave's 128 x 64 block of a tile, quad by quad (see AccLayout); only rows
+// < a_rv and columns < b_rv are written.
+template <int MODE, bool F16 = false, class ACC>
+__device__ __forceinline__ void store_tile(const Params &p, const Tile &t, const ACC &acc, int wm, int wn, int lane) {
+  using L = AccLayout<ACC>;
   char *cbase;
   int64_t row0;
   if (MODE == MODE_ROWS) {
@@ -490,36 +599,31 @@ __device__ __forceinline__ void store_tile(const Params &p, const Tile &t, const
   if (p.bias) bias_g = (const char *)p.bias + (int64_t)t.g * p.cols_j * (p.out_f32 ? 4 : 2);
   else if (p.bias_ptrs) bias_g = (const char *)p.bias_ptrs[t.g];
 #pragma unroll
-  for (int ii = 0; ii < kNI; ++ii) {
-    const int il = wm * kWTM + ii * 32 + (lane & 31);
-    if (il >= t.a_rv) continue;
-    const int64_t row = row0 + il;
-#pragma unroll
-    for (int jj = 0; jj < kNJ; ++jj) {
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int jl = wn * kWTN + jj * 32 + q4 * 8 + (lane >> 5) * 4;
-        if (jl >= t.b_rv) continue;
-        store4<F16>((uintptr_t)cbase, row, p.ldc, (int64_t)t.jt * kBN + jl, (uintptr_t)bias_g, p.out_f32, p.accumulate,
-                    acc[ii][jj][q4 * 4 + 0],
-               acc[ii][jj][q4 * 4 + 1], acc[ii][jj][q4 * 4 + 2], acc[ii][jj][q4 * 4 + 3]);
-      }
-    }
+  for (int q = 0; q < kQuads; ++q) {
+    int il, jl;
+    L::pos(q, lane, il, jl);
+    il += wm * kWTM;
+    jl += wn * kWTN;
+    if (il >= t.a_rv || jl >= t.b_rv) continue;
+    const float4 v = L::get(acc, q);
+    store4<F16>((uintptr_t)cbase, row0 + il, p.ldc, (int64_t)t.jt * kBN + jl, (uintptr_t)bias_g, p.out_f32,
+                p.accumulate, v.x, v.y, v.z, v.w);
   }
 }
 
 // 16-bit output without accumulate, staged through the idle stage ring so that
 // every store instruction writes whole cache lines.  Written directly, each store
-// instruction would touch 32 rows with 16 bytes each, and every 128-byte line of the
-// output would be assembled in L2 from 8 partial writes; on the MXFP8 wgrad (short
-// contractions, a 1 GiB output) that epilogue took half the kernel's time.
-// The tile goes to LDS as [256 rows][512 B] (16-byte slot s of row r at slot
-// s ^ (r % 32), so the 32 rows one write instruction touches spread over the
+// instruction would touch 32 (or 16) rows with 16 (or 32) bytes each, and every
+// 128-byte line of the output would be assembled in L2 from partial writes; on the
+// MXFP8 wgrad (short contractions, a 1 GiB output) that epilogue took half the
+// kernel's time.  The tile goes to LDS as [256 rows][512 B] (16-byte slot s of row r
+// at slot s ^ (r % 32), so the rows one write instruction touches spread over the
 // banks), then each wave stores 2 rows x 512 B per instruction.  Whole workgroup;
 // needs 128 KiB of `lds`, which no wave may still be reading on entry.
-template <int MODE, bool F16>
-__device__ __forceinline__ void store_tile_lds(const Params &p, const Tile &t, const f32x16_t (&acc)[kNI][kNJ],
-                                               int wm, int wn, int lane, char *lds) {
+template <int MODE, bool F16, class ACC>
+__device__ __forceinline__ void store_tile_lds(const Params &p, const Tile &t, const ACC &acc, int wm, int wn,
+                                               int lane, char *lds) {
+  using L = AccLayout<ACC>;
   uintptr_t cbase;
   int64_t row0;
   if (MODE == MODE_ROWS) {
@@ -534,26 +638,21 @@ __device__ __forceinline__ void store_tile_lds(const Params &p, const Tile &t, c
   else if (p.bias_ptrs) bias_g = (uintptr_t)p.bias_ptrs[t.g];
   __syncthreads();  // a split tile's arrival flag sits in the ring's first word
 #pragma unroll
-  for (int ii = 0; ii < kNI; ++ii) {
-    const int il = wm * kWTM + ii * 32 + (lane & 31);
-#pragma unroll
-    for (int jj = 0; jj < kNJ; ++jj) {
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int jl = wn * kWTN + jj * 32 + q4 * 8 + (lane >> 5) * 4;
-        float v0 = acc[ii][jj][q4 * 4 + 0], v1 = acc[ii][jj][q4 * 4 + 1];
-        float v2 = acc[ii][jj][q4 * 4 + 2], v3 = acc[ii][jj][q4 * 4 + 3];
-        if (bias_g && jl < t.b_rv) {
-          const uint2 bv = *(const GL_GLOBAL uint2 *)(bias_g + ((int64_t)t.jt * kBN + jl) * 2);
-          v0 += h16_to_f32<F16>(bv.x & 0xffff); v1 += h16_to_f32<F16>(bv.x >> 16);
-          v2 += h16_to_f32<F16>(bv.y & 0xffff); v3 += h16_to_f32<F16>(bv.y >> 16);
-        }
-        const int slot = jl >> 3, half = (jl >> 2) & 1;
-        *(uint2 *)(lds + il * 512 + ((slot ^ (il & 31)) << 4) + half * 8) =
-            make_uint2((uint32_t)f32_to_h16<F16>(v0) | ((uint32_t)f32_to_h16<F16>(v1) << 16),
-                       (uint32_t)f32_to_h16<F16>(v2) | ((uint32_t)f32_to_h16<F16>(v3) << 16));
-      }
+  for (int q = 0; q < kQuads; ++q) {
+    int il, jl;
+    L::pos(q, lane, il, jl);
+    il += wm * kWTM;
+    jl += wn * kWTN;
+    float4 v = L::get(acc, q);
+    if (bias_g && jl < t.b_rv) {
+      const uint2 bv = *(const GL_GLOBAL uint2 *)(bias_g + ((int64_t)t.jt * kBN + jl) * 2);
+      v.x += h16_to_f32<F16>(bv.x & 0xffff); v.y += h16_to_f32<F16>(bv.x >> 16);
+      v.z += h16_to_f32<F16>(bv.y & 0xffff); v.w += h16_to_f32<F16>(bv.y >> 16);
     }
+    const int slot = jl >> 3, half = (jl >> 2) & 1;
+    *(uint2 *)(lds + il * 512 + ((slot ^ (il & 31)) << 4) + half * 8) =
+        make_uint2((uint32_t)f32_to_h16<F16>(v.x) | ((uint32_t)f32_to_h16<F16>(v.y) << 16),
+                   (uint32_t)f32_to_h16<F16>(v.z) | ((uint32_t)f32_to_h16<F16>(v.w) << 16));
   }
   __syncthreads();
   const int wave = threadIdx.x >> 6, s = lane & 31;
