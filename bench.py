@@ -17,7 +17,7 @@ Also: the grouped MLP on the 8-group split, and two more workloads at full size
 caller buffer with per-group weights), each against its roofline.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-mxfp8] [--no-mlp] [--no-workloads]
-                    [--no-cpu-baseline]
+                    [--no-cpu-baseline] [--workloads-only]
 """
 from __future__ import annotations
 
@@ -41,10 +41,17 @@ GEMM_SRCS = [os.path.join(ROOT, "grouped_gemm_gl_amd", "csrc", f)
                        "gl_offsets.hpp")]
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 # kernel-name fragment of each pass's GEMM (template arguments <A K-major, B K-major, mode, fp16>)
-PASS_KERNELS = {"forward": "gemm_bf16_kernel<true, true, 0, false, false>",
-                "dgrad": "gemm_bf16_kernel<true, false, 0, false, false>",
-                "wgrad_bgrad": "gemm_bf16_kernel<false, false, 1, false, true>"}
+# (template arguments <A K-major, B K-major, mode, fp16, schedule, bias grad>)
+PASS_KERNELS = {"forward": "gemm_bf16_kernel<true, true, 0, false, 0, false>",
+                "dgrad": "gemm_bf16_kernel<true, false, 0, false, 1, false>",
+                "wgrad_bgrad": "gemm_bf16_kernel<false, false, 1, false, 1, true>"}
 PASS_WORKLOAD = {k: "bf16_train_g8_k4096_n14336" for k in PASS_KERNELS}
+# the GEMM passes of the other full-size workloads (bench.py --workloads-only NAME runs one)
+WORKLOAD_KERNELS = {
+    "bf16_zipf_g64_k2048_n1536": {"forward": PASS_KERNELS["forward"], "dgrad": PASS_KERNELS["dgrad"],
+                                  "wgrad_main_grad": "gemm_bf16_kernel<false, false, 1, false, 1, false>"},
+    "bf16_fwd_g256_k7168_n2048_outbuf": {"forward": PASS_KERNELS["forward"]},
+}
 GEMM_PASSES = tuple(PASS_KERNELS)
 COPY_BYTES = 1 << 30
 
@@ -116,7 +123,7 @@ def _mx_traffic_kernels():
             (f"{wl.name}:mx_wgrad", "gemm_mxfp8_kernel<2>", codes(N, ld) + codes(K, ld) + G * N * K * 2)]
 
 
-def summarize_pmc(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
+def summarize_pmc(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, workload=None):
     """Turn two rocprofv3 --pmc runs of the benchmark (FETCH_SIZE, WRITE_SIZE, in KiB
     per dispatch) into HBM bytes per launch of each pass's GEMM kernel, each counter
     scaled by what it reads for the plain copy of known size; writes the result into
@@ -135,26 +142,27 @@ def summarize_pmc(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
     table = json.load(open(TRAFFIC_JSON)) if os.path.exists(TRAFFIC_JSON) else {}
     sha = source_hash(GEMM_SRCS)
     lines = [f"copy calibration ({COPY_BYTES} B): FETCH_SIZE x{ff:.3f}, WRITE_SIZE x{fw:.3f}"]
-    for name, args in PASS_KERNELS.items():
+    passes = WORKLOAD_KERNELS[workload] if workload else PASS_KERNELS
+    for name, args in passes.items():
         sel = lambda rows: [v for k, v, _ in rows if args in k]
         fv, wv = sel(_pmc_rows(fetch_csv, "FETCH_SIZE")), sel(_pmc_rows(write_csv, "WRITE_SIZE"))
         if not fv or not wv:
             continue
         fb = sum(fv) / len(fv) * 1024.0 * ff
         wb = sum(wv) / len(wv) * 1024.0 * fw
-        workload = PASS_WORKLOAD[name]
-        entry = table.get(f"{workload}:{name}", {})
+        wname = workload or PASS_WORKLOAD[name]
+        entry = table.get(f"{wname}:{name}", {})
         if entry.get("source_sha") != sha:
             entry = {}
         entry.update({"bytes_per_launch": round(fb + wb), "fetch_bytes": round(fb), "write_bytes": round(wb),
                       "launches": len(fv), "source_sha": sha, "fetch_factor": round(ff, 4),
                       "write_factor": round(fw, 4)})
-        table[f"{workload}:{name}"] = entry
-        lines.append(f"{workload}:{name}: fetch {fb / 1e9:.3f} GB + write {wb / 1e9:.3f} GB per launch "
+        table[f"{wname}:{name}"] = entry
+        lines.append(f"{wname}:{name}: fetch {fb / 1e9:.3f} GB + write {wb / 1e9:.3f} GB per launch "
                      f"({len(fv)} launches)")
     # the MXFP8 block's single-shape kernels, when the runs included it: bytes per launch
     # and the rate they imply over the same run's dispatch durations
-    for key, frag, alg in _mx_traffic_kernels():
+    for key, frag, alg in ([] if workload else _mx_traffic_kernels()):
         fr = [(v, d) for k, v, d in _pmc_rows(fetch_csv, "FETCH_SIZE") if frag in k]
         wr = [(v, d) for k, v, d in _pmc_rows(write_csv, "WRITE_SIZE") if frag in k]
         if not fr or not wr:
@@ -189,7 +197,7 @@ CLOCK_KERNELS = [(f"bf16_train_g8_k4096_n14336:{k}", v, "bf16_train_g8_k4096_n14
     ("mxfp8_fwd_g32_k4096_n4096:mx_wgrad", "gemm_mxfp8_kernel<2>", "mxfp8_fwd_g32_k4096_n4096", FP8_FLOP_PER_CLK_CU)]
 
 
-def summarize_clock(pmc_csv):
+def summarize_clock(pmc_csv, workload=None):
     """Fold one rocprofv3 --pmc run of the benchmark with CLOCK_COUNTERS into the
     traffic table: the engine clock each pass's GEMM ran at (GRBM_GUI_ACTIVE is
     summed over the XCDs, so cycles = value / 8, divided by the dispatch's duration),
@@ -203,7 +211,9 @@ def summarize_clock(pmc_csv):
     import synth
 
     lines = [f"{'workload:pass':48s} {'sclk GHz':>9s} {'frac@sclk':>10s} {'MFMA busy':>10s} {'LDS conflicts':>14s}"]
-    for key, args, workload, flop_clk in CLOCK_KERNELS:
+    kernels = ([(f"{workload}:{k}", v, workload, BF16_FLOP_PER_CLK_CU) for k, v in WORKLOAD_KERNELS[workload].items()]
+               if workload else CLOCK_KERNELS)
+    for key, args, wname, flop_clk in kernels:
         sel = {c: [(v, d) for k, v, d in r if args in k] for c, r in rows.items()}
         if not all(sel.values()):
             continue
@@ -211,7 +221,7 @@ def summarize_clock(pmc_csv):
         dur_ns = sum(d for _, d in sel["GRBM_GUI_ACTIVE"]) / len(sel["GRBM_GUI_ACTIVE"])
         cycles = mean["GRBM_GUI_ACTIVE"] / N_XCD
         sclk = cycles / dur_ns
-        wl = synth.WORKLOADS[workload]
+        wl = synth.WORKLOADS[wname]
         flops = 2.0 * wl.T * wl.N * wl.K
         frac = flops / (dur_ns * 1e-9) / (N_CU * flop_clk * sclk * 1e9)
         mfma = mean["SQ_VALU_MFMA_BUSY_CYCLES"] / (cycles * N_CU * 4)
@@ -580,12 +590,19 @@ def bench_mlp(torch, gl, steps, warmup):
                            "backward": round(T * 5 * F * 2 / (per["swiglu_backward"] * 1e-3) / 1e9, 1)}}
 
 
-def bench_workloads(torch, gl, synth, steps, warmup):
+def bench_workloads(torch, gl, synth, steps, warmup, names=None):
     """The skewed 64-group workload (forward, dgrad, wgrad added into an fp32
     main_grad) and the 256-group forward into a caller buffer with per-group weight
-    pointers, at full size.  Split sizes come from the seeded recipe; the values are
-    drawn on the device (torch.randn, bf16), since throughput does not depend on them
-    and the host recipe would spend most of the run making 7.5 GB of weights."""
+    pointers, at full size (or only the named ones).  Split sizes come from the seeded
+    recipe; the values are drawn on the device (torch.randn, bf16), since throughput
+    does not depend on them and the host recipe would spend most of the run making
+    7.5 GB of weights.  Each pass is reported against both rooflines, and with the
+    HBM traffic and engine clock of the committed counter runs while their kernel
+    source hash matches."""
+    for name in names or ():
+        if name not in WORKLOAD_KERNELS:
+            raise SystemExit(f"unknown workload {name}; one of {sorted(WORKLOAD_KERNELS)}")
+    run_wl = lambda name: names is None or name in names
     dev = torch.device("cuda")
     bf = torch.bfloat16
     g = torch.Generator(device=dev).manual_seed(7)
@@ -593,66 +610,102 @@ def bench_workloads(torch, gl, synth, steps, warmup):
     gbs = lambda nbytes, ms: round(nbytes / (ms * 1e-3) / 1e9, 1)
     tf = lambda fl, ms: round(fl / (ms * 1e-3) / 1e12, 2)
 
+    def pass_entry(wname, k, fl, nb, ms):
+        d = {"ms": round(ms, 4), "tflops": tf(fl, ms),
+             "pct_bf16_peak": round(100 * fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+             "gbs": gbs(nb, ms), "pct_hbm": round(100 * nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
+             "algorithmic_bytes": nb}
+        tr = traffic_for(k, wname)
+        if tr:
+            d["traffic_bytes"] = tr
+            d["traffic_over_algorithmic"] = round(tr / nb, 3)
+        ck = clock_for(k, wname)
+        if ck:
+            d["measured_sclk_ghz"] = ck["sclk_ghz"]
+            d["mfma_busy_frac"] = ck["mfma_busy_frac"]
+        return d
+
     wl = synth.WORKLOADS["bf16_zipf_g64_k2048_n1536"]
-    G, K, N, T = wl.G, wl.K, wl.N, wl.T
-    m = synth.split_sizes(wl)
-    x = torch.randn(T, K, generator=g, device=dev, dtype=bf)
-    dy = torch.randn(T, N, generator=g, device=dev, dtype=bf)
-    w = torch.randn(G, N, K, generator=g, device=dev, dtype=bf) * 0.02
-    mg = torch.randn(G, N, K, generator=g, device=dev)
-    y = torch.empty(T, N, dtype=bf, device=dev)
-    dx = torch.empty(T, K, dtype=bf, device=dev)
-    ws = gl.new_workspace(G, dev)
-    gl.gl_offsets(torch.from_numpy(m).to(dev), T, ws)
-    timer = EventTimer(torch)
-    for i in range(warmup + steps):
-        run = (lambda n, f: timer.run(n, f)) if i >= warmup else (lambda n, f: f())
-        run("forward", lambda: gl.gl_forward(x, w, y, ws))
-        run("dgrad", lambda: gl.gl_dgrad(dy, w, dx, ws))
-        run("wgrad_main_grad", lambda: gl.gl_wgrad(x, dy, mg, ws, accumulate=True))
-    torch.cuda.synchronize()
-    per = timer.mean_ms()
-    fl = 2.0 * T * N * K
-    gemm_bytes = (T * K + G * N * K + T * N) * 2
-    wgrad_bytes = (T * K + T * N) * 2 + 2 * G * N * K * 4
-    d = {"num_groups": G, "in_features": K, "out_features": N, "total_rows": T, "largest_group": int(m.max()),
-         "empty_groups": int((m == 0).sum())}
-    for k in ("forward", "dgrad", "wgrad_main_grad"):
-        nb = wgrad_bytes if k == "wgrad_main_grad" else gemm_bytes
-        d[k] = {"ms": round(per[k], 4), "tflops": tf(fl, per[k]), "pct_bf16_peak": round(100 * fl / (per[k] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
-                "gbs": gbs(nb, per[k]), "pct_hbm": round(100 * nb / (per[k] * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
-                "algorithmic_bytes": nb}
-    d["fwd_dgrad_wgrad_tflops"] = tf(3 * fl, sum(per[k] for k in ("forward", "dgrad", "wgrad_main_grad")))
-    out[wl.name] = d
-    del x, dy, w, mg, y, dx
+    if run_wl(wl.name):
+        G, K, N, T = wl.G, wl.K, wl.N, wl.T
+        m = synth.split_sizes(wl)
+        x = torch.randn(T, K, generator=g, device=dev, dtype=bf)
+        dy = torch.randn(T, N, generator=g, device=dev, dtype=bf)
+        w = torch.randn(G, N, K, generator=g, device=dev, dtype=bf) * 0.02
+        mg = torch.randn(G, N, K, generator=g, device=dev)
+        y = torch.empty(T, N, dtype=bf, device=dev)
+        dx = torch.empty(T, K, dtype=bf, device=dev)
+        ws = gl.new_workspace(G, dev)
+        gl.gl_offsets(torch.from_numpy(m).to(dev), T, ws)
+        timer = EventTimer(torch)
+        for i in range(warmup + steps):
+            run = (lambda n, f: timer.run(n, f)) if i >= warmup else (lambda n, f: f())
+            run("forward", lambda: gl.gl_forward(x, w, y, ws))
+            run("dgrad", lambda: gl.gl_dgrad(dy, w, dx, ws))
+            run("wgrad_main_grad", lambda: gl.gl_wgrad(x, dy, mg, ws, accumulate=True))
+        torch.cuda.synchronize()
+        per = timer.mean_ms()
+        fl = 2.0 * T * N * K
+        gemm_bytes = (T * K + G * N * K + T * N) * 2
+        wgrad_bytes = (T * K + T * N) * 2 + 2 * G * N * K * 4
+        d = {"num_groups": G, "in_features": K, "out_features": N, "total_rows": T, "largest_group": int(m.max()),
+             "empty_groups": int((m == 0).sum())}
+        for k in ("forward", "dgrad", "wgrad_main_grad"):
+            d[k] = pass_entry(wl.name, k, fl, wgrad_bytes if k == "wgrad_main_grad" else gemm_bytes, per[k])
+        d["fwd_dgrad_wgrad_tflops"] = tf(3 * fl, sum(per[k] for k in ("forward", "dgrad", "wgrad_main_grad")))
+        out[wl.name] = d
+        del x, dy, w, mg, y, dx
 
     wl = synth.WORKLOADS["bf16_fwd_g256_k7168_n2048_outbuf"]
-    G, K, N, T = wl.G, wl.K, wl.N, wl.T
-    m = synth.split_sizes(wl)
-    x = torch.randn(T, K, generator=g, device=dev, dtype=bf)
-    w = torch.randn(G, N, K, generator=g, device=dev, dtype=bf) * 0.02
-    w_list = list(w)  # per-group weight pointers
-    rows = 34000
-    y = torch.full((rows, N), float("nan"), dtype=bf, device=dev)
-    ws = gl.new_workspace(G, dev)
-    gl.gl_offsets(torch.from_numpy(m).to(dev), T, ws)
-    timer = EventTimer(torch)
-    for i in range(warmup + steps):
-        run = (lambda n, f: timer.run(n, f)) if i >= warmup else (lambda n, f: f())
-        run("forward", lambda: gl.gl_forward(x, w_list, y, ws))
-    torch.cuda.synchronize()
-    if not bool(torch.isnan(y[T:]).all()):
-        raise RuntimeError("the caller buffer's tail was written")
-    ms = timer.mean_ms()["forward"]
-    nb = (T * K + G * N * K + T * N) * 2
-    fl = 2.0 * T * N * K
-    out[wl.name] = {"num_groups": G, "in_features": K, "out_features": N, "total_rows": T, "output_rows": rows,
-                    "weights": "per-group pointers",
-                    "forward": {"ms": round(ms, 4), "tflops": tf(fl, ms),
-                                "pct_bf16_peak": round(100 * fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
-                                "gbs": gbs(nb, ms), "pct_hbm": round(100 * nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
-                                "algorithmic_bytes": nb}}
+    if run_wl(wl.name):
+        G, K, N, T = wl.G, wl.K, wl.N, wl.T
+        m = synth.split_sizes(wl)
+        x = torch.randn(T, K, generator=g, device=dev, dtype=bf)
+        w = torch.randn(G, N, K, generator=g, device=dev, dtype=bf) * 0.02
+        w_list = list(w)  # per-group weight pointers
+        rows = wl.out_rows
+        y = torch.full((rows, N), float("nan"), dtype=bf, device=dev)
+        ws = gl.new_workspace(G, dev)
+        gl.gl_offsets(torch.from_numpy(m).to(dev), T, ws)
+        timer = EventTimer(torch)
+        for i in range(warmup + steps):
+            run = (lambda n, f: timer.run(n, f)) if i >= warmup else (lambda n, f: f())
+            run("forward", lambda: gl.gl_forward(x, w_list, y, ws))
+        torch.cuda.synchronize()
+        if not bool(torch.isnan(y[T:]).all()):
+            raise RuntimeError("the caller buffer's tail was written")
+        ms = timer.mean_ms()["forward"]
+        nb = (T * K + G * N * K + T * N) * 2
+        fl = 2.0 * T * N * K
+        out[wl.name] = {"num_groups": G, "in_features": K, "out_features": N, "total_rows": T, "output_rows": rows,
+                        "weights": "per-group pointers", "forward": pass_entry(wl.name, "forward", fl, nb, ms)}
     return out
+
+
+def bench_small_fp32(torch, gl, synth, reps=200, warmup=20):
+    """Latency of the fp32 workload (4 groups, K=64, N=32, 32 rows, one empty group):
+    a forward is a launch of a few microseconds, not a throughput figure.  Timed per
+    call with HIP events on the launch stream: the forward alone (offsets already in
+    the workspace) and the offsets scan + forward; median, p10 and p90 in
+    microseconds."""
+    wl = synth.WORKLOADS["fwd_f32_g4_k64_n32"]
+    dev = torch.device("cuda")
+    m = synth.split_sizes(wl)
+    x, w, b = synth.x(wl).to(dev), synth.weight(wl).to(dev), synth.bias(wl).to(dev)
+    md = torch.from_numpy(m).to(dev)
+    y = torch.empty(wl.T, wl.N, device=dev)
+    ws = gl.new_workspace(wl.G, dev)
+    gl.gl_offsets(md, wl.T, ws)
+    timer = EventTimer(torch)
+    for i in range(warmup + reps):
+        run = (lambda n, f: timer.run(n, f)) if i >= warmup else (lambda n, f: f())
+        run("forward", lambda: gl.gl_forward(x, w, y, ws, bias=b))
+        run("offsets_forward", lambda: (gl.gl_offsets(md, wl.T, ws), gl.gl_forward(x, w, y, ws, bias=b)))
+    torch.cuda.synchronize()
+    sp = timer.spread_ms()
+    us = lambda d: {k: round(v * 1e3, 2) for k, v in d.items()}
+    return {"workload": wl.name, "m_splits": m.tolist(), "dtype": "f32", "unit": "us", "calls": reps,
+            "forward_us": us(sp["forward"]), "offsets_forward_us": us(sp["offsets_forward"])}
 
 
 def main():
@@ -664,6 +717,11 @@ def main():
     ap.add_argument("--no-mlp", action="store_true")
     ap.add_argument("--no-workloads", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workloads-only", nargs="*", metavar="WORKLOAD", default=None,
+                    help="only the 64-group and 256-group workloads, or the named ones (one JSON object; for "
+                         "profiling runs)")
+    ap.add_argument("--workload", default=None, help="with --summarize-pmc / --summarize-clock: the run was "
+                    "--workloads-only WORKLOAD")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB copy (counter calibration)")
     ap.add_argument("--summarize-clock", metavar="PMC_CSV",
@@ -672,10 +730,10 @@ def main():
                     help="fold rocprofv3 FETCH_SIZE/WRITE_SIZE CSVs into the traffic table, then exit")
     args = ap.parse_args()
     if args.summarize_pmc:
-        summarize_pmc(*args.summarize_pmc)
+        summarize_pmc(*args.summarize_pmc, workload=args.workload)
         return
     if args.summarize_clock:
-        summarize_clock(args.summarize_clock)
+        summarize_clock(args.summarize_clock, workload=args.workload)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -690,6 +748,10 @@ def main():
     import synth
 
     gl.load()
+    if args.workloads_only is not None:
+        print(json.dumps({"workloads": bench_workloads(torch, gl, synth, args.steps, args.warmup,
+                                                       args.workloads_only or None)}))
+        return
     wl, m, host_inputs, r = bench_bf16(torch, gl, synth, args.steps, args.warmup)
     out = {
         "metric": METRIC,
@@ -716,6 +778,7 @@ def main():
         "fwd_dgrad_wgrad_events": r["fwd_dgrad_wgrad"],
         "roofline": r["roofline"],
     }
+    out["small_fp32_latency"] = bench_small_fp32(torch, gl, synth)
     if not args.no_mxfp8:
         out["mxfp8"] = bench_mxfp8(torch, gl, synth, max(5, args.steps // 2), 2)
     if not args.no_mlp:
