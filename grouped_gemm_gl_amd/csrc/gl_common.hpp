@@ -12,9 +12,15 @@ namespace gl {
 //   [32]  int64 offsets[G+1]
 //   then  int32 row-tile prefix tables, one per row-tile height in kTileRows:
 //         pre[g] = sum_{h<g} ceil(m_h / rows), pre[G] = total row tiles.
+//   then  the contraction schedule of the wgrad GEMMs (written by their plan kernel
+//         before each launch): int32 cap, split items, pad[2]; int32 order[G] (groups
+//         by decreasing contraction length); int32 items[G+1] (prefix of work items
+//         over that order)
 //   then  (1 KiB aligned) the split-contraction area of the GEMMs: int32 arrival
 //         counters[kSplitSlots] (zeroed by the offsets kernel, left zero by every
-//         GEMM launch), then kSplitSlots fp32 partial tiles of kPartialBytes each.
+//         GEMM launch), fp32 bias-grad partials [kSplitSlots][256], then the fp32
+//         partial tiles of kPartialBytes each (kSplitSlots of them in a workspace of
+//         gl_workspace_size).
 struct WsHeader {
   int32_t status;       // GL_STATUS_* bits, 0 = valid splits
   int32_t num_groups;
@@ -43,13 +49,17 @@ __host__ __device__ inline size_t ws_prefix_byte(int G, int idx) {
 // kSplitSlots counters.
 constexpr int kSplitSlots = 256;
 constexpr size_t kPartialBytes = 256 * 256 * 4;
+__host__ __device__ constexpr size_t ws_plan_byte_c(int G) {
+  return 32 + 8 * (size_t)(G + 1) + (size_t)kNumTileRows * 4 * (size_t)(G + 1);
+}
 __host__ __device__ constexpr size_t ws_split_byte_c(int G) {
-  return (32 + 8 * (size_t)(G + 1) + (size_t)kNumTileRows * 4 * (size_t)(G + 1) + 1023) & ~(size_t)1023;
+  return (ws_plan_byte_c(G) + 16 + 4 * (size_t)G + 4 * (size_t)(G + 1) + 1023) & ~(size_t)1023;
 }
 __host__ __device__ inline size_t ws_split_byte(int G) { return ws_split_byte_c(G); }
 // bytes of a workspace over G groups with `slots` partial-tile slots
+constexpr size_t kDbPartBytes = 256 * 4;  // bias-grad partial of one split part
 __host__ __device__ constexpr size_t ws_bytes_slots(int G, int slots) {
-  return ws_split_byte_c(G) + 4 * kSplitSlots + (size_t)slots * kPartialBytes;
+  return ws_split_byte_c(G) + 4 * kSplitSlots + (size_t)kSplitSlots * kDbPartBytes + (size_t)slots * kPartialBytes;
 }
 __host__ __device__ inline size_t ws_bytes(int G) { return ws_bytes_slots(G, kSplitSlots); }
 
@@ -57,8 +67,12 @@ struct WsView {
   WsHeader *hdr;
   const int64_t *off;
   const int32_t *pre[kNumTileRows];
+  int32_t *plan;        // [cap, split items, pad, pad]
+  int32_t *order;       // [G]
+  int32_t *items;       // [G + 1]
   int32_t *split_cnt;   // [kSplitSlots]
-  float *split_part;    // [kSplitSlots][kPartialBytes / 4]
+  float *db_part;       // [kSplitSlots][256]
+  float *split_part;    // [slots][kPartialBytes / 4]
 };
 __host__ __device__ inline WsView ws_view(const void *ws, int G) {
   WsView v;
@@ -66,8 +80,12 @@ __host__ __device__ inline WsView ws_view(const void *ws, int G) {
   v.hdr = (WsHeader *)b;
   v.off = (const int64_t *)(b + ws_offsets_byte(G));
   for (int i = 0; i < kNumTileRows; ++i) v.pre[i] = (const int32_t *)(b + ws_prefix_byte(G, i));
+  v.plan = (int32_t *)(b + ws_plan_byte_c(G));
+  v.order = v.plan + 4;
+  v.items = v.order + G;
   v.split_cnt = (int32_t *)(b + ws_split_byte(G));
-  v.split_part = (float *)(b + ws_split_byte(G) + 4 * kSplitSlots);
+  v.db_part = (float *)(b + ws_split_byte(G) + 4 * kSplitSlots);
+  v.split_part = (float *)(b + ws_split_byte(G) + 4 * kSplitSlots + (size_t)kSplitSlots * kDbPartBytes);
   return v;
 }
 

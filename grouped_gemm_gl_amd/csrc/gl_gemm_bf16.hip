@@ -98,11 +98,10 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
     fence();
   };
 
-  // One work item: the whole contraction of a tile, or (SPLIT) part `part` of S of
-  // the u-th split tile.
-  auto item = [&](int tile, int part, int S, int u, auto split_tag) __attribute__((always_inline)) {
+  // One work item: the whole contraction of tile t, or (SPLIT) part `part` of S of
+  // the u-th split tile, whose partials go to slots slot0 .. slot0 + S - 1.
+  auto item = [&](const Tile &t, int part, int S, int u, int slot0, auto split_tag) __attribute__((always_inline)) {
     constexpr bool SPLIT = decltype(split_tag)::value;
-    const Tile t = decode_tile<A_KMAJ, B_KMAJ, MODE>(p, off, pre, tile);
     const bool bgrad = BGRAD && t.jt == 0;
     if (MODE == MODE_CONTR && p.accumulate && t.g_rows == 0) {  // main_grad untouched
       if (bgrad) store_bgrad_zero(p, t);
@@ -138,14 +137,20 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
           sb.issue_masked(s, pmax, st + kOpBytes, wave, lane);
         }
       };
+      // 16-row blocks of this wave that hold valid rows (a group's last row tile is
+      // often part padding): the others skip their fragment reads and MFMAs, which
+      // saves power as well as LDS bandwidth.  Wave-uniform.
+      const int vb = MODE == MODE_ROWS ? min(max((t.a_rv - wm * kWTM + 15) / 16, 0), kNI16) : kNI16;
       bf16x8_t fa[kNI16], fb[kNJ16];
       auto read_step = [&](int s, int ks) {
+        if (vb == 0) return;
         const char *ta = stage_ptr(s);
         const char *tb = ta + kOpBytes;
 #pragma unroll
         for (int ii = 0; ii < kNI16; ++ii)
-          fa[ii] = A_KMAJ ? frag16_kmaj(ta, wm * kWTM + ii * 16, ks, lane)
-                          : frag16_mnmaj(ta, wm * kWTM + ii * 16, ks, lane);
+          if (ii < vb)
+            fa[ii] = A_KMAJ ? frag16_kmaj(ta, wm * kWTM + ii * 16, ks, lane)
+                            : frag16_mnmaj(ta, wm * kWTM + ii * 16, ks, lane);
 #pragma unroll
         for (int jj = 0; jj < kNJ16; ++jj)
           fb[jj] = B_KMAJ ? frag16_kmaj(tb, wn * kWTN + jj * 16, ks, lane)
@@ -154,12 +159,14 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
       auto compute_step = [&]() {
 #pragma unroll
         for (int ii = 0; ii < kNI16; ++ii)
+          if (ii < vb) {
 #pragma unroll
-          for (int jj = 0; jj < kNJ16; ++jj)
-            acc[ii][jj] = F16 ? __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, fb[jj]),
-                                                                      __builtin_bit_cast(f16x8_t, fa[ii]),
-                                                                      acc[ii][jj], 0, 0, 0)
-                              : __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[jj], fa[ii], acc[ii][jj], 0, 0, 0);
+            for (int jj = 0; jj < kNJ16; ++jj)
+              acc[ii][jj] = F16 ? __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, fb[jj]),
+                                                                        __builtin_bit_cast(f16x8_t, fa[ii]),
+                                                                        acc[ii][jj], 0, 0, 0)
+                                : __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[jj], fa[ii], acc[ii][jj], 0, 0, 0);
+          }
       };
       static_assert(kBK == 64, "two 32-deep steps per stage");
       if (kend > kbeg) {
@@ -293,11 +300,21 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
     if (h == 0) barrier();
     __builtin_amdgcn_s_barrier();  // every wave is done with the ring before it is refilled
 
+    // the tile's bias-grad column sums (thread t < 256: column t)
+    float dbv = 0.f;
+    if (BGRAD && bgrad) dbv = db_reduce(dbr, (float *)(lds + kS * kStageBytes), wave, lane);
     if constexpr (SPLIT) {
+      // a part of a bias-grad tile leaves its column sums beside its partial tile
+      GL_GLOBAL float *dbp = (GL_GLOBAL float *)ws.db_part;
+      if (BGRAD && bgrad && threadIdx.x < 256) dbp[(slot0 + part) * 256 + threadIdx.x] = dbv;
       // the ring is idle after the loop's last barrier: its first word carries the flag
-      if (!split_finish(ws, u, part, S, acc, (int *)lds)) return;
+      if (!split_finish(ws, u, slot0, part, S, acc, (int *)lds)) return;
+      if (BGRAD && bgrad && threadIdx.x < 256) {
+        dbv = 0.f;
+        for (int s_ = 0; s_ < S; ++s_) dbv += dbp[(slot0 + s_) * 256 + threadIdx.x];
+      }
     }
-    if (BGRAD && bgrad) store_bgrad<F16>(p, t, dbr, (float *)(lds + kS * kStageBytes), wave, lane);
+    if (BGRAD && bgrad) store_bgrad<F16>(p, t, dbv);
     // wgrad tiles contract over one group's rows only, so their output stores weigh
     // more: there the tile goes out through LDS as whole lines (measured neutral to
     // slightly worse for forward and dgrad, which keep the direct stores)
@@ -307,15 +324,112 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
       store_tile<MODE, F16>(p, t, acc, wm, wn, lane);
   };
 
-  // whole tiles, round after round; in row mode the last round may be split
-  const int full = MODE == MODE_ROWS ? split_plan(total, grid, nk_rows, slots).full : total;
-  for (int w = first; w < full; w += grid) item(w, 0, 1, 0, std::false_type{});
   if constexpr (MODE == MODE_ROWS) {
-    const int tiles = pre[p.G] * p.tiles_j;
-    const SplitPlan sp = split_plan(tiles, grid, nk_rows, slots);
+    // whole tiles, round after round; the last round may be split
+    const SplitPlan sp = split_plan(total, grid, nk_rows, slots);
+    for (int w = first; w < sp.full; w += grid)
+      item(decode_tile<A_KMAJ, B_KMAJ, MODE>(p, off, pre, w), 0, 1, 0, 0, std::false_type{});
     // the parts of the last round: u = first, consecutive u are consecutive tiles
-    if (first < sp.rem * sp.S)
-      item(sp.full + first % sp.rem, first / sp.rem, sp.S, first % sp.rem, std::true_type{});
+    if (first < sp.rem * sp.S) {
+      const int u = first % sp.rem;
+      item(decode_tile<A_KMAJ, B_KMAJ, MODE>(p, off, pre, sp.full + u), first / sp.rem, sp.S, u, u * sp.S,
+           std::true_type{});
+    }
+  } else {
+    // the contraction schedule of the plan kernel: work items in order of decreasing
+    // contraction length, the tiles of the longest groups cut into parts of at most
+    // `cap` stages (parts first, part-major, so the tiles of one part run side by
+    // side and share their rows in L2); the grid walks the list in snake order
+    // (round r in reverse when r is odd), which evens out what each CU gets
+    const int ntiles = p.tiles_i * p.tiles_j;
+    const int cap = ws.plan[0];
+    const int nitems = ws.items[p.G];
+    const int32_t *__restrict__ stg = ws.pre[tile_rows_index(kBK)];
+    for (int base = 0; base < nitems; base += grid) {
+      const int w = base + (((base / grid) & 1) ? grid - 1 - first : first);
+      if (w >= nitems) continue;
+      const int pos = find_group(ws.items, p.G, w);
+      const int g = ws.order[pos];
+      const int sg = stg[g + 1] - stg[g];
+      const int pg = sg > cap ? (sg + cap - 1) / cap : 1;
+      const int local = w - ws.items[pos];
+      const int part = local / ntiles, tl = local - part * ntiles;
+      const Tile t = decode_tile<A_KMAJ, B_KMAJ, MODE>(p, off, pre, g * ntiles + tl);
+      if (pg > 1)
+        item(t, part, pg, pos * ntiles + tl, ws.items[pos] + tl * pg, std::true_type{});
+      else
+        item(t, 0, 1, 0, 0, std::false_type{});
+    }
+  }
+}
+
+// The contraction schedule of a wgrad launch (one workgroup, before the GEMM): the
+// groups in order of decreasing stage count s_g = ceil(m_g / kBK) (ties by index),
+// and a cap on the stages of one work item -- two thirds of the average stage count
+// per CU, raised until the split parts fit the partial slots -- above which a
+// group's tiles are cut into ceil(s_g / cap) parts; items[] is the prefix of work
+// items (tiles x parts) over that order.  Splitting is off (cap = INT_MAX) when
+// `split` is 0 or there are more than kPlanThreads groups (then the order is the
+// group order).
+constexpr int kPlanThreads = 1024;
+__global__ __launch_bounds__(kPlanThreads) void contr_plan_kernel(void *ws_, int G, int64_t T, int ntiles, int grid,
+                                                                  int split) {
+  const WsView ws = ws_view(ws_, G);
+  if (!ws_usable(ws.hdr, G, T)) return;
+  const int32_t *__restrict__ stg = ws.pre[tile_rows_index(kBK)];
+  const int tid = threadIdx.x;
+  if (G > kPlanThreads) {
+    for (int g = tid; g <= G; g += kPlanThreads) {
+      if (g < G) ws.order[g] = g;
+      ws.items[g] = g * ntiles;
+    }
+    if (tid == 0) {
+      ws.plan[0] = INT32_MAX;
+      ws.plan[1] = 0;
+    }
+    return;
+  }
+  __shared__ int32_t sz[kPlanThreads], cnt[kPlanThreads];
+  __shared__ int32_t s_cap;
+  const int sg = tid < G ? stg[tid + 1] - stg[tid] : -1;
+  sz[tid] = sg;
+  __syncthreads();
+  if (tid == 0) {
+    const int slots = min(max(ws.hdr->split_slots, 0), kSplitSlots);
+    const int64_t avg = ((int64_t)stg[G] * ntiles + grid - 1) / grid;
+    int cap = INT32_MAX;
+    if (split) {
+      cap = (int)max((int64_t)kMinSplitStages, (2 * avg + 2) / 3);
+      for (;;) {  // parts of the split tiles must fit the partial slots
+        int64_t need = 0;
+        for (int g = 0; g < G; ++g)
+          if (sz[g] > cap) need += (int64_t)ntiles * ((sz[g] + cap - 1) / cap);
+        if (need <= slots || cap >= (1 << 28)) break;
+        cap += cap / 4 + 1;
+      }
+      if (cap >= (1 << 28)) cap = INT32_MAX;
+    }
+    s_cap = cap;
+  }
+  __syncthreads();
+  const int cap = s_cap;
+  if (tid < G) {
+    int r = 0;
+    for (int h = 0; h < G; ++h) r += (sz[h] > sg) || (sz[h] == sg && h < tid);
+    ws.order[r] = tid;
+    cnt[r] = ntiles * (sg > cap ? (sg + cap - 1) / cap : 1);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int acc = 0, nsplit = 0;
+    for (int r = 0; r < G; ++r) {
+      ws.items[r] = acc;
+      if (sz[ws.order[r]] > cap) nsplit = acc + cnt[r];
+      acc += cnt[r];
+    }
+    ws.items[G] = acc;
+    ws.plan[0] = cap;
+    ws.plan[1] = nsplit;
   }
 }
 
@@ -384,6 +498,10 @@ hipError_t launch_wgrad_bf16(int G, int64_t K, int64_t N, int64_t T, const uint1
   const int64_t max_items = (int64_t)G * p.tiles_i * p.tiles_j;
   const dim3 grid(persistent_grid(max_items)), block(kThreads);
   const bool bg = db || db_ptrs;
+  // the same plan with or without a bias grad, so gl_wgrad and gl_wgrad_bgrad give
+  // the same dW bit for bit
+  hipLaunchKernelGGL(contr_plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, const_cast<void *>(ws), G, T,
+                     p.tiles_i * p.tiles_j, (int)grid.x, 1);
   if (f16 && bg)
     hipLaunchKernelGGL((gemm_bf16_kernel<false, false, MODE_CONTR, true, SCHED_STAGED, true>), grid, block, 0, s, p);
   else if (f16)

@@ -466,20 +466,28 @@ __device__ __forceinline__ uintptr_t db_row(const Params &p, int g) {
   return p.db ? (uintptr_t)p.db + (uintptr_t)((int64_t)g * p.rows_i * (p.db_f32 ? 4 : 2)) : (uintptr_t)p.db_ptrs[g];
 }
 
-// Adds the kDbParts partials of each column in a fixed order and stores db[g][n
-// tile]; whole workgroup; `dbl` is an idle LDS area of kDbLdsBytes.
-template <bool F16>
-__device__ __forceinline__ void store_bgrad(const Params &p, const Tile &t, const float (&dbr)[8], float *dbl,
-                                            int wave, int lane) {
+// The bias-grad column sums of the whole workgroup: every lane's 8 sums go to LDS,
+// and thread t < 256 returns column t's total over the kDbParts partials, added in a
+// fixed order.  Whole workgroup; `dbl` is an idle LDS area of kDbLdsBytes.
+__device__ __forceinline__ float db_reduce(const float (&dbr)[8], float *dbl, int wave, int lane) {
   float *part = dbl + (2 * wave + (lane >> 5)) * 256 + db_col(wave, lane);
   *(float4 *)part = make_float4(dbr[0], dbr[1], dbr[2], dbr[3]);
   *(float4 *)(part + 4) = make_float4(dbr[4], dbr[5], dbr[6], dbr[7]);
   __syncthreads();
+  float v = 0.f;
+  if (threadIdx.x < 256) {
+#pragma unroll
+    for (int k = 0; k < kDbParts; ++k) v += dbl[k * 256 + threadIdx.x];
+  }
+  __syncthreads();  // the partials area is free for the next tile
+  return v;
+}
+
+// Stores column t = threadIdx.x of db[g][n tile] (v from db_reduce).
+template <bool F16>
+__device__ __forceinline__ void store_bgrad(const Params &p, const Tile &t, float v) {
   const int col = threadIdx.x;
   if (col < t.a_rv) {
-    float v = 0.f;
-#pragma unroll
-    for (int k = 0; k < kDbParts; ++k) v += dbl[k * 256 + col];
     const uintptr_t row = db_row(p, t.g);
     const int64_t n = (int64_t)t.it * kBM + col;
     if (p.db_f32)
@@ -487,7 +495,6 @@ __device__ __forceinline__ void store_bgrad(const Params &p, const Tile &t, cons
     else
       ((GL_GLOBAL uint16_t *)row)[n] = f32_to_h16<F16>(v);
   }
-  __syncthreads();  // the partials area is free for the next tile
 }
 
 // An empty group whose wgrad is skipped (accumulate mode) still has db = 0.
@@ -538,18 +545,19 @@ __device__ __forceinline__ SplitPlan split_plan(int tiles, int grid, int nk, int
   return sp;
 }
 
-// Part `part` of S of the u-th split tile is done: publish its partial; true when
-// this workgroup arrived last and acc now holds the sum of all parts.  Called by
-// the whole workgroup, as its last work item; `flag` is a workgroup-shared int.
+// Part `part` of S of the u-th split tile is done: publish its partial (into slot
+// slot0 + part); true when this workgroup arrived last and acc now holds the sum
+// of all parts.  Called by the whole workgroup; `flag` is a workgroup-shared int.
 // (The flag lives inside the kernel's one LDS array: a second __shared__ object
 // makes the compiler wait for every direct-to-LDS load before each LDS read.)  The parts of the last
 // round are items u + rem * part, so a part's CUs on one XCD run neighbouring tiles.
 template <class ACC>
-__device__ __forceinline__ bool split_finish(const WsView &ws, int u, int part, int S, ACC &acc, int *flag) {
+__device__ __forceinline__ bool split_finish(const WsView &ws, int u, int slot0, int part, int S, ACC &acc,
+                                             int *flag) {
   using L = AccLayout<ACC>;
   const int tid = threadIdx.x;
   constexpr size_t kSlotF4 = kPartialBytes / 16;
-  GL_GLOBAL float4 *slots = (GL_GLOBAL float4 *)ws.split_part + (size_t)u * S * kSlotF4;
+  GL_GLOBAL float4 *slots = (GL_GLOBAL float4 *)ws.split_part + (size_t)slot0 * kSlotF4;
   GL_GLOBAL float4 *mine = slots + (size_t)part * kSlotF4;
 #pragma unroll
   for (int q = 0; q < kQuads; ++q) mine[q * kThreads + tid] = L::get(acc, q);
