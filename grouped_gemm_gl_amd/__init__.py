@@ -37,7 +37,8 @@ NOALLOC_MAX_GROUPS = 16384  # GL_NOALLOC_MAX_GROUPS
 GL_STATUS_NEGATIVE_SPLIT, GL_STATUS_SUM_MISMATCH, GL_STATUS_WORKSPACE = 1, 2, 4
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-library_path = os.path.join(_HERE, "libgrouped_linear.so")
+# GL_LIBRARY_PATH selects another build of the same library (e.g. the host-sanitized one)
+library_path = os.environ.get("GL_LIBRARY_PATH") or os.path.join(_HERE, "libgrouped_linear.so")
 _lib = None
 
 Tensor = torch.Tensor

@@ -3,6 +3,13 @@
 Usage: ``python -m grouped_gemm_gl_amd.build`` (or ``build()`` from Python).  Each
 ``csrc/*.hip`` file is compiled to an object in ``_build/`` in parallel and the
 objects are linked into ``grouped_gemm_gl_amd/libgrouped_linear.so``.
+
+``python -m grouped_gemm_gl_amd.build --host-sanitize`` (``build(host_sanitize=True)``)
+builds a second copy, ``_build/hostsan/libgrouped_linear_hostsan.so``, whose host code
+carries AddressSanitizer and UndefinedBehaviorSanitizer (device code is built as
+usual, without them).  It is for CPU runs of the argument validation and the
+deferred-wgrad queue: load it with the clang ASan runtime preloaded
+(``asan_runtime()``) and ``GL_LIBRARY_PATH`` pointing at it.
 """
 from __future__ import annotations
 
@@ -17,6 +24,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libgrouped_linear.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
+SAN_DIR = os.path.join(BUILD_DIR, "hostsan")
+SAN_OUT = os.path.join(SAN_DIR, "libgrouped_linear_hostsan.so")
 ARCH = "gfx950"
 
 HIP_FLAGS = [
@@ -30,6 +39,19 @@ HIP_FLAGS = [
     # packed fp32 VALU forms are kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
+]
+
+# host-only sanitizers: each -fsanitize= is bound to the host pass by -Xarch_host
+SAN_COMPILE = [
+    "-Xarch_host", "-fsanitize=address",
+    "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-omit-frame-pointer",
+    "-g",
+]
+SAN_LINK = [
+    "-Xarch_host", "-fsanitize=address",
+    "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-shared-libasan",
 ]
 
 
@@ -49,28 +71,42 @@ def _run(cmd):
     return text
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def asan_runtime() -> str:
+    """Path of the clang ASan runtime that a host-sanitized library needs preloaded."""
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    clang = os.path.join(rocm, "llvm", "bin", "clang")
+    return subprocess.run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"], stdout=subprocess.PIPE,
+                          text=True, check=True).stdout.strip()
+
+
+def build(verbose: bool = False, host_sanitize: bool = False) -> str:
+    out_dir = SAN_DIR if host_sanitize else BUILD_DIR
+    out = SAN_OUT if host_sanitize else OUT
+    os.makedirs(out_dir, exist_ok=True)
     hipcc = _hipcc()
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    objs = [os.path.join(BUILD_DIR, os.path.basename(s) + ".o") for s in srcs]
+    objs = [os.path.join(out_dir, os.path.basename(s) + ".o") for s in srcs]
+    flags = HIP_FLAGS
+    if host_sanitize:
+        flags = [f for f in HIP_FLAGS if f != "-O3"] + ["-O1"] + SAN_COMPILE
 
     def compile_one(pair):
         src, obj = pair
-        return _run([hipcc, *HIP_FLAGS, "-c", src, "-o", obj])
+        return _run([hipcc, *flags, "-c", src, "-o", obj])
 
     workers = max(1, min(len(srcs), os.cpu_count() or 1, 16))
     with concurrent.futures.ThreadPoolExecutor(workers) as ex:
         logs = list(ex.map(compile_one, zip(srcs, objs)))
-    tmp = OUT + ".tmp"
-    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
-    os.replace(tmp, OUT)
+    tmp = out + ".tmp"
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *(SAN_LINK if host_sanitize else []), "-o", tmp,
+          *objs])
+    os.replace(tmp, out)
     if verbose:
         for l in logs:
             if l.strip():
                 print(l)
-    return OUT
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, host_sanitize="--host-sanitize" in sys.argv))

@@ -54,8 +54,17 @@ extern "C" {
 #endif
 
 /* Element types.  GL_F16 goes wherever GL_BF16 does except the MXFP8 quantizers
- * (whose source is bf16, as on the pages). */
-typedef enum gl_dtype { GL_F32 = 0, GL_BF16 = 1, GL_F16 = 2, GL_E4M3 = 3 } gl_dtype;
+ * (whose source is bf16, as on the pages).  The enum is int-sized, and any int a
+ * caller passes is a value of it (GL_DTYPE_INT_RANGE_ widens its range to all of
+ * int), so an unknown code is rejected with GL_ERR_DTYPE rather than being
+ * undefined behaviour in C++. */
+typedef enum gl_dtype {
+  GL_F32 = 0,
+  GL_BF16 = 1,
+  GL_F16 = 2,
+  GL_E4M3 = 3,
+  GL_DTYPE_INT_RANGE_ = 0x7fffffff
+} gl_dtype;
 
 enum {
   GL_OK = 0,
