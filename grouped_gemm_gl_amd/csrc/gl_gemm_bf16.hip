@@ -321,7 +321,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
     if (MODE != MODE_ROWS && !p.out_f32 && !p.accumulate)
       store_tile_lds<MODE, F16>(p, t, acc, wm, wn, lane, lds);
     else
-      store_tile<MODE, F16>(p, t, acc, wm, wn, lane);
+      store_tile<MODE, F16, A_KMAJ && B_KMAJ>(p, t, acc, wm, wn, lane);  // the forward takes a bias
   };
 
   if constexpr (MODE == MODE_ROWS) {
@@ -362,6 +362,17 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
     }
   }
 }
+
+// Every launched variant, instantiated explicitly: with only the launch sites to go
+// by, the host pass has left a variant's launch stub undefined.
+template __global__ void gemm_bf16_kernel<true, true, MODE_ROWS, false, SCHED_DIRECT>(Params);
+template __global__ void gemm_bf16_kernel<true, true, MODE_ROWS, true, SCHED_DIRECT>(Params);
+template __global__ void gemm_bf16_kernel<true, false, MODE_ROWS, false, SCHED_STAGED>(Params);
+template __global__ void gemm_bf16_kernel<true, false, MODE_ROWS, true, SCHED_STAGED>(Params);
+template __global__ void gemm_bf16_kernel<false, false, MODE_CONTR, false, SCHED_STAGED>(Params);
+template __global__ void gemm_bf16_kernel<false, false, MODE_CONTR, true, SCHED_STAGED>(Params);
+template __global__ void gemm_bf16_kernel<false, false, MODE_CONTR, false, SCHED_STAGED, true>(Params);
+template __global__ void gemm_bf16_kernel<false, false, MODE_CONTR, true, SCHED_STAGED, true>(Params);
 
 // The contraction schedule of a wgrad launch (one workgroup, before the GEMM): the
 // groups in order of decreasing stage count s_g = ceil(m_g / kBK) (ties by index),

@@ -274,6 +274,8 @@ template <class ACC>
 struct AccLayout;
 template <>
 struct AccLayout<Acc32> {
+  // a lane's column in quad q depends only on q % kColGroups
+  static constexpr int kColGroups = 8;
   __device__ static __forceinline__ void pos(int q, int lane, int &il, int &jl) {
     il = (q >> 3) * 32 + (lane & 31);
     jl = ((q >> 2) & 1) * 32 + (q & 3) * 8 + (lane >> 5) * 4;
@@ -299,6 +301,7 @@ struct AccLayout<Acc32> {
 };
 template <>
 struct AccLayout<Acc16> {
+  static constexpr int kColGroups = 4;
   __device__ static __forceinline__ void pos(int q, int lane, int &il, int &jl) {
     il = (q >> 2) * 16 + (lane & 15);
     jl = (q & 3) * 16 + (lane >> 4) * 4;
@@ -318,25 +321,14 @@ struct AccLayout<Acc16> {
   }
 };
 
-// Stores 4 consecutive output columns of one row: optional bias (per output
-// column, of the output's type), optional accumulate into the existing values.
-// 16-bit outputs are bf16, or fp16 when F16.
+// Stores 4 consecutive output columns of one row, optionally adding the existing
+// values (accumulate).  16-bit outputs are bf16, or fp16 when F16.
 // Addresses arrive as integers: a cast of a generic pointer to the global address
 // space can be folded back to a flat access when the pointer is a select of a
 // kernel argument and a loaded one; an integer cannot.
 template <bool F16>
-__device__ __forceinline__ void store4(uintptr_t cbase, int64_t row, int64_t ldc, int64_t col, uintptr_t bias_g,
-                                      int out_f32, int accumulate, float v0, float v1, float v2, float v3) {
-  if (bias_g) {
-    if (out_f32) {
-      const float4 bv = *(const GL_GLOBAL float4 *)(bias_g + col * 4);
-      v0 += bv.x; v1 += bv.y; v2 += bv.z; v3 += bv.w;
-    } else {
-      const uint2 bv = *(const GL_GLOBAL uint2 *)(bias_g + col * 2);
-      v0 += h16_to_f32<F16>(bv.x & 0xffff); v1 += h16_to_f32<F16>(bv.x >> 16);
-      v2 += h16_to_f32<F16>(bv.y & 0xffff); v3 += h16_to_f32<F16>(bv.y >> 16);
-    }
-  }
+__device__ __forceinline__ void store4(uintptr_t cbase, int64_t row, int64_t ldc, int64_t col, int out_f32,
+                                      int accumulate, float v0, float v1, float v2, float v3) {
   if (out_f32) {
     GL_GLOBAL float4 *dst = (GL_GLOBAL float4 *)(cbase + (row * ldc + col) * 4);
     if (accumulate) {
@@ -590,8 +582,13 @@ __device__ __forceinline__ bool split_finish(const WsView &ws, int u, int slot0,
 }
 
 // Stores a wave's 128 x 64 block of a tile, quad by quad (see AccLayout); only rows
-// < a_rv and columns < b_rv are written.
-template <int MODE, bool F16 = false, class ACC>
+// < a_rv and columns < b_rv are written.  The optional bias (per output column, of
+// the output's type) is added to the fp32 sum first; a lane's column depends only
+// on q % kColGroups, so its bias values are loaded once per distinct column, ahead
+// of the stores (loaded beside each store, every quad waited for its load: the
+// compiler cannot move a load above a store that may alias it).  BIAS: the kernel
+// takes a bias at all (the forward); the others carry no bias code or registers.
+template <int MODE, bool F16, bool BIAS, class ACC>
 __device__ __forceinline__ void store_tile(const Params &p, const Tile &t, const ACC &acc, int wm, int wn, int lane) {
   using L = AccLayout<ACC>;
   char *cbase;
@@ -604,8 +601,25 @@ __device__ __forceinline__ void store_tile(const Params &p, const Tile &t, const
     row0 = (int64_t)t.it * kBM;
   }
   const char *bias_g = nullptr;
-  if (p.bias) bias_g = (const char *)p.bias + (int64_t)t.g * p.cols_j * (p.out_f32 ? 4 : 2);
-  else if (p.bias_ptrs) bias_g = (const char *)p.bias_ptrs[t.g];
+  if (BIAS && p.bias) bias_g = (const char *)p.bias + (int64_t)t.g * p.cols_j * (p.out_f32 ? 4 : 2);
+  else if (BIAS && p.bias_ptrs) bias_g = (const char *)p.bias_ptrs[t.g];
+  float4 bv[L::kColGroups];
+#pragma unroll
+  for (int c = 0; c < L::kColGroups; ++c) {
+    int il, jl;
+    L::pos(c, lane, il, jl);
+    const int64_t col = (int64_t)t.jt * kBN + jl + wn * kWTN;
+    bv[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (BIAS && bias_g && jl + wn * kWTN < t.b_rv) {
+      if (p.out_f32) {
+        bv[c] = *(const GL_GLOBAL float4 *)((uintptr_t)bias_g + col * 4);
+      } else {
+        const uint2 u = *(const GL_GLOBAL uint2 *)((uintptr_t)bias_g + col * 2);
+        bv[c] = make_float4(h16_to_f32<F16>(u.x & 0xffff), h16_to_f32<F16>(u.x >> 16),
+                            h16_to_f32<F16>(u.y & 0xffff), h16_to_f32<F16>(u.y >> 16));
+      }
+    }
+  }
 #pragma unroll
   for (int q = 0; q < kQuads; ++q) {
     int il, jl;
@@ -613,9 +627,13 @@ __device__ __forceinline__ void store_tile(const Params &p, const Tile &t, const
     il += wm * kWTM;
     jl += wn * kWTN;
     if (il >= t.a_rv || jl >= t.b_rv) continue;
-    const float4 v = L::get(acc, q);
-    store4<F16>((uintptr_t)cbase, row0 + il, p.ldc, (int64_t)t.jt * kBN + jl, (uintptr_t)bias_g, p.out_f32,
-                p.accumulate, v.x, v.y, v.z, v.w);
+    float4 v = L::get(acc, q);
+    if (BIAS && bias_g) {
+      const float4 c = bv[q % L::kColGroups];
+      v.x += c.x; v.y += c.y; v.z += c.z; v.w += c.w;
+    }
+    store4<F16>((uintptr_t)cbase, row0 + il, p.ldc, (int64_t)t.jt * kBN + jl, p.out_f32, p.accumulate, v.x, v.y,
+                v.z, v.w);
   }
 }
 
