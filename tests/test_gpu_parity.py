@@ -55,6 +55,9 @@ SHAPES = [
     (3, 256, 512, [256, 257, 255]),
     (1, 64, 8, [37]),
     (8, 136, 72, [3, 0, 0, 70, 260, 1, 0, 90]),
+    # several full 256-row tiles in a group, then a ragged one
+    (2, 200, 264, [700, 301]),
+    (3, 136, 72, [600, 0, 517]),
 ]
 
 
