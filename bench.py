@@ -119,8 +119,8 @@ def _mx_traffic_kernels():
     return [(f"{wl.name}:offsets_quantize_x", "offsets_quantize_mxfp8_kernel", T * K * 2 + codes(T, K) + 8 * G),
             (f"{wl.name}:offsets_quantize_x_both", "quantize_mxfp8_colwise_tile_kernel<true>",
              T * K * 2 + codes(T, K) + codes(K, ld) + 8 * G),
-            (f"{wl.name}:mx_forward_and_dgrad", "gemm_mxfp8_kernel<0>", codes(T, K) + codes(G * N, K) + T * N * 2),
-            (f"{wl.name}:mx_wgrad", "gemm_mxfp8_kernel<2>", codes(N, ld) + codes(K, ld) + G * N * K * 2)]
+            (f"{wl.name}:mx_forward_and_dgrad", "gemm_mxfp8_kernel<0,", codes(T, K) + codes(G * N, K) + T * N * 2),
+            (f"{wl.name}:mx_wgrad", "gemm_mxfp8_kernel<2,", codes(N, ld) + codes(K, ld) + G * N * K * 2)]
 
 
 def summarize_pmc(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, workload=None):
@@ -192,9 +192,9 @@ N_XCD, N_CU, BF16_FLOP_PER_CLK_CU, FP8_FLOP_PER_CLK_CU = 8, 256, 4096, 8192
 # the clock run covers; the MXFP8 forward and dgrad share one kernel and one shape
 CLOCK_KERNELS = [(f"bf16_train_g8_k4096_n14336:{k}", v, "bf16_train_g8_k4096_n14336", BF16_FLOP_PER_CLK_CU)
                  for k, v in PASS_KERNELS.items()] + [
-    ("mxfp8_fwd_g32_k4096_n4096:mx_forward_and_dgrad", "gemm_mxfp8_kernel<0>", "mxfp8_fwd_g32_k4096_n4096",
+    ("mxfp8_fwd_g32_k4096_n4096:mx_forward_and_dgrad", "gemm_mxfp8_kernel<0,", "mxfp8_fwd_g32_k4096_n4096",
      FP8_FLOP_PER_CLK_CU),
-    ("mxfp8_fwd_g32_k4096_n4096:mx_wgrad", "gemm_mxfp8_kernel<2>", "mxfp8_fwd_g32_k4096_n4096", FP8_FLOP_PER_CLK_CU)]
+    ("mxfp8_fwd_g32_k4096_n4096:mx_wgrad", "gemm_mxfp8_kernel<2,", "mxfp8_fwd_g32_k4096_n4096", FP8_FLOP_PER_CLK_CU)]
 
 
 def summarize_clock(pmc_csv, workload=None):
