@@ -124,7 +124,9 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
     ACC acc;
     L::zero(acc);
     const int h = wm;  // ping-pong group
-    float dbr[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};  // bias-grad column sums (STAGED)
+    // this lane's bias-grad column sums (STAGED), in LDS beside the ring
+    float *dbs = db_slot((float *)(lds + kS * kStageBytes), wave, lane);
+    if (BGRAD && bgrad) db_zero(dbs);
 
     if constexpr (SCHED == SCHED_DIRECT) {
       auto issue = [&](int s) {
@@ -251,7 +253,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
       if (kend > kbeg) {
         load_stage(kbeg, kbeg < nfull);
         wait_vm0();
-        if (BGRAD && bgrad) db_add<F16>(dbr, ra);
+        if (BGRAD && bgrad) db_add<F16>(dbs, ra);
         write_stage(kbeg);
         if (kbeg + 1 < kend) load_stage(kbeg + 1, kbeg + 1 < nfull);
         wait_lgkm0();
@@ -271,7 +273,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
         fence();
         if (steady || kt + 1 < kend) {
           wait_vm0();
-          if (BGRAD && bgrad) db_add<F16>(dbr, ra);  // dy rows of stage kt + 1
+          if (BGRAD && bgrad) db_add<F16>(dbs, ra);  // dy rows of stage kt + 1
           write_stage(kt + 1);
         }
         fence();
@@ -302,7 +304,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
 
     // the tile's bias-grad column sums (thread t < 256: column t)
     float dbv = 0.f;
-    if (BGRAD && bgrad) dbv = db_reduce(dbr, (float *)(lds + kS * kStageBytes), wave, lane);
+    if (BGRAD && bgrad) dbv = db_reduce((const float *)(lds + kS * kStageBytes));
     if constexpr (SPLIT) {
       // a part of a bias-grad tile leaves its column sums beside its partial tile
       GL_GLOBAL float *dbp = (GL_GLOBAL float *)ws.db_part;

@@ -429,9 +429,12 @@ __device__ __forceinline__ Tile decode_tile(const Params &p, const int64_t *__re
 // c = (lane % 32) ^ swz_m(p).  The swizzle of p does not depend on q, so a lane's
 // pieces of every stage cover the same 8 columns: the tiles of the first k column
 // add each stage's pieces, as they come in, into 8 fp32 column sums per lane (rows
-// past the group's end are zero pieces and add nothing).  At the end the 16 partial
-// sums of each column (8 waves x 2 lane halves) meet in LDS in a fixed order.
-// db_g = sum over the group's rows of dy, read once for both outputs.
+// past the group's end are zero pieces and add nothing).  The sums live in the
+// lane's own 32-byte slot of an LDS area beside the stage ring, not in registers:
+// 8 registers held across the contraction loop made the compiler spill inside it.
+// At the end the 16 partial sums of each column (8 waves x 2 lane halves) are added
+// in a fixed order.  db_g = sum over the group's rows of dy, read once for both
+// outputs.
 constexpr int kDbParts = 2 * kWaves;
 constexpr int kDbLdsBytes = kDbParts * 256 * 4;
 static_assert(kThreads == 512 && kBK == 64 && kQ == 4, "bias-grad lane mapping");
@@ -441,8 +444,22 @@ __device__ __forceinline__ int db_col(int wave, int lane) {
   return ((lane & 31) ^ swz_m(2 * wave + (lane >> 5))) * 8;
 }
 
+// This lane's slot of the bias-grad area `dbl` (kDbLdsBytes): part 2 wave + lane / 32,
+// columns db_col .. + 7.
+__device__ __forceinline__ float *db_slot(float *dbl, int wave, int lane) {
+  return dbl + (2 * wave + (lane >> 5)) * 256 + db_col(wave, lane);
+}
+
+__device__ __forceinline__ void db_zero(float *slot) {
+  *(float4 *)slot = make_float4(0.f, 0.f, 0.f, 0.f);
+  *(float4 *)(slot + 4) = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+// Adds the rows of this lane's staged pieces into its 8 column sums.
 template <bool F16>
-__device__ __forceinline__ void db_add(float (&dbr)[8], const uint4 (&r)[kQ]) {
+__device__ __forceinline__ void db_add(float *slot, const uint4 (&r)[kQ]) {
+  const float4 lo = *(const float4 *)slot, hi = *(const float4 *)(slot + 4);
+  float dbr[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
 #pragma unroll
   for (int q = 0; q < kQ; ++q) {
     const uint32_t d[4] = {r[q].x, r[q].y, r[q].z, r[q].w};
@@ -452,19 +469,18 @@ __device__ __forceinline__ void db_add(float (&dbr)[8], const uint4 (&r)[kQ]) {
       dbr[2 * e + 1] += h16_to_f32<F16>((uint16_t)(d[e] >> 16));
     }
   }
+  *(float4 *)slot = make_float4(dbr[0], dbr[1], dbr[2], dbr[3]);
+  *(float4 *)(slot + 4) = make_float4(dbr[4], dbr[5], dbr[6], dbr[7]);
 }
 
 __device__ __forceinline__ uintptr_t db_row(const Params &p, int g) {
   return p.db ? (uintptr_t)p.db + (uintptr_t)((int64_t)g * p.rows_i * (p.db_f32 ? 4 : 2)) : (uintptr_t)p.db_ptrs[g];
 }
 
-// The bias-grad column sums of the whole workgroup: every lane's 8 sums go to LDS,
-// and thread t < 256 returns column t's total over the kDbParts partials, added in a
-// fixed order.  Whole workgroup; `dbl` is an idle LDS area of kDbLdsBytes.
-__device__ __forceinline__ float db_reduce(const float (&dbr)[8], float *dbl, int wave, int lane) {
-  float *part = dbl + (2 * wave + (lane >> 5)) * 256 + db_col(wave, lane);
-  *(float4 *)part = make_float4(dbr[0], dbr[1], dbr[2], dbr[3]);
-  *(float4 *)(part + 4) = make_float4(dbr[4], dbr[5], dbr[6], dbr[7]);
+// The bias-grad column sums of the whole workgroup: thread t < 256 returns column
+// t's total over the kDbParts partials in `dbl`, added in a fixed order.  Whole
+// workgroup.
+__device__ __forceinline__ float db_reduce(const float *dbl) {
   __syncthreads();
   float v = 0.f;
   if (threadIdx.x < 256) {
