@@ -165,15 +165,18 @@ struct Stream {
       r[q] = make_uint4(v[0], v[1], v[2], v[3]);
     }
   }
-  // The last stage of a contraction: pieces past pmax are zeros.
+  // The last stage of a contraction: pieces past pmax are zeros.  (The count of
+  // valid contraction indices left is wave-uniform and at most kBK, so the per-lane
+  // test is a 32-bit compare.)
   __device__ __forceinline__ void load_regs_masked(int t, int64_t pmax, uint4 (&r)[kQ], int wave, int lane) const {
     const __amdgpu_buffer_rsrc_t rs = rsrc_at(base + (int64_t)t * step);
+    const int left = (int)min64(pmax - (int64_t)t * kBK, kBK);
 #pragma unroll
     for (int q = 0; q < kQ; ++q) {
       const int u = wave + kWaves * q;
       const int pfirst =
           KMAJ ? ((lane % kChunks) ^ swz_k(kRowsPerPiece * u + lane / kChunks)) * 8 : 2 * u + (lane >> 5);
-      if ((int64_t)t * kBK + pfirst < pmax) {
+      if (pfirst < left) {
         const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, off[q], 0, 0);
         r[q] = make_uint4(v[0], v[1], v[2], v[3]);
       } else {
@@ -190,6 +193,7 @@ struct Stream {
   // into their LDS slot instead of loading.
   __device__ __forceinline__ void issue_masked(int t, int64_t pmax, char *st, int wave, int lane) const {
     const __amdgpu_buffer_rsrc_t r = rsrc_at(base + (int64_t)t * step);
+    const int left = (int)min64(pmax - (int64_t)t * kBK, kBK);
 #pragma unroll
     for (int q = 0; q < kQ; ++q) {
       const int u = wave + kWaves * q;
@@ -197,7 +201,7 @@ struct Stream {
       // first contraction index (within the stage) this lane's piece holds
       const int pfirst =
           KMAJ ? ((lane % kChunks) ^ swz_k(kRowsPerPiece * u + lane / kChunks)) * 8 : 2 * u + (lane >> 5);
-      if ((int64_t)t * kBK + pfirst < pmax)
+      if (pfirst < left)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (GL_LDS void *)dst, 16, off[q], 0, 0, 0);
       else
         *(uint4 *)(dst + lane * 16) = make_uint4(0, 0, 0, 0);
@@ -346,16 +350,6 @@ __device__ __forceinline__ void store4(uintptr_t cbase, int64_t row, int64_t ldc
     *dst = make_uint2((uint32_t)f32_to_h16<F16>(v0) | ((uint32_t)f32_to_h16<F16>(v1) << 16),
                       (uint32_t)f32_to_h16<F16>(v2) | ((uint32_t)f32_to_h16<F16>(v3) << 16));
   }
-}
-
-// MXFP8 operand fragment for the scaled 32x32x64 MFMA, step s (64 codes) of a
-// 128-code K-major stage row: lane l holds row l % 32 and, for each of the step's
-// two 32-code scale blocks, 16 codes -- those at byte 16 (l / 32) of the block.
-__device__ __forceinline__ i32x8_t frag_mx(const char *st, int row0, int s, int lane) {
-  const int r = row0 + (lane & 31), h = lane >> 5;
-  const i32x4_t lo = *(const i32x4_t *)(st + r * kRowB + (((4 * s + h) ^ swz_k(r)) << 4));
-  const i32x4_t hi = *(const i32x4_t *)(st + r * kRowB + (((4 * s + 2 + h) ^ swz_k(r)) << 4));
-  return (i32x8_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
 // One output tile of one group: what a work item decodes to.
