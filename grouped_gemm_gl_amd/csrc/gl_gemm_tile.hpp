@@ -29,6 +29,7 @@ constexpr int kQ = kOpBytes / 1024 / kWaves;        // pieces per wave per opera
 constexpr int kLoadsPerStage = 2 * kQ;              // direct loads per wave per stage
 constexpr int kOrdM = 8, kOrdN = 4;                 // blocked work-item order
 static_assert(kS >= 2 && kS * kStageBytes <= 160 * 1024, "LDS ring");
+static_assert(5 * kOpBytes <= 160 * 1024, "direct-load ring with three weight slots");
 static_assert((kS - 2) * kLoadsPerStage <= 63, "vmcnt range");
 
 // MODE_ROWS: the grouped index is the tile row (forward, dgrad).  MODE_CONTR: the

@@ -20,9 +20,12 @@ TOL_F16 = 2e-3
 F16 = torch.float16
 
 SHAPES = [
+    # groups of at most 256 rows on average (the forward's deeper weight ring) ...
     (5, 200, 264, [0, 300, 1, 0, 513]),
     (3, 256, 512, [256, 257, 255]),
     (8, 136, 72, [3, 0, 0, 70, 260, 1, 0, 90]),
+    # ... and larger ones (its default ring)
+    (2, 200, 264, [700, 301]),
 ]
 
 

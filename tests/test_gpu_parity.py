@@ -50,7 +50,9 @@ def int_case(seed, G, K, N, m, dtype):
 
 
 SHAPES = [
-    # (G, K, N, m): ragged rows, partial k tile (K % 64), partial n tile, empty groups
+    # (G, K, N, m): ragged rows, partial k tile (K % 64), partial n tile, empty groups.
+    # The first four average at most 256 rows per group (the forward's deeper weight
+    # ring), the last two more (its default ring).
     (5, 200, 264, [0, 300, 1, 0, 513]),
     (3, 256, 512, [256, 257, 255]),
     (1, 64, 8, [37]),
