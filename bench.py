@@ -40,8 +40,8 @@ GEMM_SRCS = [os.path.join(ROOT, "grouped_gemm_gl_amd", "csrc", f)
              for f in ("gl_gemm_tile.hpp", "gl_gemm_bf16.hip", "gl_gemm_mxfp8.hip", "gl_common.hpp",
                        "gl_offsets.hpp")]
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
-# kernel-name fragment of each pass's GEMM (template arguments <A K-major, B K-major, mode, fp16>)
-# (template arguments <A K-major, B K-major, mode, fp16, schedule, bias grad>)
+# kernel-name fragment of each pass's GEMM (template arguments <A K-major, B K-major, mode,
+# fp16, schedule, bias grad>)
 PASS_KERNELS = {"forward": "gemm_bf16_kernel<true, true, 0, false, 0, false>",
                 "dgrad": "gemm_bf16_kernel<true, false, 0, false, 1, false>",
                 "wgrad_bgrad": "gemm_bf16_kernel<false, false, 1, false, 1, true>"}
@@ -50,7 +50,8 @@ PASS_WORKLOAD = {k: "bf16_train_g8_k4096_n14336" for k in PASS_KERNELS}
 WORKLOAD_KERNELS = {
     "bf16_zipf_g64_k2048_n1536": {"forward": PASS_KERNELS["forward"], "dgrad": PASS_KERNELS["dgrad"],
                                   "wgrad_main_grad": "gemm_bf16_kernel<false, false, 1, false, 1, false>"},
-    "bf16_fwd_g256_k7168_n2048_outbuf": {"forward": PASS_KERNELS["forward"]},
+    # groups of 128 rows on average: the forward's schedule with the deeper weight ring
+    "bf16_fwd_g256_k7168_n2048_outbuf": {"forward": "gemm_bf16_kernel<true, true, 0, false, 2, false>"},
 }
 GEMM_PASSES = tuple(PASS_KERNELS)
 COPY_BYTES = 1 << 30
@@ -482,6 +483,7 @@ def bench_mxfp8(torch, gl, synth, steps, warmup):
     dx = torch.empty(T, K, dtype=torch.bfloat16, device=dev)
     dw = torch.empty(G, N, K, dtype=torch.bfloat16, device=dev)
     gl.gl_quantize_mxfp8_weights(w, wq, wsc, wtq, wts)   # cached quantized weights
+    w_copy, dy_copy = torch.empty_like(w), torch.empty_like(dy)
     timer = EventTimer(torch)
     for i in range(warmup + steps):
         t = timer if i >= warmup else None
@@ -503,6 +505,10 @@ def bench_mxfp8(torch, gl, synth, steps, warmup):
         run("offsets_quantize_x", lambda: gl.gl_offsets_quantize_mxfp8(md, x, ws, xq, xs))
         run("quantize_w_again", lambda: gl.gl_group_quantize_mxfp8(w, wq, wsc))  # evicts x from the caches
         run("quantize_x_colwise", lambda: gl.gl_group_quantize_mxfp8_colwise(x, xtq, xts, ws, G))
+        # plain device copies of the same byte counts, the ceiling of a stream that
+        # reads and writes about as much as it reads (as the quantizers do)
+        run("copy_w", lambda: w_copy.copy_(w))
+        run("copy_dy", lambda: dy_copy.copy_(dy))
     torch.cuda.synchronize()
     per = timer.mean_ms()
     flops = 2.0 * T * N * K
@@ -530,6 +536,8 @@ def bench_mxfp8(torch, gl, synth, steps, warmup):
                            "offsets_and_x_both": gbs("offsets_quantize_x_both",
                                                      row_bytes(T, K) + col_bytes(T, K) - T * K * 2),
                            "w_rowwise_and_colwise": gbs("weights_refresh", G * N * K * (2 + 2 * (1 + 1 / 32)))}
+    out["copy_gbs"] = {"dy": gbs("copy_dy", 2 * T * N * 2), "w": gbs("copy_w", 2 * G * N * K * 2),
+                       "note": "device copy of dy / w into a buffer of its size, bytes read + written"}
     out["launch_us"] = {"offsets_quantize_x": round(per["offsets_quantize_x"] * 1e3, 1),
                         "offsets_quantize_x_both_ways": round(per["offsets_quantize_x_both"] * 1e3, 1),
                         "quantize_x": round(per["quantize_x"] * 1e3, 1),
