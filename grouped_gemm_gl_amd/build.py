@@ -4,6 +4,12 @@ Usage: ``python -m grouped_gemm_gl_amd.build`` (or ``build()`` from Python).  Ea
 ``csrc/*.hip`` file is compiled to an object in ``_build/`` in parallel and the
 objects are linked into ``grouped_gemm_gl_amd/libgrouped_linear.so``.
 
+``build()`` also builds the device-check copy ``grouped_gemm_gl_amd/libgrouped_linear_checked.so``
+(the same sources with ``GL_DEVICE_CHECKS=1``): its persistent kernels verify every work
+item they decode and flag a failure in the workspace status word
+(``GL_STATUS_DEVICE_CHECK``) instead of touching memory.  Select it with
+``GL_LIBRARY_PATH``.  ``--product-only`` (``build(device_checks=False)``) skips it.
+
 ``python -m grouped_gemm_gl_amd.build --host-sanitize`` (``build(host_sanitize=True)``)
 builds a second copy, ``_build/hostsan/libgrouped_linear_hostsan.so``, whose host code
 carries AddressSanitizer and UndefinedBehaviorSanitizer (device code is built as
@@ -26,6 +32,8 @@ OUT = os.path.join(HERE, "libgrouped_linear.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 SAN_DIR = os.path.join(BUILD_DIR, "hostsan")
 SAN_OUT = os.path.join(SAN_DIR, "libgrouped_linear_hostsan.so")
+CHECKED_DIR = os.path.join(BUILD_DIR, "checked")
+CHECKED_OUT = os.path.join(HERE, "libgrouped_linear_checked.so")
 ARCH = "gfx950"
 
 HIP_FLAGS = [
@@ -79,34 +87,42 @@ def asan_runtime() -> str:
                           text=True, check=True).stdout.strip()
 
 
-def build(verbose: bool = False, host_sanitize: bool = False) -> str:
-    out_dir = SAN_DIR if host_sanitize else BUILD_DIR
-    out = SAN_OUT if host_sanitize else OUT
-    os.makedirs(out_dir, exist_ok=True)
+def build(verbose: bool = False, host_sanitize: bool = False, device_checks: bool = True) -> str:
+    """Compile and link the library (returns its path); with device_checks, also the
+    device-check copy, its objects compiled in the same pool."""
     hipcc = _hipcc()
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    objs = [os.path.join(out_dir, os.path.basename(s) + ".o") for s in srcs]
-    flags = HIP_FLAGS
+    # (output directory, library, compile flags, link flags) of each copy
     if host_sanitize:
-        flags = [f for f in HIP_FLAGS if f != "-O3"] + ["-O1"] + SAN_COMPILE
+        copies = [(SAN_DIR, SAN_OUT, [f for f in HIP_FLAGS if f != "-O3"] + ["-O1"] + SAN_COMPILE, SAN_LINK)]
+    else:
+        copies = [(BUILD_DIR, OUT, HIP_FLAGS, [])]
+        if device_checks:
+            copies.append((CHECKED_DIR, CHECKED_OUT, HIP_FLAGS + ["-DGL_DEVICE_CHECKS=1"], []))
+    jobs = []
+    for out_dir, _, flags, _ in copies:
+        os.makedirs(out_dir, exist_ok=True)
+        jobs += [(src, os.path.join(out_dir, os.path.basename(src) + ".o"), flags) for src in srcs]
 
-    def compile_one(pair):
-        src, obj = pair
+    def compile_one(job):
+        src, obj, flags = job
         return _run([hipcc, *flags, "-c", src, "-o", obj])
 
-    workers = max(1, min(len(srcs), os.cpu_count() or 1, 16))
+    workers = max(1, min(len(jobs), os.cpu_count() or 1, 16))
     with concurrent.futures.ThreadPoolExecutor(workers) as ex:
-        logs = list(ex.map(compile_one, zip(srcs, objs)))
-    tmp = out + ".tmp"
-    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *(SAN_LINK if host_sanitize else []), "-o", tmp,
-          *objs])
-    os.replace(tmp, out)
+        logs = list(ex.map(compile_one, jobs))
+    for out_dir, out, _, link in copies:
+        objs = [os.path.join(out_dir, os.path.basename(s) + ".o") for s in srcs]
+        tmp = out + ".tmp"
+        _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *link, "-o", tmp, *objs])
+        os.replace(tmp, out)
     if verbose:
         for l in logs:
             if l.strip():
                 print(l)
-    return out
+    return copies[0][1]
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv, host_sanitize="--host-sanitize" in sys.argv))
+    print(build(verbose="-v" in sys.argv, host_sanitize="--host-sanitize" in sys.argv,
+                device_checks="--product-only" not in sys.argv))

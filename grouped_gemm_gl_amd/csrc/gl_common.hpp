@@ -102,6 +102,23 @@ __device__ inline bool ws_usable(const WsHeader *h, int G, int64_t T) {
 
 __host__ __device__ __forceinline__ int64_t min64(int64_t a, int64_t b) { return a < b ? a : b; }
 
+// Device checks.  The device-check build of the library (compiled with
+// GL_DEVICE_CHECKS=1) verifies each work item a persistent kernel decodes --
+// group index, tile row inside its group, tile column, contraction-schedule entry
+// -- before it touches memory; a failed check sets GL_STATUS_DEVICE_CHECK in the
+// workspace status word and skips the item (no trap: the kernel still runs to its
+// end).  The product build compiles the checks out.
+#ifndef GL_DEVICE_CHECKS
+#define GL_DEVICE_CHECKS 0
+#endif
+constexpr int32_t kStatusDeviceCheck = 8;
+// true when ok (or checks are off); otherwise flags the workspace and returns false
+__device__ __forceinline__ bool device_check(bool ok, const void *ws) {
+  if (!GL_DEVICE_CHECKS || ok) return true;
+  atomicOr((int *)ws, kStatusDeviceCheck);  // the status word opens the header
+  return false;
+}
+
 // Index of the group owning row tile q: the last g with pre[g] <= q (pre is the
 // non-decreasing exclusive prefix of per-group tile counts, pre[G] = total).
 // The whole wave searches: each lane tests a slice of pre[] and the ballots count.

@@ -110,6 +110,8 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
   // the u-th split tile, whose partials go to slots slot0 .. slot0 + S - 1.
   auto item = [&](const Tile &t, int part, int S, int u, int slot0, auto split_tag) __attribute__((always_inline)) {
     constexpr bool SPLIT = decltype(split_tag)::value;
+    if (!device_check(t.ok && (!SPLIT || (part >= 0 && part < S && slot0 >= 0 && slot0 + S <= slots)), p.ws))
+      return;
     const bool bgrad = BGRAD && t.jt == 0;
     if (MODE == MODE_CONTR && p.accumulate && t.g_rows == 0) {  // main_grad untouched
       if (bgrad) store_bgrad_zero(p, t);
@@ -371,11 +373,14 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
       const int w = base + (((base / grid) & 1) ? grid - 1 - first : first);
       if (w >= nitems) continue;
       const int pos = find_group(ws.items, p.G, w);
+      if (!device_check(pos >= 0 && pos < p.G, p.ws)) continue;
       const int g = ws.order[pos];
+      if (!device_check(g >= 0 && g < p.G, p.ws)) continue;
       const int sg = stg[g + 1] - stg[g];
       const int pg = sg > cap ? (sg + cap - 1) / cap : 1;
       const int local = w - ws.items[pos];
       const int part = local / ntiles, tl = local - part * ntiles;
+      if (!device_check(local >= 0 && part < pg, p.ws)) continue;
       const Tile t = decode_tile<A_KMAJ, B_KMAJ, MODE>(p, off, pre, g * ntiles + tl);
       if (pg > 1)
         item(t, part, pg, pos * ntiles + tl, ws.items[pos] + tl * pg, std::true_type{});

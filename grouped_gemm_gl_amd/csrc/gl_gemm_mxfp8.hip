@@ -87,6 +87,7 @@ __global__ __launch_bounds__(kThreads) void gemm_mxfp8_kernel(Params p) {
 
   for (int w = first; w < total; w += grid) {
     const Tile t = decode_tile<true, true, MODE>(p, off, pre, w, cpre);
+    if (!device_check(t.ok, p.ws)) continue;
     if (MODE == MODE_KCONTR && p.accumulate && t.g_rows == 0) continue;  // main_grad untouched
     // every stage is complete: K % 128 == 0 in row mode, padded groups otherwise
     const int nk = (int)(t.pmax / kBK);

@@ -359,6 +359,7 @@ struct Tile {
   int64_t g_off, g_rows;
   const uint16_t *a_base, *b_base;  // operand tile bases at contraction 0
   int a_rv, b_rv;                   // valid rows of the A and B tiles
+  bool ok;                          // device-check build: the item lies inside the launch
   int64_t pmax;                     // contraction length
 };
 
@@ -375,11 +376,15 @@ __device__ __forceinline__ Tile decode_tile(const Params &p, const int64_t *__re
   const int NT = p.tiles_j;
   if (MODE == MODE_ROWS) {
     t.g = find_group(pre, p.G, w / NT);
+    t.ok = t.g >= 0 && t.g < p.G;
+    if (GL_DEVICE_CHECKS && !t.ok) return t;
     local = w - pre[t.g] * NT;
     MT = pre[t.g + 1] - pre[t.g];
   } else {
     const int per = p.tiles_i * NT;
     t.g = w / per;
+    t.ok = w >= 0 && t.g < p.G;
+    if (GL_DEVICE_CHECKS && !t.ok) return t;
     local = w - t.g * per;
     MT = p.tiles_i;
   }
@@ -393,6 +398,13 @@ __device__ __forceinline__ Tile decode_tile(const Params &p, const int64_t *__re
   t.jt = cb * kOrdN + l3 / bh;
   t.g_off = off[t.g];
   t.g_rows = off[t.g + 1] - t.g_off;
+  if (GL_DEVICE_CHECKS) {
+    t.ok = MT > 0 && local >= 0 && local < MT * NT && t.it < MT && t.jt < NT && t.g_off >= 0 && t.g_rows >= 0 &&
+           t.g_off + t.g_rows <= p.T;
+    if (MODE == MODE_ROWS) t.ok = t.ok && (int64_t)t.it * kBM < t.g_rows;
+    if (MODE == MODE_KCONTR) t.ok = t.ok && cpre[t.g] >= 0 && cpre[t.g + 1] >= cpre[t.g];
+    if (!t.ok) return t;
+  }
   if (MODE == MODE_ROWS) {
     t.a_base = p.A + (t.g_off + (int64_t)t.it * kBM) * p.lda;
     t.a_rv = (int)min64(kBM, t.g_rows - (int64_t)t.it * kBM);

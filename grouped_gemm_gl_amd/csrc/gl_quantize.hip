@@ -342,6 +342,8 @@ __global__ __launch_bounds__(kQThreads) void quantize_mxfp8_colwise_tile_kernel(
     r0 = v.off[g] + (b128 - pre[g]) * kCtRows;
     rend = v.off[g + 1];
   }
+  // (device-check build) the tile's rows lie inside the input, its codes inside the output
+  if (!device_check(r0 >= 0 && r0 < rend && rend <= total_rows && (b128 + 1) * kCtRows <= ld, ws)) return;
   ct_tile(src, cols, r0, rend, c0, data + c0 * ld + b128 * kCtRows, ld, scale + c0 * (ld / 32) + b128 * (kCtRows / 32),
           ld / 32, row_data, row_scale, lds);
 }

@@ -80,7 +80,11 @@ enum {
 enum {
   GL_STATUS_NEGATIVE_SPLIT = 1, /* some m_splits[g] < 0 */
   GL_STATUS_SUM_MISMATCH = 2,   /* sum of m_splits != total_rows */
-  GL_STATUS_WORKSPACE = 4       /* a later call named a workspace built for other G / T */
+  GL_STATUS_WORKSPACE = 4,      /* a later call named a workspace built for other G / T */
+  GL_STATUS_DEVICE_CHECK = 8    /* device-check build only (libgrouped_linear_checked.so): a
+                                   kernel decoded a work item outside its launch's bounds (a
+                                   workspace changed after the offsets call, or a defect) and
+                                   skipped it without touching memory */
 };
 
 /*
