@@ -107,12 +107,15 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
   };
 
   // One work item: the whole contraction of tile t, or (SPLIT) part `part` of S of
-  // the u-th split tile, whose partials go to slots slot0 .. slot0 + S - 1.
-  auto item = [&](const Tile &t, int part, int S, int u, int slot0, auto split_tag) __attribute__((always_inline)) {
+  // the u-th split tile, whose partials go to slots slot0 .. slot0 + S - 1.  The
+  // bias-grad tag marks a tile of the first column of a BGRAD launch: its loop is a
+  // copy of its own, so the other tiles run the plain loop (its registers and code).
+  auto item = [&](const Tile &t, int part, int S, int u, int slot0, auto split_tag,
+                  auto bgrad_tag) __attribute__((always_inline)) {
     constexpr bool SPLIT = decltype(split_tag)::value;
     if (!device_check(t.ok && (!SPLIT || (part >= 0 && part < S && slot0 >= 0 && slot0 + S <= slots)), p.ws))
       return;
-    const bool bgrad = BGRAD && t.jt == 0;
+    constexpr bool bgrad = BGRAD && decltype(bgrad_tag)::value;
     if (MODE == MODE_CONTR && p.accumulate && t.g_rows == 0) {  // main_grad untouched
       if (bgrad) store_bgrad_zero(p, t);
       return;
@@ -352,12 +355,12 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
     // whole tiles, round after round; the last round may be split
     const SplitPlan sp = split_plan(total, grid, nk_rows, slots);
     for (int w = first; w < sp.full; w += grid)
-      item(decode_tile<A_KMAJ, B_KMAJ, MODE>(p, off, pre, w), 0, 1, 0, 0, std::false_type{});
+      item(decode_tile<A_KMAJ, B_KMAJ, MODE>(p, off, pre, w), 0, 1, 0, 0, std::false_type{}, std::false_type{});
     // the parts of the last round: u = first, consecutive u are consecutive tiles
     if (first < sp.rem * sp.S) {
       const int u = first % sp.rem;
       item(decode_tile<A_KMAJ, B_KMAJ, MODE>(p, off, pre, sp.full + u), first / sp.rem, sp.S, u, u * sp.S,
-           std::true_type{});
+           std::true_type{}, std::false_type{});
     }
   } else {
     // the contraction schedule of the plan kernel: work items in order of decreasing
@@ -382,10 +385,18 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
       const int part = local / ntiles, tl = local - part * ntiles;
       if (!device_check(local >= 0 && part < pg, p.ws)) continue;
       const Tile t = decode_tile<A_KMAJ, B_KMAJ, MODE>(p, off, pre, g * ntiles + tl);
-      if (pg > 1)
-        item(t, part, pg, pos * ntiles + tl, ws.items[pos] + tl * pg, std::true_type{});
-      else
-        item(t, 0, 1, 0, 0, std::false_type{});
+      auto run = [&](auto bgrad_tag) __attribute__((always_inline)) {
+        if (pg > 1)
+          item(t, part, pg, pos * ntiles + tl, ws.items[pos] + tl * pg, std::true_type{}, bgrad_tag);
+        else
+          item(t, 0, 1, 0, 0, std::false_type{}, bgrad_tag);
+      };
+      if constexpr (BGRAD) {
+        if (t.jt == 0) run(std::true_type{});
+        else run(std::false_type{});
+      } else {
+        run(std::false_type{});
+      }
     }
   }
 }
