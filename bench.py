@@ -744,7 +744,7 @@ def main():
         summarize_clock(args.summarize_clock, workload=args.workload)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(groups would shard across GPUs as expert parallelism).", file=sys.stderr)
         sys.exit(2)
 

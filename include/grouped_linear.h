@@ -71,7 +71,7 @@ enum {
   GL_ERR_ARG = -1,         /* bad size, NULL or misaligned pointer, both/neither weight forms */
   GL_ERR_DTYPE = -2,       /* element type not valid for this call */
   GL_ERR_SHAPE = -3,       /* output capacity < total_rows, K/N alignment, K % 32 for MXFP8 */
-  GL_ERR_UNSUPPORTED = -4, /* reserved: recognised but not provided by this build */
+  GL_ERR_UNSUPPORTED = -4, /* reserved: recognised but not provided by the library */
   GL_ERR_HIP = -5,         /* a HIP runtime call failed */
   GL_ERR_HOST_MEMORY = -6  /* a deferred-wgrad queue could not allocate its host record */
 };
