@@ -143,13 +143,13 @@ typedef __attribute__((ext_vector_type(4))) int i32x4_t;
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
-// Round-to-nearest-even float -> bfloat16 bits; NaN stays a (quiet) NaN.
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
+// Round-to-nearest-even float -> bfloat16 bits, by gfx950's conversion instruction
+// (v_cvt_pk_bf16_f32): for a finite or infinite value, the bits of adding 0x7fff plus
+// the lowest kept bit and truncating; a NaN keeps its sign and upper payload with the
+// quiet bit set.  (Compared on the device over all 2^32 inputs.)  Written out in
+// integer operations instead, with a NaN test per value, the conversion was most of
+// the GEMM epilogues' instructions.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 // fp16 <-> fp32 (the float -> half conversion rounds to nearest even; overflow gives inf)
 __device__ __forceinline__ float f16_to_f32(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
@@ -159,9 +159,14 @@ template <bool F16>
 __device__ __forceinline__ float h16_to_f32(uint16_t h) { return F16 ? f16_to_f32(h) : bf16_to_f32(h); }
 template <bool F16>
 __device__ __forceinline__ uint16_t f32_to_h16(float f) { return F16 ? f32_to_f16(f) : f32_to_bf16(f); }
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+// Two values as one word of 16-bit outputs (lo in the low half); bf16 pairs take one
+// conversion instruction, with the bits of f32_to_bf16 for each.
+template <bool F16>
+__device__ __forceinline__ uint32_t pack_h16x2(float lo, float hi) {
+  if (F16) return (uint32_t)f32_to_f16(lo) | ((uint32_t)f32_to_f16(hi) << 16);
+  typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
 }  // namespace gl

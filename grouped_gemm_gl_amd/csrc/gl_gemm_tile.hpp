@@ -348,6 +348,7 @@ __device__ __forceinline__ void store4(uintptr_t cbase, int64_t row, int64_t ldc
       v0 += h16_to_f32<F16>(o.x & 0xffff); v1 += h16_to_f32<F16>(o.x >> 16);
       v2 += h16_to_f32<F16>(o.y & 0xffff); v3 += h16_to_f32<F16>(o.y >> 16);
     }
+    // (value by value: measured faster here than the pair conversion in the forward)
     *dst = make_uint2((uint32_t)f32_to_h16<F16>(v0) | ((uint32_t)f32_to_h16<F16>(v1) << 16),
                       (uint32_t)f32_to_h16<F16>(v2) | ((uint32_t)f32_to_h16<F16>(v3) << 16));
   }
@@ -707,8 +708,7 @@ __device__ __forceinline__ void store_tile_lds(const Params &p, const Tile &t, c
     }
     const int slot = jl >> 3, half = (jl >> 2) & 1;
     *(uint2 *)(lds + il * 512 + ((slot ^ (il & 31)) << 4) + half * 8) =
-        make_uint2((uint32_t)f32_to_h16<F16>(v.x) | ((uint32_t)f32_to_h16<F16>(v.y) << 16),
-                   (uint32_t)f32_to_h16<F16>(v.z) | ((uint32_t)f32_to_h16<F16>(v.w) << 16));
+        make_uint2(pack_h16x2<F16>(v.x, v.y), pack_h16x2<F16>(v.z, v.w));
   }
   __syncthreads();
   const int wave = threadIdx.x >> 6, s = lane_t & 31;

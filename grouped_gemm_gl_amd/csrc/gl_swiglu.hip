@@ -46,7 +46,7 @@ struct Vec16 {
     uint32_t w[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      w[i] = (uint32_t)f32_to_h16<F16>(v[2 * i]) | ((uint32_t)f32_to_h16<F16>(v[2 * i + 1]) << 16);
+      w[i] = pack_h16x2<F16>(v[2 * i], v[2 * i + 1]);
     *(uint4 *)p = make_uint4(w[0], w[1], w[2], w[3]);
   }
 };
