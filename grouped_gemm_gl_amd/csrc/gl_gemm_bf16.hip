@@ -84,8 +84,16 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
   // the stage ring; wgrad adds the bias-grad partial sums after it (one LDS object:
   // a second __shared__ array makes the compiler wait for the direct loads before
   // every LDS read)
+  // The forward on the two-slot weight ring keeps each tile's 256 bias values in LDS
+  // beside the ring (two 512-byte buffers, alternating by tile), loaded with the
+  // tile's first stage: read from global memory in the epilogue, each tile waited
+  // for them there.
+  constexpr bool kBiasLds = DIRECT && kLeadB == 1;
+  constexpr int kBiasBytes = kBN * 2;
   __shared__ __attribute__((aligned(1024)))
-  char lds[DIRECT ? (2 + kLeadB + 1) * kOpBytes : kS * kStageBytes + (BGRAD ? kDbLdsBytes : 0)];
+  char lds[DIRECT ? (2 + kLeadB + 1) * kOpBytes + (kBiasLds ? 2 * kBiasBytes : 0)
+                  : kS * kStageBytes + (BGRAD ? kDbLdsBytes : 0)];
+  int ntile = 0;  // items begun by this workgroup (the bias buffer's parity)
 
   const WsView ws = ws_view(p.ws, p.G);
   if (!ws_usable(ws.hdr, p.G, p.T)) return;
@@ -130,6 +138,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
 
     Stream<A_KMAJ> sa;
     Stream<B_KMAJ> sb;
+    const char *bias_l = nullptr;  // this tile's bias in LDS (kBiasLds)
     sa.init(t.a_base, p.lda, t.a_rv, wave, lane);
     sb.init(t.b_base, p.ldb, t.b_rv, wave, lane);
     auto stage_ptr = [&](int s) { return lds + (s % kS) * kStageBytes; };
@@ -192,6 +201,19 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
       // B kt + 2 in flight.  A masked stage may send fewer: then everything is waited
       // for.
       if (kend > kbeg) {
+        if (kBiasLds) {
+          // wave 0: the tile's bias columns (past the last column: zeros), 16 bytes per
+          // lane of its first half; waited for with the first stage
+          bias_l = lds + (2 + kLeadB + 1) * kOpBytes + (ntile++ & 1) * kBiasBytes;
+          const char *brow = p.bias ? (const char *)p.bias + (int64_t)t.g * p.cols_j * 2
+                                    : p.bias_ptrs ? (const char *)p.bias_ptrs[t.g] : nullptr;
+          if (brow && wave == 0 && lane < kBiasBytes / 16) {
+            const int64_t c0 = (int64_t)t.jt * kBN;
+            const __amdgpu_buffer_rsrc_t r =
+                __builtin_amdgcn_make_buffer_rsrc((void *)(brow + c0 * 2), (short)0, t.b_rv * 2, 0x00020000);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (GL_LDS void *)bias_l, 16, lane * 16, 0, 0, 0);
+          }
+        }
         issue_a(kbeg);
         issue_b(kbeg);
         if (kLeadB == 2 && kbeg + 1 < kend) issue_b(kbeg + 1);
@@ -348,7 +370,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
     if (MODE != MODE_ROWS && !p.out_f32 && !p.accumulate)
       store_tile_lds<MODE, F16>(p, t, acc, wm, wn, lane, lds);
     else
-      store_tile<MODE, F16, A_KMAJ && B_KMAJ>(p, t, acc, wm, wn, lane);  // the forward takes a bias
+      store_tile<MODE, F16, A_KMAJ && B_KMAJ>(p, t, acc, wm, wn, lane, bias_l);  // the forward takes a bias
   };
 
   if constexpr (MODE == MODE_ROWS) {

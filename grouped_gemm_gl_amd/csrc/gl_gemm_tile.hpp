@@ -610,10 +610,12 @@ __device__ __forceinline__ bool split_finish(const WsView &ws, int u, int slot0,
 // the output's type) is added to the fp32 sum first; a lane's column depends only
 // on q % kColGroups, so its bias values are loaded once per distinct column, ahead
 // of the stores (loaded beside each store, every quad waited for its load: the
-// compiler cannot move a load above a store that may alias it).  BIAS: the kernel
+// compiler cannot move a load above a store that may alias it), or read from
+// `bias_lds` when the caller staged the tile's 16-bit bias there.  BIAS: the kernel
 // takes a bias at all (the forward); the others carry no bias code or registers.
 template <int MODE, bool F16, bool BIAS, class ACC>
-__device__ __forceinline__ void store_tile(const Params &p, const Tile &t, const ACC &acc, int wm, int wn, int lane) {
+__device__ __forceinline__ void store_tile(const Params &p, const Tile &t, const ACC &acc, int wm, int wn, int lane,
+                                           const char *bias_lds = nullptr) {
   using L = AccLayout<ACC>;
   char *cbase;
   int64_t row0;
@@ -634,7 +636,11 @@ __device__ __forceinline__ void store_tile(const Params &p, const Tile &t, const
     L::pos(c, lane, il, jl);
     const int64_t col = (int64_t)t.jt * kBN + jl + wn * kWTN;
     bv[c] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (BIAS && bias_g && jl + wn * kWTN < t.b_rv) {
+    if (BIAS && bias_g && bias_lds) {  // the tile's 16-bit bias, staged in LDS
+      const uint2 u = *(const uint2 *)(bias_lds + (jl + wn * kWTN) * 2);
+      bv[c] = make_float4(h16_to_f32<F16>(u.x & 0xffff), h16_to_f32<F16>(u.x >> 16),
+                          h16_to_f32<F16>(u.y & 0xffff), h16_to_f32<F16>(u.y >> 16));
+    } else if (BIAS && bias_g && jl + wn * kWTN < t.b_rv) {
       if (p.out_f32) {
         bv[c] = *(const GL_GLOBAL float4 *)((uintptr_t)bias_g + col * 4);
       } else {
