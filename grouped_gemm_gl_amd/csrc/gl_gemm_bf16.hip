@@ -139,8 +139,11 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
     Stream<A_KMAJ> sa;
     Stream<B_KMAJ> sb;
     const char *bias_l = nullptr;  // this tile's bias in LDS (kBiasLds)
-    sa.init(t.a_base, p.lda, t.a_rv, wave, lane);
-    sb.init(t.b_base, p.ldb, t.b_rv, wave, lane);
+    // the deep ring's operand bases as visibly wave-uniform pointers (its stage loads
+    // otherwise went through per-load loops over distinct resource values)
+    constexpr bool kUniformBases = SCHED == SCHED_DIRECT_DEEP;
+    sa.init(kUniformBases ? uniform_ptr(t.a_base) : t.a_base, p.lda, t.a_rv, wave, lane);
+    sb.init(kUniformBases ? uniform_ptr(t.b_base) : t.b_base, p.ldb, t.b_rv, wave, lane);
     auto stage_ptr = [&](int s) { return lds + (s % kS) * kStageBytes; };
 
     ACC acc;

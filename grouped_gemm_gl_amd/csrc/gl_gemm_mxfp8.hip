@@ -31,8 +31,9 @@ struct ScaleStream {
   const char *base;  // scale row 0 of the tile, at the tile's first contraction dword
   uint32_t off;      // this lane's row offset
 
+  template <bool UNIFORM>
   __device__ __forceinline__ void init(const uint8_t *rows, int64_t ld, int rv, int r) {
-    base = (const char *)rows;
+    base = UNIFORM ? uniform_ptr((const char *)rows) : (const char *)rows;
     off = (uint32_t)((int64_t)(r < rv ? r : rv - 1) * ld);
   }
   // dword t of the row
@@ -94,24 +95,28 @@ __global__ __launch_bounds__(kThreads) void gemm_mxfp8_kernel(Params p) {
     const int kbeg = 0, kend = nk;
 
     Stream<true> sa, sb;
-    sa.init(t.a_base, p.lda, t.a_rv, wave, lane);
-    sb.init(t.b_base, p.ldb, t.b_rv, wave, lane);
+    // row mode: the operand bases as visibly wave-uniform pointers (the weights' may
+    // come from a pointer array; each stage's weight loads went through per-load
+    // loops over distinct resource values).  The wgrad's bases are arguments plus
+    // offsets, already uniform.
+    sa.init(MODE == MODE_ROWS ? uniform_ptr(t.a_base) : t.a_base, p.lda, t.a_rv, wave, lane);
+    sb.init(MODE == MODE_ROWS ? uniform_ptr(t.b_base) : t.b_base, p.ldb, t.b_rv, wave, lane);
     // scale rows from their 16-byte aligned start; stage s's dword is d0 + s of the
     // row (the group's scale columns start at 4 per padded 128-element tile)
     const int d0 = MODE == MODE_ROWS ? 0 : cpre[t.g];
     ScaleStream ss;
     if (MODE == MODE_ROWS) {
       if (wave < 4) {
-        ss.init(p.a_scale + (t.g_off + (int64_t)t.it * kBM) * p.scale_ld, p.scale_ld, t.a_rv, wave * 64 + lane);
+        ss.template init<MODE == MODE_ROWS>(p.a_scale + (t.g_off + (int64_t)t.it * kBM) * p.scale_ld, p.scale_ld, t.a_rv, wave * 64 + lane);
       } else {
         const uint8_t *bs = p.b_scale ? p.b_scale + (int64_t)t.g * p.cols_j * p.scale_ld : p.b_scale_ptrs[t.g];
-        ss.init(bs + (int64_t)t.jt * kBN * p.scale_ld, p.scale_ld, t.b_rv, (wave - 4) * 64 + lane);
+        ss.template init<MODE == MODE_ROWS>(bs + (int64_t)t.jt * kBN * p.scale_ld, p.scale_ld, t.b_rv, (wave - 4) * 64 + lane);
       }
     } else {
       if (wave < 4)
-        ss.init(p.a_scale + (int64_t)t.it * kBM * p.scale_ld, p.scale_ld, t.a_rv, wave * 64 + lane);
+        ss.template init<MODE == MODE_ROWS>(p.a_scale + (int64_t)t.it * kBM * p.scale_ld, p.scale_ld, t.a_rv, wave * 64 + lane);
       else
-        ss.init(p.b_scale + (int64_t)t.jt * kBN * p.scale_ld, p.scale_ld, t.b_rv, (wave - 4) * 64 + lane);
+        ss.template init<MODE == MODE_ROWS>(p.b_scale + (int64_t)t.jt * kBN * p.scale_ld, p.scale_ld, t.b_rv, (wave - 4) * 64 + lane);
     }
     auto stage_ptr = [&](int s) { return lds + (s % kS) * kStageBytes; };
     // operands of stage s, and its scales: with 16-byte chunks, the chunk holding
