@@ -700,6 +700,7 @@ __device__ __forceinline__ void store_tile(const Params &p, const Tile &t, const
 template <int MODE, bool F16, class ACC>
 __device__ __forceinline__ void store_tile_lds(const Params &p, const Tile &t, const ACC &acc, int wm, int wn,
                                                int lane, char *lds) {
+  // Only the wgrads call it (no bias); the row-mode origin is kept for completeness.
   using L = AccLayout<ACC>;
   uintptr_t cbase;
   int64_t row0;
@@ -710,9 +711,6 @@ __device__ __forceinline__ void store_tile_lds(const Params &p, const Tile &t, c
     cbase = p.C ? (uintptr_t)p.C + (uintptr_t)((int64_t)t.g * p.c_gstride * 2) : (uintptr_t)p.C_ptrs[t.g];
     row0 = (int64_t)t.it * kBM;
   }
-  uintptr_t bias_g = 0;
-  if (p.bias) bias_g = (uintptr_t)p.bias + (uintptr_t)((int64_t)t.g * p.cols_j * 2);
-  else if (p.bias_ptrs) bias_g = (uintptr_t)p.bias_ptrs[t.g];
   __syncthreads();  // a split tile's arrival flag sits in the ring's first word
   int lane_t = lane;  // opaque, as in store_tile (measured: faster in the bf16 wgrad, not the MXFP8 one)
   if (MODE == MODE_CONTR) asm volatile("" : "+v"(lane_t));
@@ -722,25 +720,36 @@ __device__ __forceinline__ void store_tile_lds(const Params &p, const Tile &t, c
     L::pos(q, lane_t, il, jl);
     il += wm * kWTM;
     jl += wn * kWTN;
-    float4 v = L::get(acc, q);
-    if (bias_g && jl < t.b_rv) {
-      const uint2 bv = *(const GL_GLOBAL uint2 *)(bias_g + ((int64_t)t.jt * kBN + jl) * 2);
-      v.x += h16_to_f32<F16>(bv.x & 0xffff); v.y += h16_to_f32<F16>(bv.x >> 16);
-      v.z += h16_to_f32<F16>(bv.y & 0xffff); v.w += h16_to_f32<F16>(bv.y >> 16);
-    }
+    const float4 v = L::get(acc, q);
     const int slot = jl >> 3, half = (jl >> 2) & 1;
     *(uint2 *)(lds + il * 512 + ((slot ^ (il & 31)) << 4) + half * 8) =
         make_uint2(pack_h16x2<F16>(v.x, v.y), pack_h16x2<F16>(v.z, v.w));
   }
   __syncthreads();
+  // The stores go through a buffer resource over the tile's output block, from its
+  // first element: a lane outside the block stores at an offset past the resource's
+  // end, which the hardware drops.  So every store is issued unconditionally, and
+  // each group of four rows has its LDS reads in flight together (guarded stores
+  // each waited for their own read).  Offsets: r < 256 rows of at most 2^22
+  // columns, under 2^31 bytes.
   const int wave = threadIdx.x >> 6, s = lane_t & 31;
-#pragma unroll 4
-  for (int it = 0; it < kBM / kWaves / 2; ++it) {
-    const int r = wave * (kBM / kWaves) + it * 2 + (lane_t >> 5);
-    if (r < t.a_rv && s * 8 < t.b_rv) {
-      const uint4 v = *(const uint4 *)(lds + r * 512 + ((s ^ (r & 31)) << 4));
-      *(GL_GLOBAL uint4 *)(cbase + ((row0 + r) * p.ldc + (int64_t)t.jt * kBN + s * 8) * 2) = v;
+  const __amdgpu_buffer_rsrc_t rs =
+      rsrc_at(uniform_ptr((const char *)(cbase + (uintptr_t)(row0 * p.ldc + (int64_t)t.jt * kBN) * 2)));
+  const bool col_ok = s * 8 < t.b_rv;
+  typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+  constexpr int kRowsPerWave = kBM / kWaves, kIters = kRowsPerWave / 2, kBatch = 4;
+#pragma unroll
+  for (int it0 = 0; it0 < kIters; it0 += kBatch) {
+    u32x4_t v[kBatch];
+    uint32_t o[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int r = wave * kRowsPerWave + (it0 + k) * 2 + (lane_t >> 5);
+      v[k] = *(const u32x4_t *)(lds + r * 512 + ((s ^ (r & 31)) << 4));
+      o[k] = r < t.a_rv && col_ok ? (uint32_t)(((int64_t)r * p.ldc + s * 8) * 2) : 0x80000000u;
     }
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) __builtin_amdgcn_raw_buffer_store_b128(v[k], rs, o[k], 0, 0);
   }
   __syncthreads();  // the ring is refilled by the next tile
 }
