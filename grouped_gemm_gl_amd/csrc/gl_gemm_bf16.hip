@@ -138,7 +138,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
 
     Stream<A_KMAJ> sa;
     Stream<B_KMAJ> sb;
-    const char *bias_l = nullptr;  // this tile's bias in LDS (kBiasLds)
+    const char *bias_l = nullptr;  // this tile's bias in LDS (kBiasLds, when the launch has a bias)
     // the deep ring's operand bases as visibly wave-uniform pointers (its stage loads
     // otherwise went through per-load loops over distinct resource values)
     constexpr bool kUniformBases = SCHED == SCHED_DIRECT_DEEP;
@@ -207,14 +207,15 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
         if (kBiasLds) {
           // wave 0: the tile's bias columns (past the last column: zeros), 16 bytes per
           // lane of its first half; waited for with the first stage
-          bias_l = lds + (2 + kLeadB + 1) * kOpBytes + (ntile++ & 1) * kBiasBytes;
+          char *const buf = lds + (2 + kLeadB + 1) * kOpBytes + (ntile++ & 1) * kBiasBytes;
           const char *brow = p.bias ? (const char *)p.bias + (int64_t)t.g * p.cols_j * 2
                                     : p.bias_ptrs ? (const char *)p.bias_ptrs[t.g] : nullptr;
+          bias_l = brow ? buf : nullptr;  // null: no bias
           if (brow && wave == 0 && lane < kBiasBytes / 16) {
             const int64_t c0 = (int64_t)t.jt * kBN;
             const __amdgpu_buffer_rsrc_t r =
                 __builtin_amdgcn_make_buffer_rsrc((void *)(brow + c0 * 2), (short)0, t.b_rv * 2, 0x00020000);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (GL_LDS void *)bias_l, 16, lane * 16, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (GL_LDS void *)buf, 16, lane * 16, 0, 0, 0);
           }
         }
         issue_a(kbeg);
@@ -370,8 +371,8 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
     // Tiles of the register-staged schedule (dgrad, wgrad) with a 16-bit output go out
     // through LDS as whole lines (64-group dgrad -2.4%, 8-group dgrad neutral, wgrads
     // faster); the forward keeps its direct stores, which add its bias.
-    if (!DIRECT && !p.out_f32 && !p.accumulate)
-      store_tile_lds<MODE, F16>(p, t, acc, wm, wn, lane, lds);
+    if ((!DIRECT || kBiasLds) && !p.out_f32 && !p.accumulate)
+      store_tile_lds<MODE, F16>(p, t, acc, wm, wn, lane, lds, bias_l);
     else
       store_tile<MODE, F16, A_KMAJ && B_KMAJ>(p, t, acc, wm, wn, lane, bias_l);  // the forward takes a bias
   };

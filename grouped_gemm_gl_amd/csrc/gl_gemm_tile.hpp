@@ -699,8 +699,9 @@ __device__ __forceinline__ void store_tile(const Params &p, const Tile &t, const
 // needs 128 KiB of `lds`, which no wave may still be reading on entry.
 template <int MODE, bool F16, class ACC>
 __device__ __forceinline__ void store_tile_lds(const Params &p, const Tile &t, const ACC &acc, int wm, int wn,
-                                               int lane, char *lds) {
-  // No bias: the wgrads and dgrad call it.
+                                               int lane, char *lds, const char *bias_lds = nullptr) {
+  // bias_lds: the tile's 16-bit bias, staged in LDS outside the first 128 KiB (the
+  // forward); null for the others.
   using L = AccLayout<ACC>;
   uintptr_t cbase;
   int64_t row0;
@@ -723,7 +724,12 @@ __device__ __forceinline__ void store_tile_lds(const Params &p, const Tile &t, c
     L::pos(q, lane_t, il, jl);
     il += wm * kWTM;
     jl += wn * kWTN;
-    const float4 v = L::get(acc, q);
+    float4 v = L::get(acc, q);
+    if (bias_lds) {
+      const uint2 u = *(const uint2 *)(bias_lds + jl * 2);
+      v.x += h16_to_f32<F16>(u.x & 0xffff); v.y += h16_to_f32<F16>(u.x >> 16);
+      v.z += h16_to_f32<F16>(u.y & 0xffff); v.w += h16_to_f32<F16>(u.y >> 16);
+    }
     const int slot = jl >> 3, half = (jl >> 2) & 1;
     *(uint2 *)(lds + il * 512 + ((slot ^ (il & 31)) << 4) + half * 8) =
         make_uint2(pack_h16x2<F16>(v.x, v.y), pack_h16x2<F16>(v.z, v.w));
