@@ -183,9 +183,11 @@ __global__ __launch_bounds__(kThreads) void gemm_mxfp8_kernel(Params p) {
       wait_lgkm0();
       __builtin_amdgcn_s_barrier();
     }
-    // the wgrad's short contractions make its 1 GiB output the larger cost: there
-    // the tile goes out through LDS as whole lines
-    if (MODE != MODE_ROWS && !p.out_f32 && !p.accumulate)
+    // 16-bit outputs go out through LDS as whole lines (the ring is idle after the
+    // loop; the scale area lies beyond it): the wgrad's short contractions make its
+    // 1 GiB output the larger cost, and the forward and dgrad gain 1-2% too.  A
+    // row-mode launch with a bias keeps the direct stores, which add it.
+    if (!p.out_f32 && !p.accumulate && (MODE != MODE_ROWS || (!p.bias && !p.bias_ptrs)))
       store_tile_lds<MODE, false>(p, t, acc, wm, wn, lane, lds);
     else
       store_tile<MODE, false, MODE == MODE_ROWS>(p, t, acc, wm, wn, lane);
