@@ -41,9 +41,10 @@
 //     waves themselves, in the middle of a compute phase, a stage later; the loads of
 //     stage kt + 2 go out in the read phase after stage kt + 1 is written, and the
 //     direct-load return path no longer competes with the transpose reads for LDS.
-//     32x32x16 MFMAs (two 16-deep steps per phase).  The wgrad tiles of the first
-//     column also add their dy stages into the bias gradient from the staging
-//     registers, before each stage is written to the ring.
+//     32x32x16 MFMAs (two 16-deep steps per phase).  The wgrad tiles of one column
+//     per group (column g mod the column count) also add their dy stages into the
+//     bias gradient from the staging registers, before each stage is written to the
+//     ring.
 //
 // Loads: per lane the address of a piece is a fixed 32-bit offset from a
 // wave-uniform tile base held in a buffer resource (scalar registers), so issuing a
@@ -72,8 +73,8 @@ enum { SCHED_DIRECT = 0, SCHED_STAGED = 1, SCHED_DIRECT_DEEP = 2 };
 
 // F16: the operands are fp16 instead of bf16; staging and fragments are the same
 // 16-byte moves of 2-byte elements.
-// BGRAD (wgrad, STAGED only): the tiles of the first column also produce the bias
-// gradient.
+// BGRAD (wgrad, STAGED only): the tiles of one column per group also produce the
+// bias gradient.
 template <bool A_KMAJ, bool B_KMAJ, int MODE, bool F16, int SCHED, bool BGRAD = false>
 __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
   static_assert(!BGRAD || SCHED == SCHED_STAGED, "the bias-grad fusion runs on the staged schedule");
@@ -116,7 +117,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
 
   // One work item: the whole contraction of tile t, or (SPLIT) part `part` of S of
   // the u-th split tile, whose partials go to slots slot0 .. slot0 + S - 1.  The
-  // bias-grad tag marks a tile of the first column of a BGRAD launch: its loop is a
+  // bias-grad tag marks a tile of a group's bias-grad column in a BGRAD launch: its loop is a
   // copy of its own, so the other tiles run the plain loop (its registers and code).
   auto item = [&](const Tile &t, int part, int S, int u, int slot0, auto split_tag,
                   auto bgrad_tag) __attribute__((always_inline)) {
@@ -418,7 +419,11 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(Params p) {
           item(t, 0, 1, 0, 0, std::false_type{}, bgrad_tag);
       };
       if constexpr (BGRAD) {
-        if (t.jt == 0) run(std::true_type{});
+        // Any tile of a row block streams the same dy columns, so the bias grad may come
+        // from any column: group g takes column g mod tiles_j, which spreads these
+        // slower tiles over the grid (8-group workload: at most 2 per CU instead of 4;
+        // the sums and their order are the same in every column).
+        if (t.jt == t.g % p.tiles_j) run(std::true_type{});
         else run(std::false_type{});
       } else {
         run(std::false_type{});

@@ -451,8 +451,8 @@ __device__ __forceinline__ Tile decode_tile(const Params &p, const int64_t *__re
 // operand, MN-major, through the staging registers: piece q of a lane holds the 8
 // columns c*8 .. c*8 + 7 of contraction row p = 2 (wave + 8 q) + lane / 32, with
 // c = (lane % 32) ^ swz_m(p).  The swizzle of p does not depend on q, so a lane's
-// pieces of every stage cover the same 8 columns: the tiles of the first k column
-// add each stage's pieces, as they come in, into 8 fp32 column sums per lane (rows
+// pieces of every stage cover the same 8 columns: the tiles of one k column per
+// group add each stage's pieces, as they come in, into 8 fp32 column sums per lane (rows
 // past the group's end are zero pieces and add nothing).  The sums live in the
 // lane's own 32-byte slot of an LDS area beside the stage ring, not in registers:
 // 8 registers held across the contraction loop made the compiler spill inside it.

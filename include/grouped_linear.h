@@ -187,7 +187,7 @@ int gl_bgrad(int num_groups, int64_t out_features, int64_t total_rows, gl_dtype 
  * gl_wgrad and gl_bgrad of the same dy in one call, dy read once (page
  * "transformer_engine/pytorch/ops/basic/grouped_linear.py", fuser_backward: the
  * bias gradient and the wgrad GEMMs both consume the grad output).  For bf16 / fp16
- * inputs the wgrad tiles of the first column of in_features also add up their dy
+ * inputs the wgrad tiles of one column of in_features per group also add up their dy
  * stages while those sit in LDS, so no separate pass over dy runs; for fp32 inputs
  * the bias gradient is a second launch.  Arguments as gl_wgrad, plus
  *   db_dtype       GL_F32 or in_dtype
