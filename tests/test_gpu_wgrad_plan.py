@@ -35,17 +35,20 @@ def workspace_for(m):
     return ws
 
 
-def test_plan_splits_exact_on_integers():
-    say(f"wgrad plan, integer inputs G={G} K={K} N={N} m={M}")
+# The long group's split parts carry its bias grad: in tile column 0, then (group 1, with
+# column g mod 2 = 1) in the partial second column of K = 264.
+@pytest.mark.parametrize("m", [M, [64, 9000, 0, 130]])
+def test_plan_splits_exact_on_integers(m):
+    say(f"wgrad plan, integer inputs G={G} K={K} N={N} m={m}")
     g = torch.Generator().manual_seed(31)
-    T = sum(M)
+    T = sum(m)
     r = lambda *s: torch.randint(-3, 4, s, generator=g)
     x, dy = r(T, K).to(torch.bfloat16), r(T, N).to(torch.bfloat16)
     mg = r(G, N, K).float()
     X, DY, MG = to64(x), to64(dy), to64(mg)
-    ref_dw = oracle.wgrad(X, DY, M)
-    ref_db = oracle.bgrad(DY, M)
-    ws = workspace_for(M)
+    ref_dw = oracle.wgrad(X, DY, m)
+    ref_db = oracle.bgrad(DY, m)
+    ws = workspace_for(m)
     xd, dyd = x.to(DEV), dy.to(DEV)
 
     dw32 = torch.empty(G, N, K, device=DEV)
@@ -62,9 +65,10 @@ def test_plan_splits_exact_on_integers():
     # the exact sums rounded once to bf16, as the oracle's exact values round
     assert_bits_equal(dw16, torch.from_numpy(ref_dw).to(torch.bfloat16), "bf16 dW")
     assert_bits_equal(db16, torch.from_numpy(ref_db).to(torch.bfloat16), "bf16 db")
-    ref_mg = oracle.wgrad(X, DY, M, main_grad=MG, accumulate=True)
+    ref_mg = oracle.wgrad(X, DY, m, main_grad=MG, accumulate=True)
     assert np.array_equal(mgd.cpu().numpy(), ref_mg), "main_grad accumulate (split parts) not exact"
-    assert bool((mgd[1] == mg[1].to(DEV)).all()), "empty group's main_grad touched"
+    e = m.index(0)
+    assert bool((mgd[e] == mg[e].to(DEV)).all()), "empty group's main_grad touched"
 
 
 def test_plan_splits_random_bf16():
