@@ -479,18 +479,41 @@ __device__ __forceinline__ void db_zero(float *slot) {
   *(float4 *)(slot + 4) = make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
-// Adds the rows of this lane's staged pieces into its 8 column sums.
+// Adds the rows of this lane's staged pieces into its 8 column sums.  bf16: pieces
+// q and q + 1 hold the same columns of two rows, so one byte permute pairs a column's
+// two values and one v_dot2_f32_bf16 against (1, 1) adds both into the column's sum
+// (two VALU instructions per column and pair of rows instead of four: this add sits
+// between the two MFMA steps of a stage).  fp16: one conversion and one add per value.
 template <bool F16>
 __device__ __forceinline__ void db_add(float *slot, const uint4 (&r)[kQ]) {
   const float4 lo = *(const float4 *)slot, hi = *(const float4 *)(slot + 4);
   float dbr[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  if constexpr (!F16) {
+    static_assert(kQ % 2 == 0, "pieces pair up");
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+    const bf16x2_t one = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
 #pragma unroll
-  for (int q = 0; q < kQ; ++q) {
-    const uint32_t d[4] = {r[q].x, r[q].y, r[q].z, r[q].w};
+    for (int q = 0; q < kQ; q += 2) {
+      const uint32_t a[4] = {r[q].x, r[q].y, r[q].z, r[q].w};
+      const uint32_t b[4] = {r[q + 1].x, r[q + 1].y, r[q + 1].z, r[q + 1].w};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      dbr[2 * e] += h16_to_f32<F16>((uint16_t)(d[e] & 0xffffu));
-      dbr[2 * e + 1] += h16_to_f32<F16>((uint16_t)(d[e] >> 16));
+      for (int e = 0; e < 4; ++e) {
+        // byte pool {b, a}, a in bytes 0-3: pl = low halves (a in its low half), ph = high halves
+        const uint32_t pl = __builtin_amdgcn_perm(b[e], a[e], 0x05040100u);
+        const uint32_t ph = __builtin_amdgcn_perm(b[e], a[e], 0x07060302u);
+        dbr[2 * e] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pl), one, dbr[2 * e], false);
+        dbr[2 * e + 1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, ph), one, dbr[2 * e + 1], false);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) {
+      const uint32_t d[4] = {r[q].x, r[q].y, r[q].z, r[q].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dbr[2 * e] += h16_to_f32<F16>((uint16_t)(d[e] & 0xffffu));
+        dbr[2 * e + 1] += h16_to_f32<F16>((uint16_t)(d[e] >> 16));
+      }
     }
   }
   *(float4 *)slot = make_float4(dbr[0], dbr[1], dbr[2], dbr[3]);

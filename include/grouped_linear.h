@@ -194,7 +194,10 @@ int gl_bgrad(int num_groups, int64_t out_features, int64_t total_rows, gl_dtype 
  *   db / db_ptrs   stacked [G, N] or device array of G pointers to [N]; every group
  *                  gets its column sums (zeros for an empty group, also when
  *                  accumulate leaves that group's main_grad untouched)
- * fp32 accumulation in a fixed order (deterministic).
+ * fp32 accumulation in a fixed order (deterministic).  For bf16 inputs each step adds
+ * two rows with one fp32 dot instruction, whose add may differ from round-to-nearest
+ * by about one ulp, so db may differ from gl_bgrad's in the last bits; exact whenever
+ * the partial sums are representable (integer-valued inputs).
  */
 int gl_wgrad_bgrad(int num_groups, int64_t in_features, int64_t out_features, int64_t total_rows,
                    gl_dtype in_dtype, gl_dtype out_dtype, gl_dtype db_dtype, const void *x, const void *dy,

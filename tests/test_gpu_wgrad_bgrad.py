@@ -94,6 +94,21 @@ def test_wgrad_bgrad_integer_exact(dtype):
     assert np.array_equal(dw.cpu().numpy(), oracle.wgrad(to64(x), to64(dy), m)), "dW not exact on integers"
 
 
+def test_wgrad_bgrad_long_group_fp32_db():
+    # fp32 bias grad of bf16 inputs over a 20000-row group (its tiles split into parts by
+    # the contraction plan), held to the fp32 bound: each lane's column sum takes about
+    # 1250 rows, two at a time
+    G, K, N, m = 2, 64, 264, [20000, 37]
+    say(f"wgrad+bgrad long group, fp32 db G={G} K={K} N={N} m={m}")
+    x, dy, _ = case(24, G, K, N, m, torch.bfloat16)
+    ws = workspace_for(m)
+    dw = torch.empty(G, N, K, dtype=torch.bfloat16, device=DEV)
+    db = torch.full((G, N), float("nan"), device=DEV)
+    gl.gl_wgrad_bgrad(x.to(DEV), dy.to(DEV), dw, db, ws)
+    torch.cuda.synchronize()
+    assert_close(db, oracle.bgrad(to64(dy), m), TOL_F32, "db fp32, 20000-row group")
+
+
 def test_wgrad_bgrad_deterministic():
     G, K, N, m = 3, 512, 1024, [1000, 17, 600]
     x, dy, _ = case(23, G, K, N, m, torch.bfloat16)
